@@ -1,0 +1,49 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+This shows the pins have teeth: a dropped term, a wrong sign, a transposed or
+mis-strided operand, SiLU on the wrong branch, a lost precision step or a
+wrong rounding mode would not go unnoticed.  Mistakes are planted only in
+temporary copies of the oracle's C source, built with gcc, on the CPU.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+MUTANTS = {
+    "exp_sign": ("exp(-z)", "exp(z)"),
+    "silu_on_up": ("oracle_silu(ag[b]) * au[b]", "oracle_silu(au[b]) * ag[b]"),
+    "no_silu": ("oracle_silu(ag[b]) * au[b]", "ag[b] * au[b]"),
+    "sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "down_transposed": ("double w = widen_bf16(rd[n]);",
+                        "double w = widen_bf16(c->wd[(size_t)n * M + m]);"),
+    "gate_up_drops_last_k": ("for (int k = 0; k < K; ++k) {", "for (int k = 0; k < K - 1; ++k) {"),
+    "down_drops_last_n": ("for (int n = 0; n < N; ++n) {", "for (int n = 0; n < N - 1; ++n) {"),
+    "x_batch_stride": ("c->xd[(size_t)b * K + k]", "c->xd[(size_t)b + k]"),
+    "h_rounded_fp32": ("c->h[o] = oracle_silu(ag[b]) * au[b];",
+                       "c->h[o] = (float)(oracle_silu(ag[b]) * au[b]);"),
+    "y_stored_transposed": ("c->y[(size_t)b * M + (size_t)m] = acc[b];",
+                            "c->y[(size_t)m * B + (size_t)b] = acc[b];"),
+    "bf16_truncates": ("nearbyint(a / q)", "floor(a / q)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / f"mutant_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.build(str(path), str(tmp_path / f"libmutant_{name}.so"))
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            failed.append(check.__name__)
+            break
+    assert failed, f"no pin caught the planted mistake {name}"
