@@ -1,0 +1,172 @@
+/*
+ * dfk.h -- C ABI of the fused decode-stage SwiGLU MLP library for MI355X (gfx950).
+ *
+ * The method ("Deep Kernel Fusion for Transformer Decoding", podcast episode
+ * page, episode summary; "Deep Kernel Fusion for Transformers", hgpu.org post,
+ * abstract): in the decode stage of a transformer, the SwiGLU MLP
+ *     h = SiLU(x W_gate^T) * (x W_up^T),     y = h W_down^T
+ * is memory-bandwidth bound.  The gate projection, the up projection, SiLU and
+ * the elementwise product run as ONE kernel that streams both weight matrices
+ * once; the down projection is a SEPARATE kernel; a profiler-driven scheduler
+ * picks a row-major or a column-major traversal variant of each kernel.
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Tensors are dense and row-major with no strides:
+ *       x       [B, d_model]        bf16
+ *       W_gate  [d_ff, d_model]     bf16   (nn.Linear layout: [out, in])
+ *       W_up    [d_ff, d_model]     bf16
+ *       W_down  [d_model, d_ff]     bf16
+ *       h       [B, d_ff]           fp32   (SiLU(g) * u, unrounded fp32)
+ *       out     [B, d_model]        bf16   (fp32 accumulation, round-to-nearest-even)
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller (e.g.
+ *     allocated by PyTorch); the library never frees or retains it beyond the
+ *     call's kernels.  Outputs must not alias inputs.  Pointers must be 16-byte
+ *     aligned.
+ *   - Calls are asynchronous on `stream` (0 = the null stream): they enqueue
+ *     kernels and return without synchronising.  Faults inside kernels surface
+ *     at the caller's next synchronisation.  The functions are thread-safe.
+ *   - Arguments are validated before anything is enqueued; on any error status
+ *     nothing has been launched.  No C++ exception crosses this ABI.
+ *   - Limits: 1 <= B <= 256 (decode batch; larger B is prefill, not served
+ *     here), d_model and d_ff positive multiples of 8 (rows are whole 16-byte
+ *     vectors), d_model * d_ff < 2^31.
+ *   - Inputs are assumed finite; NaN or Inf propagate through the arithmetic
+ *     and are not checked.
+ */
+#ifndef DFK_H
+#define DFK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Weight-traversal variant of a kernel.  Every variant computes the same
+ * mathematics over the same (row-major) storage; they differ only in how the
+ * weight matrix is walked, hence only in fp32 summation order.
+ *
+ *   ROW  row-major traversal: each output row's dot product is owned by one
+ *        wavefront, which streams the whole weight row (all of K) and reduces
+ *        across its lanes; the epilogue runs in registers.
+ *   COL  column-major traversal: the weight matrix is cut into column panels
+ *        (K slices); each workgroup streams one panel for many rows and the
+ *        per-panel partial sums are combined, in fixed panel order, by the
+ *        last workgroup to finish a row block (no float atomics, so results
+ *        are run-to-run deterministic).
+ *
+ * The engine under a traversal is the vector ALU (bf16 dot2 / fp32 FMA, batch
+ * below 16) or the matrix cores (MFMA bf16 -> fp32, batch 16 and up, or where
+ * the VALU kernel's LDS staging does not fit).  AUTO asks the scheduler
+ * (dfk_schedule_select).  ROW and COL pick the engine by that batch rule; the
+ * *_VALU / *_MFMA values force an engine (DFK_ERR_UNSUPPORTED where that
+ * engine cannot run the shape).
+ */
+typedef enum {
+    DFK_LAYOUT_AUTO = 0,
+    DFK_LAYOUT_ROW = 1,
+    DFK_LAYOUT_COL = 2,
+    DFK_LAYOUT_ROW_VALU = 3,
+    DFK_LAYOUT_COL_VALU = 4,
+    DFK_LAYOUT_ROW_MFMA = 5,
+    DFK_LAYOUT_COL_MFMA = 6
+} dfk_layout_t;
+
+typedef enum {
+    DFK_OK = 0,
+    DFK_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum value */
+    DFK_ERR_UNSUPPORTED = 2, /* B > 256, a dim not a multiple of 8, too large, or a forced
+                                engine that cannot run the shape */
+    DFK_ERR_MISALIGNED = 3,  /* a tensor pointer not 16-byte aligned */
+    DFK_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+    DFK_ERR_OOM = 5          /* the library could not allocate its workspace */
+} dfk_status_t;
+
+/*
+ * Fused gate + up projection + SiLU + elementwise product ("Deep Kernel Fusion
+ * for Transformer Decoding", episode summary: one decode-stage kernel for the
+ * up projection, the gate projection, the SiLU activation and the elementwise
+ * multiply).  Computes, for b < B and n < d_ff,
+ *     g = sum_k x[b,k] W_gate[n,k],  u = sum_k x[b,k] W_up[n,k],
+ *     h[b,n] = g / (1 + exp(-g)) * u
+ * with fp32 accumulation; h is written in fp32 (not rounded to bf16).
+ * Each weight matrix is read from HBM once per call; g and u never touch HBM.
+ */
+dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate,
+                                  const uint16_t *W_up, float *h, int B, int d_model,
+                                  int d_ff, dfk_layout_t layout, hipStream_t stream);
+
+/*
+ * Down projection, a separate kernel (same passage: the down projection stays
+ * out of the fused kernel).  out[b,m] = RNE_bf16( sum_n h[b,n] W_down[m,n] ),
+ * fp32 accumulation from the fp32 h.
+ */
+dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out, int B,
+                           int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream);
+
+/*
+ * The whole MLP: dfk_gate_up_silu_mul then dfk_down_proj on the same stream,
+ * with h in a library-owned fp32 workspace (B * d_ff * 4 bytes) kept per
+ * (device, stream) and grown on demand; it lives until the library is
+ * unloaded.  Two launches per call.  The layout applies to both kernels; with
+ * AUTO each kernel takes the scheduler's own choice.
+ */
+dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up,
+                            const uint16_t *W_down, uint16_t *out, int B, int d_model,
+                            int d_ff, dfk_layout_t layout, hipStream_t stream);
+
+/*
+ * Profiler-driven variant choice ("Deep Kernel Fusion for Transformer
+ * Decoding", episode summary: runtime scheduling across row-major and
+ * column-major kernel variants; "Deep Kernel Fusion for Transformers",
+ * abstract: a kernel scheduler).  Host only; never touches the device.
+ * Looks the shape up in the tuning table (the file named by the environment
+ * variable DFK_TUNING_TABLE, else the table installed beside the library):
+ * exact (B, d_model, d_ff) entry, else the entry for the same (d_model, d_ff)
+ * with the nearest tuned batch at or above B (else the largest below), else
+ * a built-in heuristic.  Writes explicit variants (never AUTO) to both
+ * outputs.  DFK_FORCE_LAYOUT=row|col overrides the traversal.
+ */
+dfk_status_t dfk_schedule_select(int B, int d_model, int d_ff, dfk_layout_t *gate_up_layout,
+                                 dfk_layout_t *down_layout);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *dfk_status_string(dfk_status_t s);
+
+/* Static name of a layout value, e.g. "row_valu" (never NULL). */
+const char *dfk_layout_name(dfk_layout_t layout);
+
+/* Library version string, e.g. "dfk 0.1.0 gfx950". */
+const char *dfk_version(void);
+
+/*
+ * Reload the tuning table from `path` (NULL: the default location).  Returns
+ * DFK_OK when a table was loaded, DFK_ERR_INVALID_ARG when the file is missing
+ * or malformed (the scheduler then uses its heuristic).  Host only.
+ */
+dfk_status_t dfk_load_tuning_table(const char *path);
+
+/*
+ * Where the scheduler's current table came from: the path of the loaded file,
+ * or "heuristic" when none is loaded.  Static storage, valid until the next
+ * dfk_load_tuning_table call.
+ */
+const char *dfk_tuning_table_source(void);
+
+/*
+ * Release the workspaces the library holds for the current device (waits for
+ * the device first).  Optional: they are also released when the library is
+ * unloaded.
+ */
+dfk_status_t dfk_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFK_H */

@@ -1,0 +1,208 @@
+"""Fused decode-stage SwiGLU MLP for MI355X (gfx950): Python binding of libdfk.so.
+
+Argument marshalling only: every step of the MLP runs in the HIP kernels of
+``libdfk.so``; this module checks tensor dtypes/devices/shapes, passes device
+pointers and the current HIP stream through the C ABI (``include/dfk.h``), and
+turns a non-OK status into ``DfkError``.  There is no fallback path: if the
+library is missing, every call raises.
+
+The functions keep the C names:
+    dfk_gate_up_silu_mul(x, W_gate, W_up, h=None, layout=AUTO, stream=None) -> h
+    dfk_down_proj(h, W_down, out=None, layout=AUTO, stream=None) -> out
+    dfk_swiglu_mlp(x, W_gate, W_up, W_down, out=None, layout=AUTO, stream=None) -> out
+    dfk_schedule_select(B, d_model, d_ff) -> (gate_up_layout, down_layout)
+Tensors: x [B, d_model] bf16, W_gate/W_up [d_ff, d_model] bf16, W_down
+[d_model, d_ff] bf16, h [B, d_ff] fp32, out [B, d_model] bf16, all contiguous
+on one GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+from typing import Optional, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG_DIR, "libdfk.so")
+TUNING_TABLE = os.path.join(PKG_DIR, "tuning", "gfx950.json")
+
+
+class Layout(enum.IntEnum):
+    AUTO = 0
+    ROW = 1
+    COL = 2
+    ROW_VALU = 3
+    COL_VALU = 4
+    ROW_MFMA = 5
+    COL_MFMA = 6
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    INVALID_ARG = 1
+    UNSUPPORTED = 2
+    MISALIGNED = 3
+    HIP = 4
+    OOM = 5
+
+
+EXPORTED = (
+    "dfk_gate_up_silu_mul", "dfk_down_proj", "dfk_swiglu_mlp", "dfk_schedule_select",
+    "dfk_status_string", "dfk_layout_name", "dfk_version", "dfk_load_tuning_table",
+    "dfk_tuning_table_source", "dfk_release_workspace",
+)
+
+
+class DfkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"{LIBRARY} is not built; run `python -m swiglu_mlp_amd.build` "
+            "(the HIP library is required: there is no fallback path)")
+    L = ctypes.CDLL(LIBRARY)
+    vp, i, u16p, f32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    L.dfk_gate_up_silu_mul.argtypes = [u16p, u16p, u16p, f32p, i, i, i, i, vp]
+    L.dfk_gate_up_silu_mul.restype = i
+    L.dfk_down_proj.argtypes = [f32p, u16p, u16p, i, i, i, i, vp]
+    L.dfk_down_proj.restype = i
+    L.dfk_swiglu_mlp.argtypes = [u16p, u16p, u16p, u16p, u16p, i, i, i, i, vp]
+    L.dfk_swiglu_mlp.restype = i
+    L.dfk_schedule_select.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.dfk_schedule_select.restype = i
+    L.dfk_status_string.argtypes = [i]
+    L.dfk_status_string.restype = ctypes.c_char_p
+    L.dfk_layout_name.argtypes = [i]
+    L.dfk_layout_name.restype = ctypes.c_char_p
+    L.dfk_version.argtypes = []
+    L.dfk_version.restype = ctypes.c_char_p
+    L.dfk_load_tuning_table.argtypes = [ctypes.c_char_p]
+    L.dfk_load_tuning_table.restype = i
+    L.dfk_tuning_table_source.argtypes = []
+    L.dfk_tuning_table_source.restype = ctypes.c_char_p
+    L.dfk_release_workspace.argtypes = []
+    L.dfk_release_workspace.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().dfk_status_string(int(status)).decode()
+
+
+def layout_name(layout: int) -> str:
+    return lib().dfk_layout_name(int(layout)).decode()
+
+
+def version() -> str:
+    return lib().dfk_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != Status.OK:
+        raise DfkError(status, where)
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _expect(t, name: str, dtype, shape) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def dfk_gate_up_silu_mul(x, W_gate, W_up, h=None, layout: int = Layout.AUTO, stream=None):
+    """h = SiLU(x W_gate^T) * (x W_up^T) in fp32, one fused kernel."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(W_gate, "W_gate", torch.bfloat16, (d_ff, d_model))
+    _expect(W_up, "W_up", torch.bfloat16, (d_ff, d_model))
+    if h is None:
+        h = torch.empty((B, d_ff), dtype=torch.float32, device=x.device)
+    _expect(h, "h", torch.float32, (B, d_ff))
+    st = lib().dfk_gate_up_silu_mul(x.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(), h.data_ptr(),
+                                    B, d_model, d_ff, int(layout), _stream_handle(stream, x.device))
+    _check(st, "dfk_gate_up_silu_mul")
+    return h
+
+
+def dfk_down_proj(h, W_down, out=None, layout: int = Layout.AUTO, stream=None):
+    """out = bf16_RNE(h W_down^T), a separate kernel."""
+    import torch
+    B, d_ff = h.shape
+    d_model = W_down.shape[0]
+    _expect(h, "h", torch.float32, (B, d_ff))
+    _expect(W_down, "W_down", torch.bfloat16, (d_model, d_ff))
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=h.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_down_proj(h.data_ptr(), W_down.data_ptr(), out.data_ptr(), B, d_model, d_ff,
+                             int(layout), _stream_handle(stream, h.device))
+    _check(st, "dfk_down_proj")
+    return out
+
+
+def dfk_swiglu_mlp(x, W_gate, W_up, W_down, out=None, layout: int = Layout.AUTO, stream=None):
+    """The whole MLP: fused gate-up kernel, then the down-projection kernel."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(W_gate, "W_gate", torch.bfloat16, (d_ff, d_model))
+    _expect(W_up, "W_up", torch.bfloat16, (d_ff, d_model))
+    _expect(W_down, "W_down", torch.bfloat16, (d_model, d_ff))
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=x.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_swiglu_mlp(x.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(), W_down.data_ptr(),
+                              out.data_ptr(), B, d_model, d_ff, int(layout),
+                              _stream_handle(stream, x.device))
+    _check(st, "dfk_swiglu_mlp")
+    return out
+
+
+def dfk_schedule_select(B: int, d_model: int, d_ff: int) -> Tuple[Layout, Layout]:
+    """The scheduler's (gate_up, down) variants for a shape (host only)."""
+    g, d = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().dfk_schedule_select(int(B), int(d_model), int(d_ff), ctypes.byref(g), ctypes.byref(d))
+    _check(st, "dfk_schedule_select")
+    return Layout(g.value), Layout(d.value)
+
+
+def dfk_load_tuning_table(path: Optional[str] = None) -> None:
+    st = lib().dfk_load_tuning_table(path.encode() if path is not None else None)
+    _check(st, "dfk_load_tuning_table")
+
+
+def dfk_tuning_table_source() -> str:
+    return lib().dfk_tuning_table_source().decode()
+
+
+def dfk_release_workspace() -> None:
+    _check(lib().dfk_release_workspace(), "dfk_release_workspace")

@@ -1,0 +1,657 @@
+// dfk_runtime.cpp -- the C ABI of include/dfk.h: argument checks, variant
+// resolution, per-(device, stream) workspaces and the tuning-table scheduler.
+//
+// Host code only; the kernels are in dfk_kernels.hip.  No exception leaves an
+// exported function.
+
+#include <dlfcn.h>
+
+#include <algorithm>
+#include <cctype>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "dfk.h"
+#include "dfk_kernels.h"
+
+namespace {
+
+using dfk::Engine;
+using dfk::Op;
+using dfk::Plan;
+using dfk::Traversal;
+
+constexpr int kMaxBatch = 256;
+
+int log_level() {
+    static int level = [] {
+        const char *s = std::getenv("DFK_LOG");
+        return s ? std::atoi(s) : 0;
+    }();
+    return level;
+}
+
+// ------------------------------------------------------------ validation --
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dfk_status_t check_dims(int B, int d_model, int d_ff) {
+    if (B < 1 || d_model < 1 || d_ff < 1) return DFK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return DFK_ERR_UNSUPPORTED;
+    if ((d_model % 8) || (d_ff % 8)) return DFK_ERR_UNSUPPORTED;
+    if ((long long)d_model * (long long)d_ff >= (1LL << 31)) return DFK_ERR_UNSUPPORTED;
+    return DFK_OK;
+}
+
+bool valid_layout(dfk_layout_t l) { return l >= DFK_LAYOUT_AUTO && l <= DFK_LAYOUT_COL_MFMA; }
+
+// ------------------------------------------------------------ devices -----
+
+int device_cus(int dev) {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    cache[dev] = cus;
+    return cus;
+}
+
+// ------------------------------------------------------------ workspace ---
+//
+// Per (device, stream): a data buffer [h (swiglu_mlp only)] [COL partial sums]
+// and a separate counter buffer for the COL arrival counters.  Kernels on one
+// stream run in order, so the two kernels of a call share both.  The counter
+// buffer is zeroed when it is allocated and every kernel leaves the counters
+// it used at zero, so it is all-zero between calls.  Growing frees the old
+// buffer (hipFree waits for the device).
+
+struct Slot {
+    std::mutex mu;
+    void *data = nullptr;
+    size_t data_bytes = 0;
+    unsigned *counters = nullptr;
+    size_t n_counters = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Slot>> g_ws;
+
+Slot *slot_for(int dev, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto &p = g_ws[std::make_pair(dev, stream)];
+    if (!p) p.reset(new Slot);
+    return p.get();
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+struct Carve {
+    float *h = nullptr;
+    float *partial = nullptr;
+    unsigned *counters = nullptr;
+};
+
+// Caller holds slot->mu.
+dfk_status_t ensure_workspace(Slot *slot, size_t h_floats, size_t partial_floats, size_t counters,
+                              hipStream_t stream, Carve *c) {
+    const size_t h_bytes = align256(h_floats * sizeof(float));
+    const size_t need = h_bytes + align256(partial_floats * sizeof(float));
+    if (need > slot->data_bytes) {
+        if (slot->data) {
+            if (hipFree(slot->data) != hipSuccess) return DFK_ERR_HIP;
+            slot->data = nullptr;
+            slot->data_bytes = 0;
+        }
+        const size_t grow = std::max(need, size_t(1) << 20);
+        if (hipMalloc(&slot->data, grow) != hipSuccess) {
+            slot->data = nullptr;
+            (void)hipGetLastError();
+            return DFK_ERR_OOM;
+        }
+        slot->data_bytes = grow;
+    }
+    if (counters > slot->n_counters) {
+        if (slot->counters) {
+            if (hipFree(slot->counters) != hipSuccess) return DFK_ERR_HIP;
+            slot->counters = nullptr;
+            slot->n_counters = 0;
+        }
+        const size_t n = std::max(counters, size_t(4096));
+        if (hipMalloc(reinterpret_cast<void **>(&slot->counters), n * sizeof(unsigned)) != hipSuccess) {
+            slot->counters = nullptr;
+            (void)hipGetLastError();
+            return DFK_ERR_OOM;
+        }
+        if (hipMemsetAsync(slot->counters, 0, n * sizeof(unsigned), stream) != hipSuccess) return DFK_ERR_HIP;
+        slot->n_counters = n;
+    }
+    char *base = static_cast<char *>(slot->data);
+    c->h = h_floats ? reinterpret_cast<float *>(base) : nullptr;
+    c->partial = partial_floats ? reinterpret_cast<float *>(base + h_bytes) : nullptr;
+    c->counters = counters ? slot->counters : nullptr;
+    return DFK_OK;
+}
+
+// ------------------------------------------------------------ tiny JSON ---
+//
+// Enough JSON for the tuning table: objects, arrays, strings (no \u escapes
+// beyond ASCII), numbers, true/false/null.
+
+struct JVal {
+    enum Kind { NUL, BOOL, NUM, STR, ARR, OBJ } kind = NUL;
+    bool b = false;
+    double num = 0;
+    std::string str;
+    std::vector<JVal> arr;
+    std::vector<std::pair<std::string, JVal>> obj;
+    const JVal *get(const char *key) const {
+        if (kind != OBJ) return nullptr;
+        for (auto &kv : obj)
+            if (kv.first == key) return &kv.second;
+        return nullptr;
+    }
+};
+
+struct JParser {
+    const char *p, *end;
+    bool ok = true;
+    void ws() {
+        while (p < end && std::isspace((unsigned char)*p)) ++p;
+    }
+    bool lit(const char *s) {
+        size_t n = std::strlen(s);
+        if ((size_t)(end - p) >= n && std::strncmp(p, s, n) == 0) {
+            p += n;
+            return true;
+        }
+        return false;
+    }
+    bool string(std::string *out) {
+        if (p >= end || *p != '"') return false;
+        ++p;
+        while (p < end && *p != '"') {
+            char ch = *p++;
+            if (ch == '\\') {
+                if (p >= end) return false;
+                char e = *p++;
+                switch (e) {
+                    case 'n': ch = '\n'; break;
+                    case 't': ch = '\t'; break;
+                    case 'r': ch = '\r'; break;
+                    case 'b': ch = '\b'; break;
+                    case 'f': ch = '\f'; break;
+                    case 'u': {
+                        if (end - p < 4) return false;
+                        unsigned v = 0;
+                        for (int i = 0; i < 4; ++i) {
+                            char hch = *p++;
+                            v <<= 4;
+                            if (hch >= '0' && hch <= '9') v |= hch - '0';
+                            else if (hch >= 'a' && hch <= 'f') v |= hch - 'a' + 10;
+                            else if (hch >= 'A' && hch <= 'F') v |= hch - 'A' + 10;
+                            else return false;
+                        }
+                        ch = v < 128 ? (char)v : '?';
+                        break;
+                    }
+                    default: ch = e; break;
+                }
+            }
+            out->push_back(ch);
+        }
+        if (p >= end) return false;
+        ++p;
+        return true;
+    }
+    bool value(JVal *v, int depth) {
+        if (depth > 32) return false;
+        ws();
+        if (p >= end) return false;
+        if (*p == '{') {
+            ++p;
+            v->kind = JVal::OBJ;
+            ws();
+            if (p < end && *p == '}') { ++p; return true; }
+            for (;;) {
+                ws();
+                std::string key;
+                if (!string(&key)) return false;
+                ws();
+                if (p >= end || *p != ':') return false;
+                ++p;
+                JVal child;
+                if (!value(&child, depth + 1)) return false;
+                v->obj.emplace_back(std::move(key), std::move(child));
+                ws();
+                if (p < end && *p == ',') { ++p; continue; }
+                if (p < end && *p == '}') { ++p; return true; }
+                return false;
+            }
+        }
+        if (*p == '[') {
+            ++p;
+            v->kind = JVal::ARR;
+            ws();
+            if (p < end && *p == ']') { ++p; return true; }
+            for (;;) {
+                JVal child;
+                if (!value(&child, depth + 1)) return false;
+                v->arr.push_back(std::move(child));
+                ws();
+                if (p < end && *p == ',') { ++p; continue; }
+                if (p < end && *p == ']') { ++p; return true; }
+                return false;
+            }
+        }
+        if (*p == '"') {
+            v->kind = JVal::STR;
+            return string(&v->str);
+        }
+        if (lit("true")) { v->kind = JVal::BOOL; v->b = true; return true; }
+        if (lit("false")) { v->kind = JVal::BOOL; v->b = false; return true; }
+        if (lit("null")) { v->kind = JVal::NUL; return true; }
+        char *q = nullptr;
+        std::string tmp(p, std::min<size_t>(end - p, 64));
+        double d = std::strtod(tmp.c_str(), &q);
+        if (q == tmp.c_str()) return false;
+        p += (q - tmp.c_str());
+        v->kind = JVal::NUM;
+        v->num = d;
+        return true;
+    }
+};
+
+bool parse_json(const std::string &text, JVal *out) {
+    JParser ps{text.data(), text.data() + text.size()};
+    if (!ps.value(out, 0)) return false;
+    ps.ws();
+    return ps.p == ps.end;
+}
+
+// ------------------------------------------------------------ variants ----
+
+struct Variant {
+    Engine engine;
+    Traversal trav;
+};
+
+bool variant_from_name(const std::string &s, Variant *v) {
+    if (s == "row_valu") { *v = {dfk::ENGINE_VALU, dfk::TRAV_ROW}; return true; }
+    if (s == "col_valu") { *v = {dfk::ENGINE_VALU, dfk::TRAV_COL}; return true; }
+    if (s == "row_mfma") { *v = {dfk::ENGINE_MFMA, dfk::TRAV_ROW}; return true; }
+    if (s == "col_mfma") { *v = {dfk::ENGINE_MFMA, dfk::TRAV_COL}; return true; }
+    return false;
+}
+
+dfk_layout_t layout_of(Variant v) {
+    if (v.engine == dfk::ENGINE_VALU) return v.trav == dfk::TRAV_ROW ? DFK_LAYOUT_ROW_VALU : DFK_LAYOUT_COL_VALU;
+    return v.trav == dfk::TRAV_ROW ? DFK_LAYOUT_ROW_MFMA : DFK_LAYOUT_COL_MFMA;
+}
+
+// ------------------------------------------------------------ tuning table -
+
+struct Entry {
+    Op op;
+    int B, d_model, d_ff;
+    Variant v;
+};
+
+struct Table {
+    std::mutex mu;
+    bool loaded = false;     // a file was parsed successfully
+    bool attempted = false;  // the default load has been tried
+    std::string source = "heuristic";
+    std::vector<Entry> entries;
+};
+
+Table &table() {
+    static Table t;
+    return t;
+}
+
+std::string default_table_path() {
+    Dl_info info;
+    if (dladdr(reinterpret_cast<void *>(&default_table_path), &info) && info.dli_fname) {
+        std::string lib(info.dli_fname);
+        size_t slash = lib.find_last_of('/');
+        std::string dir = (slash == std::string::npos) ? "." : lib.substr(0, slash);
+        return dir + "/tuning/gfx950.json";
+    }
+    return "tuning/gfx950.json";
+}
+
+// Parse a table file; false (and no change) on any problem.
+bool load_table_file(const std::string &path, std::vector<Entry> *out) {
+    std::ifstream f(path, std::ios::binary);
+    if (!f) return false;
+    std::stringstream ss;
+    ss << f.rdbuf();
+    JVal root;
+    if (!parse_json(ss.str(), &root) || root.kind != JVal::OBJ) return false;
+    const JVal *fmt = root.get("format");
+    if (!fmt || fmt->kind != JVal::STR || fmt->str != "dfk-tuning-v1") return false;
+    const JVal *arch = root.get("arch");
+    if (!arch || arch->kind != JVal::STR || arch->str != "gfx950") return false;
+    const JVal *ents = root.get("entries");
+    if (!ents || ents->kind != JVal::ARR) return false;
+    std::vector<Entry> v;
+    for (const JVal &e : ents->arr) {
+        const JVal *op = e.get("op"), *B = e.get("B"), *dm = e.get("d_model"), *df = e.get("d_ff"),
+                   *w = e.get("winner");
+        if (!op || !B || !dm || !df || !w || op->kind != JVal::STR || B->kind != JVal::NUM ||
+            dm->kind != JVal::NUM || df->kind != JVal::NUM || w->kind != JVal::STR)
+            return false;
+        Entry en;
+        if (op->str == "gate_up") en.op = dfk::OP_GATE_UP;
+        else if (op->str == "down") en.op = dfk::OP_DOWN;
+        else return false;
+        en.B = (int)B->num;
+        en.d_model = (int)dm->num;
+        en.d_ff = (int)df->num;
+        if (!variant_from_name(w->str, &en.v)) return false;
+        if (en.B < 1 || en.d_model < 1 || en.d_ff < 1) return false;
+        v.push_back(en);
+    }
+    *out = std::move(v);
+    return true;
+}
+
+// Caller holds table().mu.
+void ensure_table_loaded() {
+    Table &t = table();
+    if (t.attempted) return;
+    t.attempted = true;
+    const char *env = std::getenv("DFK_TUNING_TABLE");
+    std::string path = env && *env ? std::string(env) : default_table_path();
+    std::vector<Entry> v;
+    if (load_table_file(path, &v)) {
+        t.entries = std::move(v);
+        t.loaded = true;
+        t.source = path;
+    }
+    if (log_level() >= 1)
+        std::fprintf(stderr, "[dfk] tuning table: %s (%zu entries)\n", t.source.c_str(), t.entries.size());
+}
+
+// The built-in choice when the table has nothing for a shape: VALU row
+// traversal while the batch is small, MFMA with K panels above.
+Variant heuristic(Op op, int B) {
+    if (B <= dfk::kValuMaxBatch) return {dfk::ENGINE_VALU, dfk::TRAV_ROW};
+    (void)op;
+    return {dfk::ENGINE_MFMA, dfk::TRAV_COL};
+}
+
+// Exact entry; else nearest tuned batch >= B for the same (d_model, d_ff);
+// else the largest tuned batch below B; else the heuristic.
+Variant lookup(Op op, int B, int d_model, int d_ff) {
+    Table &t = table();
+    std::lock_guard<std::mutex> lock(t.mu);
+    ensure_table_loaded();
+    const Entry *above = nullptr, *below = nullptr;
+    for (const Entry &e : t.entries) {
+        if (e.op != op || e.d_model != d_model || e.d_ff != d_ff) continue;
+        if (e.B == B) return e.v;
+        if (e.B > B && (!above || e.B < above->B)) above = &e;
+        if (e.B < B && (!below || e.B > below->B)) below = &e;
+    }
+    if (above) return above->v;
+    if (below) return below->v;
+    return heuristic(op, B);
+}
+
+// Apply DFK_FORCE_LAYOUT=row|col to a traversal.
+void apply_force(Variant *v) {
+    const char *f = std::getenv("DFK_FORCE_LAYOUT");
+    if (!f) return;
+    if (!std::strcmp(f, "row")) v->trav = dfk::TRAV_ROW;
+    else if (!std::strcmp(f, "col")) v->trav = dfk::TRAV_COL;
+}
+
+// Turn a layout argument into a runnable plan.
+dfk_status_t resolve(Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int cus, Plan *plan) {
+    Variant v;
+    bool forced_engine = false;
+    switch (layout) {
+        case DFK_LAYOUT_AUTO:
+            v = lookup(op, B, d_model, d_ff);
+            apply_force(&v);
+            break;
+        case DFK_LAYOUT_ROW: v = {B >= 16 ? dfk::ENGINE_MFMA : dfk::ENGINE_VALU, dfk::TRAV_ROW}; break;
+        case DFK_LAYOUT_COL: v = {B >= 16 ? dfk::ENGINE_MFMA : dfk::ENGINE_VALU, dfk::TRAV_COL}; break;
+        case DFK_LAYOUT_ROW_VALU: v = {dfk::ENGINE_VALU, dfk::TRAV_ROW}; forced_engine = true; break;
+        case DFK_LAYOUT_COL_VALU: v = {dfk::ENGINE_VALU, dfk::TRAV_COL}; forced_engine = true; break;
+        case DFK_LAYOUT_ROW_MFMA: v = {dfk::ENGINE_MFMA, dfk::TRAV_ROW}; forced_engine = true; break;
+        case DFK_LAYOUT_COL_MFMA: v = {dfk::ENGINE_MFMA, dfk::TRAV_COL}; forced_engine = true; break;
+        default: return DFK_ERR_INVALID_ARG;
+    }
+    if (dfk::make_plan(op, v.engine, v.trav, B, d_model, d_ff, cus, plan)) return DFK_OK;
+    if (forced_engine) return DFK_ERR_UNSUPPORTED;
+    // the VALU kernel cannot hold this shape: the matrix cores can
+    if (dfk::make_plan(op, dfk::ENGINE_MFMA, v.trav, B, d_model, d_ff, cus, plan)) return DFK_OK;
+    return DFK_ERR_UNSUPPORTED;
+}
+
+void log_plan(const char *what, const Plan &p) {
+    if (log_level() < 2) return;
+    std::fprintf(stderr, "[dfk] %s: %s/%s B=%d rows=%d K=%d groups=%d splits=%d grid=%d block=%d lds=%zu\n",
+                 what, p.engine == dfk::ENGINE_VALU ? "valu" : "mfma", p.trav == dfk::TRAV_ROW ? "row" : "col",
+                 p.B, p.rows, p.K, p.groups, p.splits, p.grid, p.block, p.lds_bytes);
+}
+
+// Current device, or an error status.
+dfk_status_t current_device(int *dev) {
+    if (hipGetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return DFK_ERR_HIP;
+    }
+    return DFK_OK;
+}
+
+}  // namespace
+
+// ================================================================ C ABI ====
+
+extern "C" {
+
+const char *dfk_status_string(dfk_status_t s) {
+    switch (s) {
+        case DFK_OK: return "DFK_OK";
+        case DFK_ERR_INVALID_ARG: return "DFK_ERR_INVALID_ARG: null pointer, non-positive size or bad enum";
+        case DFK_ERR_UNSUPPORTED: return "DFK_ERR_UNSUPPORTED: shape or forced engine not supported";
+        case DFK_ERR_MISALIGNED: return "DFK_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
+        case DFK_ERR_HIP: return "DFK_ERR_HIP: HIP runtime call or kernel launch failed";
+        case DFK_ERR_OOM: return "DFK_ERR_OOM: workspace allocation failed";
+    }
+    return "DFK_ERR_UNKNOWN";
+}
+
+const char *dfk_layout_name(dfk_layout_t l) {
+    switch (l) {
+        case DFK_LAYOUT_AUTO: return "auto";
+        case DFK_LAYOUT_ROW: return "row";
+        case DFK_LAYOUT_COL: return "col";
+        case DFK_LAYOUT_ROW_VALU: return "row_valu";
+        case DFK_LAYOUT_COL_VALU: return "col_valu";
+        case DFK_LAYOUT_ROW_MFMA: return "row_mfma";
+        case DFK_LAYOUT_COL_MFMA: return "col_mfma";
+    }
+    return "invalid";
+}
+
+const char *dfk_version(void) { return "dfk 0.1.0 gfx950"; }
+
+dfk_status_t dfk_schedule_select(int B, int d_model, int d_ff, dfk_layout_t *gate_up_layout,
+                                 dfk_layout_t *down_layout) {
+    try {
+        if (!gate_up_layout || !down_layout) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        Variant g = lookup(dfk::OP_GATE_UP, B, d_model, d_ff);
+        Variant d = lookup(dfk::OP_DOWN, B, d_model, d_ff);
+        apply_force(&g);
+        apply_force(&d);
+        // a VALU winner from a neighbouring batch cannot serve a batch above
+        // the VALU limit: keep its traversal, move it to the matrix cores
+        if (g.engine == dfk::ENGINE_VALU && B > dfk::kValuMaxBatch) g.engine = dfk::ENGINE_MFMA;
+        if (d.engine == dfk::ENGINE_VALU && B > dfk::kValuMaxBatch) d.engine = dfk::ENGINE_MFMA;
+        if (g.engine == dfk::ENGINE_VALU && (size_t)B * d_model * 2 > dfk::kValuLdsLimit)
+            g.engine = dfk::ENGINE_MFMA;
+        *gate_up_layout = layout_of(g);
+        *down_layout = layout_of(d);
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_load_tuning_table(const char *path) {
+    try {
+        Table &t = table();
+        std::lock_guard<std::mutex> lock(t.mu);
+        std::string p = path ? std::string(path) : default_table_path();
+        std::vector<Entry> v;
+        t.attempted = true;
+        if (!load_table_file(p, &v)) {
+            t.entries.clear();
+            t.loaded = false;
+            t.source = "heuristic";
+            return DFK_ERR_INVALID_ARG;
+        }
+        t.entries = std::move(v);
+        t.loaded = true;
+        t.source = p;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_INVALID_ARG;
+    }
+}
+
+const char *dfk_tuning_table_source(void) {
+    Table &t = table();
+    std::lock_guard<std::mutex> lock(t.mu);
+    ensure_table_loaded();
+    return t.source.c_str();
+}
+
+dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up, float *h,
+                                  int B, int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!x || !W_gate || !W_up || !h || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h)) return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan p;
+        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
+        log_plan("gate_up", p);
+        Slot *slot = slot_for(dev, stream);
+        std::lock_guard<std::mutex> lock(slot->mu);
+        Carve c;
+        if (p.splits > 1 && (st = ensure_workspace(slot, 0, p.partial_floats, p.counters, stream, &c)) != DFK_OK)
+            return st;
+        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, c.partial, c.counters, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out, int B, int d_model, int d_ff,
+                           dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!h || !W_down || !out || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(h) || !aligned16(W_down) || !aligned16(out)) return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan p;
+        if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
+        log_plan("down", p);
+        Slot *slot = slot_for(dev, stream);
+        std::lock_guard<std::mutex> lock(slot->mu);
+        Carve c;
+        if (p.splits > 1 && (st = ensure_workspace(slot, 0, p.partial_floats, p.counters, stream, &c)) != DFK_OK)
+            return st;
+        if (dfk::launch_down(p, h, W_down, out, c.partial, c.counters, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up,
+                            const uint16_t *W_down, uint16_t *out, int B, int d_model, int d_ff,
+                            dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!x || !W_gate || !W_up || !W_down || !out || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) || !aligned16(out))
+            return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        const int cus = device_cus(dev);
+        Plan pg, pd;
+        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, cus, &pg)) != DFK_OK) return st;
+        if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
+        log_plan("gate_up", pg);
+        log_plan("down", pd);
+        const size_t partial = std::max(pg.splits > 1 ? pg.partial_floats : 0, pd.splits > 1 ? pd.partial_floats : 0);
+        const size_t counters = std::max(pg.splits > 1 ? pg.counters : 0, pd.splits > 1 ? pd.counters : 0);
+        Slot *slot = slot_for(dev, stream);
+        std::lock_guard<std::mutex> lock(slot->mu);
+        Carve c;
+        if ((st = ensure_workspace(slot, (size_t)B * d_ff, partial, counters, stream, &c)) != DFK_OK) return st;
+        if (dfk::launch_gate_up(pg, x, W_gate, W_up, c.h, c.partial, c.counters, stream) != hipSuccess)
+            return DFK_ERR_HIP;
+        if (dfk::launch_down(pd, c.h, W_down, out, c.partial, c.counters, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_release_workspace(void) {
+    try {
+        int dev;
+        dfk_status_t st = current_device(&dev);
+        if (st != DFK_OK) return st;
+        if (hipDeviceSynchronize() != hipSuccess) return DFK_ERR_HIP;
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        for (auto it = g_ws.begin(); it != g_ws.end();) {
+            if (it->first.first != dev) {
+                ++it;
+                continue;
+            }
+            {
+                std::lock_guard<std::mutex> l2(it->second->mu);
+                if (it->second->data && hipFree(it->second->data) != hipSuccess) st = DFK_ERR_HIP;
+                if (it->second->counters && hipFree(it->second->counters) != hipSuccess) st = DFK_ERR_HIP;
+                it->second->data = nullptr;
+                it->second->counters = nullptr;
+            }
+            it = g_ws.erase(it);
+        }
+        return st;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+}  // extern "C"

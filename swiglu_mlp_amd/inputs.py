@@ -159,5 +159,25 @@ def integer_h(B: int, d_ff: int, seed: int, bound: int = 256) -> np.ndarray:
 
 
 def h_like(B: int, d_ff: int, seed: int, std: float = 1.0) -> np.ndarray:
-    """fp32 h with a SiLU(g)*u-like spread: a normal with occasional large values."""
+    """fp32 h drawn from N(0, std^2) (the spread of SiLU(g)*u at unit-scale g, u)."""
     return randn_f32((B, d_ff), std, seed)
+
+
+def randn_bf16_device(shape, std: float, seed: int, device="cuda"):
+    """bf16 N(0, std^2) drawn on the GPU with a seeded device generator (for
+    multi-GB weight sets: the chained 32-layer stack and the benchmark's
+    rotating weight copies).  Returns a torch bf16 tensor on `device`."""
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(torch.bfloat16)
+
+
+def stack_layer_weights_device(layer: int, device="cuda"):
+    """W_gate, W_up, W_down of layer `layer` of the 8B 32-layer stack, on the GPU."""
+    d_model, d_ff = LLAMA3_8B
+    base = 3000 + 4 * layer
+    return (randn_bf16_device((d_ff, d_model), 0.02, base + 1, device),
+            randn_bf16_device((d_ff, d_model), 0.02, base + 2, device),
+            randn_bf16_device((d_model, d_ff), 0.02, base + 3, device))

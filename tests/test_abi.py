@@ -1,0 +1,197 @@
+"""The C ABI on the host: symbols, argument checks, the scheduler's table logic.
+
+No test here launches a kernel: every call either fails validation before any
+HIP call or is host-only (dfk_schedule_select and the table functions).
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import swiglu_mlp_amd as dfk
+from swiglu_mlp_amd import Layout, Status
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dfk.h")
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation first.  A is 16-byte aligned, MIS is not.
+A = 0x10000
+MIS = 0x10008
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return dfk.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dfk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exported_set():
+    assert header_functions() == sorted(dfk.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in header_functions():
+        assert hasattr(L, name), f"libdfk.so does not export {name}"
+
+
+def test_strings(L):
+    for s in Status:
+        text = dfk.status_string(s)
+        assert text.startswith("DFK_")
+    assert dfk.status_string(99) == "DFK_ERR_UNKNOWN"
+    names = [dfk.layout_name(l) for l in Layout]
+    assert names == ["auto", "row", "col", "row_valu", "col_valu", "row_mfma", "col_mfma"]
+    assert dfk.layout_name(42) == "invalid"
+    assert "gfx950" in dfk.version()
+
+
+GU_OK = dict(x=A, wg=A, wu=A, h=A, B=1, dm=256, dff=688, layout=0)
+
+
+def gate_up(L, x=A, wg=A, wu=A, h=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_gate_up_silu_mul(x, wg, wu, h, B, dm, dff, layout, None)
+
+
+def down(L, h=A, wd=A, out=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_down_proj(h, wd, out, B, dm, dff, layout, None)
+
+
+def mlp(L, x=A, wg=A, wu=A, wd=A, out=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_swiglu_mlp(x, wg, wu, wd, out, B, dm, dff, layout, None)
+
+
+@pytest.mark.parametrize("fn", [gate_up, down, mlp], ids=["gate_up", "down", "mlp"])
+def test_invalid_arguments(L, fn):
+    import inspect
+    ptrs = [p for p in inspect.signature(fn).parameters if p in ("x", "wg", "wu", "wd", "h", "out")]
+    for p in ptrs:
+        assert fn(L, **{p: NULL}) == Status.INVALID_ARG, p
+        assert fn(L, **{p: MIS}) == Status.MISALIGNED, p
+    assert fn(L, B=0) == Status.INVALID_ARG
+    assert fn(L, B=-3) == Status.INVALID_ARG
+    assert fn(L, dm=0) == Status.INVALID_ARG
+    assert fn(L, dff=-8) == Status.INVALID_ARG
+    assert fn(L, B=257) == Status.UNSUPPORTED
+    assert fn(L, dm=260) == Status.UNSUPPORTED
+    assert fn(L, dff=690) == Status.UNSUPPORTED
+    assert fn(L, dm=65536, dff=32768) == Status.UNSUPPORTED  # d_model*d_ff >= 2^31
+    assert fn(L, layout=7) == Status.INVALID_ARG
+    assert fn(L, layout=-1) == Status.INVALID_ARG
+    # validation order: a null pointer is reported before a bad size
+    assert fn(L, B=0, **{ptrs[0]: NULL}) == Status.INVALID_ARG
+
+
+def test_schedule_select_argument_checks(L):
+    g, d = ctypes.c_int(), ctypes.c_int()
+    assert L.dfk_schedule_select(1, 4096, 14336, None, ctypes.byref(d)) == Status.INVALID_ARG
+    assert L.dfk_schedule_select(1, 4096, 14336, ctypes.byref(g), None) == Status.INVALID_ARG
+    assert L.dfk_schedule_select(0, 4096, 14336, ctypes.byref(g), ctypes.byref(d)) == Status.INVALID_ARG
+    assert L.dfk_schedule_select(300, 4096, 14336, ctypes.byref(g), ctypes.byref(d)) == Status.UNSUPPORTED
+    assert L.dfk_schedule_select(1, 4095, 14336, ctypes.byref(g), ctypes.byref(d)) == Status.UNSUPPORTED
+
+
+# ----------------------------------------------------------------- tables --
+
+def write_table(path, entries, arch="gfx950", fmt="dfk-tuning-v1"):
+    with open(path, "w") as f:
+        json.dump({"format": fmt, "arch": arch, "entries": entries}, f)
+    return str(path)
+
+
+def entry(op, B, dm, dff, winner):
+    return {"op": op, "B": B, "d_model": dm, "d_ff": dff, "winner": winner,
+            "us": {winner: 1.0}}
+
+
+@pytest.fixture
+def restore_table():
+    yield
+    os.environ.pop("DFK_FORCE_LAYOUT", None)
+    try:
+        dfk.dfk_load_tuning_table(None)
+    except dfk.DfkError:
+        pass
+
+
+def test_table_exact_nearest_and_heuristic(tmp_path, restore_table):
+    path = write_table(tmp_path / "t.json", [
+        entry("gate_up", 1, 4096, 14336, "col_valu"),
+        entry("down", 1, 4096, 14336, "row_mfma"),
+        entry("gate_up", 4, 4096, 14336, "row_mfma"),
+        entry("down", 4, 4096, 14336, "col_valu"),
+        entry("gate_up", 16, 4096, 14336, "row_mfma"),
+        entry("down", 16, 4096, 14336, "col_mfma"),
+    ])
+    dfk.dfk_load_tuning_table(path)
+    assert dfk.dfk_tuning_table_source() == path
+    S = dfk.dfk_schedule_select
+    assert S(1, 4096, 14336) == (Layout.COL_VALU, Layout.ROW_MFMA)       # exact
+    assert S(4, 4096, 14336) == (Layout.ROW_MFMA, Layout.COL_VALU)       # exact
+    assert S(2, 4096, 14336) == (Layout.ROW_MFMA, Layout.COL_VALU)       # nearest tuned B >= 2 is 4
+    assert S(9, 4096, 14336) == (Layout.ROW_MFMA, Layout.COL_MFMA)       # -> 16
+    assert S(64, 4096, 14336) == (Layout.ROW_MFMA, Layout.COL_MFMA)      # largest below
+    # a VALU winner from a smaller batch cannot serve B > 8: same traversal, MFMA
+    path2 = write_table(tmp_path / "t2.json", [entry("gate_up", 8, 4096, 14336, "col_valu"),
+                                                entry("down", 8, 4096, 14336, "row_valu")])
+    dfk.dfk_load_tuning_table(path2)
+    assert S(32, 4096, 14336) == (Layout.COL_MFMA, Layout.ROW_MFMA)
+    # untuned shape -> heuristic: VALU rows at small batch, MFMA panels above
+    assert S(1, 2048, 5632) == (Layout.ROW_VALU, Layout.ROW_VALU)
+    assert S(16, 2048, 5632) == (Layout.COL_MFMA, Layout.COL_MFMA)
+    # x too large for the VALU kernel's LDS (B * d_model * 2 > 160 KB) -> MFMA
+    assert S(8, 16384, 1024)[0] == Layout.ROW_MFMA
+
+
+def test_force_layout_env(tmp_path, restore_table):
+    path = write_table(tmp_path / "t.json", [entry("gate_up", 1, 4096, 14336, "row_valu"),
+                                               entry("down", 1, 4096, 14336, "row_mfma")])
+    dfk.dfk_load_tuning_table(path)
+    os.environ["DFK_FORCE_LAYOUT"] = "col"
+    assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.COL_VALU, Layout.COL_MFMA)
+    os.environ["DFK_FORCE_LAYOUT"] = "row"
+    assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.ROW_VALU, Layout.ROW_MFMA)
+
+
+@pytest.mark.parametrize("content", [
+    "not json", '{"format": "dfk-tuning-v1", "arch": "gfx950"}',
+    '{"format": "other", "arch": "gfx950", "entries": []}',
+    '{"format": "dfk-tuning-v1", "arch": "gfx942", "entries": []}',
+    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": [{"op": "gate_up"}]}',
+    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": [{"op": "x", "B": 1, "d_model": 8, "d_ff": 8, "winner": "row_valu"}]}',
+    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": [{"op": "down", "B": 1, "d_model": 8, "d_ff": 8, "winner": "diag"}]}',
+])
+def test_bad_table_falls_back_to_heuristic(tmp_path, content, restore_table):
+    p = tmp_path / "bad.json"
+    p.write_text(content)
+    with pytest.raises(dfk.DfkError) as e:
+        dfk.dfk_load_tuning_table(str(p))
+    assert e.value.status == Status.INVALID_ARG
+    assert dfk.dfk_tuning_table_source() == "heuristic"
+    assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.ROW_VALU, Layout.ROW_VALU)
+
+
+def test_missing_table(tmp_path, restore_table):
+    with pytest.raises(dfk.DfkError):
+        dfk.dfk_load_tuning_table(str(tmp_path / "nope.json"))
+    assert dfk.dfk_tuning_table_source() == "heuristic"
+
+
+def test_installed_table_parses(restore_table):
+    """The table shipped with the package (if any) loads and names only known variants."""
+    if not os.path.exists(dfk.TUNING_TABLE):
+        pytest.skip("no tuning table installed yet")
+    dfk.dfk_load_tuning_table(dfk.TUNING_TABLE)
+    t = json.load(open(dfk.TUNING_TABLE))
+    for e in t["entries"]:
+        g, d = dfk.dfk_schedule_select(e["B"], e["d_model"], e["d_ff"])
+        got = g if e["op"] == "gate_up" else d
+        assert dfk.layout_name(got) == e["winner"]
