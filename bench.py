@@ -1,0 +1,262 @@
+"""Benchmark: decode-stage SwiGLU MLP on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
+                    [--no-cpu-baseline] [--no-sweep]
+
+A step is one call of the whole hot path, dfk_swiglu_mlp (the fused gate-up
+kernel, then the down-projection kernel), on a Llama-3-8B-shaped layer
+(d_model 4096, d_ff 14336) at decode batch B (default 1), with every input
+already resident in HBM.  Weights rotate over 5 seeded sets (5 x 352 MB, far
+beyond the 256 MB Infinity Cache) so every call streams its weights from HBM.
+
+Printed: one JSON line with the metric (us per MLP call; lower is better),
+the dominant kernel's roofline (algorithmic bytes / measured launch duration
+vs the 8 TB/s HBM peak), per-batch figures for B = 1..64, and the fp64 CPU
+oracle timed on the host cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/MLP call + achieved HBM GB/s (% of peak), Llama-3-8B shape, batch 1–64"
+HBM_PEAK_GBPS = 8000.0
+D_MODEL, D_FF = 4096, 14336
+ROTATE = 5
+KERNEL_SOURCE = os.path.join(ROOT, "swiglu_mlp_amd", "csrc", "dfk_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_llama8b_B1_traffic.txt")
+
+
+def gate_up_bytes(B, d_model=D_MODEL, d_ff=D_FF):
+    """Algorithmic HBM bytes of one fused gate-up launch: both weight matrices
+    once, x once, h (fp32) written once."""
+    return 2 * (2 * d_ff * d_model) + 2 * B * d_model + 4 * B * d_ff
+
+
+def down_bytes(B, d_model=D_MODEL, d_ff=D_FF):
+    """W_down once, h (fp32) read once, y (bf16) written once."""
+    return 2 * d_model * d_ff + 4 * B * d_ff + 2 * B * d_model
+
+
+def mlp_bytes(B, d_model=D_MODEL, d_ff=D_FF):
+    return gate_up_bytes(B, d_model, d_ff) + down_bytes(B, d_model, d_ff)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(B):
+    """HBM bytes per gate-up launch from the committed rocprofv3 PMC summary,
+    if it was taken on the current kernel source and batch; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if int(fields.get("batch", -1)) != B:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def make_weights(R, device):
+    from swiglu_mlp_amd import inputs
+    sets = []
+    for r in range(R):
+        base = 6000 + 10 * r
+        sets.append((inputs.randn_bf16_device((D_FF, D_MODEL), 0.02, base + 1, device),
+                     inputs.randn_bf16_device((D_FF, D_MODEL), 0.02, base + 2, device),
+                     inputs.randn_bf16_device((D_MODEL, D_FF), 0.02, base + 3, device)))
+    return sets
+
+
+def _timed(fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` back-to-back calls, bracketed
+    by one pair of HIP events on the current stream (the launch stream)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def time_batch(B, sets, steps, warmup, device):
+    """Per batch B: ms per whole-MLP call (dfk_swiglu_mlp, the step), and ms
+    per launch of each kernel timed back to back on its own.  Weights rotate
+    every call."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import inputs
+
+    x = inputs.randn_bf16_device((B, D_MODEL), 1.0, 6100 + B, device)
+    h = torch.empty((B, D_FF), dtype=torch.float32, device=device)
+    out = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device)
+    gl, dl = dfk.dfk_schedule_select(B, D_MODEL, D_FF)
+    R = len(sets)
+
+    def mlp(i):
+        dfk.dfk_swiglu_mlp(x, *sets[i % R], out)
+
+    def gate_up(i):
+        wg, wu, _ = sets[i % R]
+        dfk.dfk_gate_up_silu_mul(x, wg, wu, h, layout=gl)
+
+    def down(i):
+        dfk.dfk_down_proj(h, sets[i % R][2], out, layout=dl)
+
+    ms_call = _timed(mlp, steps, warmup)
+    ms_gu = _timed(gate_up, steps, warmup)
+    ms_dn = _timed(down, steps, warmup)
+    return ms_call, ms_gu, ms_dn, (dfk.layout_name(gl), dfk.layout_name(dl))
+
+
+def cpu_baseline(sets, budget_s=12.0, max_calls=400):
+    """The fp64 oracle on the host cores: whole-MLP calls at B=1 on weight set 0."""
+    import numpy as np
+    import torch
+    import oracle
+    from swiglu_mlp_amd import inputs
+
+    wg, wu, wd = (t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for t in sets[0])
+    x = inputs.randn_bf16((1, D_MODEL), 1.0, 6101)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = min(cores, 16)  # the host CPU share that goes with one GPU
+    orc = oracle.get()
+    orc.mlp(x, wg, wu, wd, nthreads=cores)  # warm
+    n = 0
+    t0 = time.perf_counter()
+    while n < max_calls and (time.perf_counter() - t0) < budget_s:
+        orc.mlp(x, wg, wu, wd, nthreads=cores)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / n * 1e6, 1), "unit": "µs/MLP call", "cores": cores, "kind": "oracle",
+            "sample": f"{n} whole-MLP calls (all outputs, fp64) at B=1 on one Llama-3-8B-shaped "
+                      f"weight set, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (the reference kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode MLP here runs on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import swiglu_mlp_amd as dfk
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 10}))
+        return
+    dfk.lib()
+    sets = make_weights(ROTATE, device)
+    torch.cuda.synchronize()
+
+    B = args.batch
+    ms_per_step, ms_gu, ms_dn, variants = time_batch(B, sets, args.steps, args.warmup, device)
+    us_per_call = ms_per_step * 1e3
+    gu_us, dn_us = ms_gu * 1e3, ms_dn * 1e3
+    bytes_call = mlp_bytes(B)
+    achieved_call = bytes_call / (us_per_call * 1e-6) / 1e9
+    gu_achieved = gate_up_bytes(B) / (gu_us * 1e-6) / 1e9
+
+    per_batch = {}
+    if not args.no_sweep:
+        for b in (1, 2, 4, 8, 16, 32, 64):
+            t, g, d, v = time_batch(b, sets, 200, 20, device)
+            us = t * 1e3
+            gbps = mlp_bytes(b) / (us * 1e-6) / 1e9
+            per_batch[str(b)] = {"us_per_call": round(us, 2), "GBps": round(gbps, 1),
+                                 "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                                 "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
+                                 "variants": list(v)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_per_call, 3),
+        "unit": "µs/MLP call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"Llama-3-8B-shaped SwiGLU MLP layer, decode batch {B}",
+            "batch": B, "d_model": D_MODEL, "d_ff": D_FF,
+            "weight_sets_rotated": ROTATE,
+            "variants": {"gate_up": variants[0], "down": variants[1]},
+            "parallelism": "single GPU",
+        },
+        "achieved_GBps": round(achieved_call, 1),
+        "frac_of_hbm_peak": round(achieved_call / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_call": bytes_call,
+        "kernel_us": {"gate_up": round(gu_us, 2), "down": round(dn_us, 2)},
+        "roofline": {
+            "kernel": "gate_up (fused gate+up+SiLU*mul)",
+            "bound": "hbm",
+            "achieved": round(gu_achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(B),
+            "algorithmic_bytes_per_launch": gate_up_bytes(B),
+        },
+        "per_batch": per_batch,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sets)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,14 +51,15 @@ extern "C" {
  * mathematics over the same (row-major) storage; they differ only in how the
  * weight matrix is walked, hence only in fp32 summation order.
  *
- *   ROW  row-major traversal: each output row's dot product is owned by one
- *        wavefront, which streams the whole weight row (all of K) and reduces
- *        across its lanes; the epilogue runs in registers.
- *   COL  column-major traversal: the weight matrix is cut into column panels
- *        (K slices); each workgroup streams one panel for many rows and the
- *        per-panel partial sums are combined, in fixed panel order, by the
- *        last workgroup to finish a row block (no float atomics, so results
- *        are run-to-run deterministic).
+ *   ROW  row-major traversal: one wavefront owns each output row's whole dot
+ *        product (all of K): the vector kernels put the 64 lanes along K and
+ *        reduce across them; the matrix-core kernels give a wavefront a
+ *        16-row tile.
+ *   COL  column-major traversal: a workgroup owns a group of rows and its
+ *        wavefronts split the columns (K) of those rows into slices; the
+ *        slices' sums are added in a fixed order through LDS.  More
+ *        wavefronts per row than ROW, for shapes with few or long rows.
+ * Both are run-to-run deterministic (no float atomics).
  *
  * The engine under a traversal is the vector ALU (bf16 dot2 / fp32 FMA, batch
  * below 16) or the matrix cores (MFMA bf16 -> fp32, batch 16 and up, or where
@@ -104,7 +105,10 @@ dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate,
 /*
  * Down projection, a separate kernel (same passage: the down projection stays
  * out of the fused kernel).  out[b,m] = RNE_bf16( sum_n h[b,n] W_down[m,n] ),
- * fp32 accumulation from the fp32 h.
+ * fp32 accumulation from the fp32 h.  The column traversal on the matrix
+ * cores (B <= 16) cuts K into panels across workgroups and adds the panel
+ * sums with a second, small kernel on the same stream; its scratch
+ * (panels * B * d_model * 4 bytes) is library-owned per (device, stream).
  */
 dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out, int B,
                            int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream);

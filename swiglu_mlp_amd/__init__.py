@@ -23,7 +23,9 @@ import os
 from typing import Optional, Tuple
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(PKG_DIR, "libdfk.so")
+# DFK_LIBRARY may name another build of the same library (e.g. one compiled
+# with different tile parameters for a sweep).
+LIBRARY = os.environ.get("DFK_LIBRARY") or os.path.join(PKG_DIR, "libdfk.so")
 TUNING_TABLE = os.path.join(PKG_DIR, "tuning", "gfx950.json")
 
 

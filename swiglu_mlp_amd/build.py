@@ -38,10 +38,10 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, defines=(), build_dir: str = BUILD_DIR) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *HIP_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         # host-only runtime: plain C++ against the HIP runtime headers
         cmd = [hipcc(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
@@ -56,19 +56,20 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libdfk.so; returns the library path."""
+def build(verbose: bool = False, output: str = LIBRARY, defines=(), build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link the library; returns its path.  `defines`
+    (NAME=VALUE strings) override the kernels' compile-time tile parameters."""
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
-        objs = list(pool.map(_compile, SOURCES))
-    tmp = LIBRARY + ".tmp"
+        objs = list(pool.map(lambda s: _compile(s, defines, build_dir), SOURCES))
+    tmp = output + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-ldl"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, output)
     if verbose:
-        print(f"built {LIBRARY}")
-    return LIBRARY
+        print(f"built {output}")
+    return output
 
 
 if __name__ == "__main__":

@@ -15,27 +15,46 @@ enum Op { OP_GATE_UP = 0, OP_DOWN = 1 };
 // Largest batch the VALU kernels are instantiated for.  Above it (and where a
 // VALU kernel's LDS staging would not fit) the MFMA kernels run.
 constexpr int kValuMaxBatch = 8;
-// Dynamic LDS the VALU gate-up kernel may use to keep x resident.
-constexpr size_t kValuLdsLimit = 160 * 1024;
+// LDS of one gfx950 CU: the most a workgroup may ask for (the VALU gate-up
+// kernels keep all of x there).
+constexpr size_t kLdsLimit = 160 * 1024;
+// The VALU down kernels keep all of h in LDS up to this size (two workgroups
+// per CU), else they read it through the caches.
+constexpr size_t kHLdsLimit = 64 * 1024;
+// LDS budget of one h panel of the K-panel down kernel (two workgroups per CU).
+constexpr size_t kPanelLds = 64 * 1024;
 
-// A fully resolved launch: which kernel, how the weight matrix is cut, how
-// much scratch the COL combine needs.
+enum Kind {
+    KIND_GU_VALU_ROW = 0,
+    KIND_GU_VALU_COL = 1,
+    KIND_DN_VALU_ROW = 2,
+    KIND_DN_VALU_COL = 3,
+    KIND_GU_MFMA_ROW = 4,
+    KIND_GU_MFMA_COL = 5,
+    KIND_DN_MFMA_ROW = 6,
+    KIND_DN_MFMA_COL = 7,
+    KIND_DN_MFMA_PANEL = 8  // down col traversal, K panels across workgroups + a reduce kernel
+};
+
+// A fully resolved launch: which kernel and how the weight matrix is cut.
 struct Plan {
     Op op;
     Engine engine;
     Traversal trav;
+    Kind kind;
     int B;
-    int rows;          // output rows: d_ff (gate-up) or d_model (down)
-    int K;             // reduction length: d_model (gate-up) or d_ff (down)
-    int groups;        // row groups (a wave's unit of rows)
-    int splits;        // K panels (1 for ROW)
-    int chunks_per_split;  // 8-element chunks per panel
-    int grid;          // workgroups
-    int block;         // threads per workgroup
-    size_t lds_bytes;  // dynamic LDS per workgroup
-    size_t partial_floats;  // COL scratch: per-panel partial sums
-    size_t counters;        // COL scratch: arrival counters (one per row group)
-    int kernel_id;     // index into the kernel table of the op/engine
+    int rows;            // output rows: d_ff (gate-up) or d_model (down)
+    int K;               // reduction length: d_model (gate-up) or d_ff (down)
+    int rows_per_group;  // rows of one work item
+    int groups;          // work items
+    int grid;            // workgroups
+    int block;           // threads per workgroup
+    size_t lds_bytes;    // dynamic LDS per workgroup
+    bool h_in_lds;       // VALU down: all of h staged in LDS
+    int splits;          // K panels (KIND_DN_MFMA_PANEL), else 1
+    int chunks_per_split;     // 16-byte chunks per panel
+    size_t partial_floats;    // scratch the plan needs (panel partial sums), else 0
+    const void *fn;      // the kernel
 };
 
 // Fill a plan for the given shape, engine and traversal.  Returns false when
@@ -44,12 +63,11 @@ struct Plan {
 bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus,
                Plan *plan);
 
-// Enqueue the kernel of a plan.  `partial` and `counters` must hold the plan's
-// scratch (counters zeroed before first use; the kernel leaves them zeroed).
+// Enqueue the kernel of a plan on `stream`.
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate,
-                          const uint16_t *w_up, float *h, float *partial, unsigned *counters,
-                          hipStream_t stream);
+                          const uint16_t *w_up, float *h, hipStream_t stream);
+// `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y,
-                       float *partial, unsigned *counters, hipStream_t stream);
+                       float *partial, hipStream_t stream);
 
 }  // namespace dfk

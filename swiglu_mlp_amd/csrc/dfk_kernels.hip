@@ -23,11 +23,15 @@
 //     of the down projection is split into bf16 hi + lo and fed as two MFMAs,
 //     which keeps ~16 significant bits of h.
 // Traversals (the row-major / column-major variants of the episode summary)
-//   ROW  each output row's whole dot product belongs to one wave (VALU) or one
-//        workgroup (MFMA, its 4 waves split K and combine through LDS).
-//   COL  the weight matrix is cut into K panels; a panel's partial sums go to
-//        scratch and the last arrival for a row block (an atomic counter)
-//        adds the panels in fixed order and runs the epilogue.  Deterministic.
+//   ROW  one wave owns each output row's whole dot product (VALU: lanes along
+//        K and a DPP reduction; MFMA: a 16-row tile over all of K).
+//   COL  a workgroup owns a group of rows and its waves split the columns (K)
+//        of those rows into contiguous slices; the per-wave sums are added in
+//        wave order through LDS.  The split stays inside one workgroup on
+//        purpose: combining partial sums across workgroups needs agent-scope
+//        release/acquire, which on a multi-XCD gfx950 means writing back and
+//        invalidating an XCD's whole L2 per arrival (measured: it turns a
+//        37 us kernel into 1.5 ms).  Both traversals are deterministic.
 // Every kernel is persistent-style: the grid is sized to the machine and each
 // wave / workgroup walks a strided list of work items.
 
@@ -47,8 +51,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kValuBlock = 512;  // 8 waves
-constexpr int kMfmaBlock = 256;  // 4 waves
-constexpr int kMfmaWaves = kMfmaBlock / kWave;
+constexpr int kMfmaRowBlock = 256;  // 4 waves, one tile group each
 
 // ---------------------------------------------------------------- helpers --
 
@@ -119,22 +122,6 @@ __device__ __forceinline__ void split_hi_lo(f32x4_t a, f32x4_t b, bf16x8_t &hi, 
     }
 }
 
-// Last-arrival protocol of the COL traversal.  Every wave that finished a
-// panel of row group `group` calls this after storing its partials; exactly
-// one caller (the last) gets true, sees every panel's partials, and must
-// reset the counter.  Release/acquire fences at agent scope make the
-// partials visible across XCDs (each XCD has its own L2).
-__device__ __forceinline__ bool arrive_last(unsigned *counter, int panels) {
-    __threadfence();
-    unsigned prev = 0;
-    if ((threadIdx.x & (kWave - 1)) == 0) prev = atomicAdd(counter, 1u);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev == (unsigned)(panels - 1)) {
-        __threadfence();
-        return true;
-    }
-    return false;
-}
 
 // ------------------------------------------------------------- arguments --
 
@@ -143,49 +130,138 @@ struct GateUpArgs {
     const uint16_t *wg;
     const uint16_t *wu;
     float *h;
-    float *partial;
-    unsigned *counters;
-    int B, K, N;   // batch, d_model, d_ff
-    int C;         // 16-byte chunks per weight row (K / 8)
-    int S;         // K panels
-    int CS;        // chunks per panel
-    int groups;    // row groups
-    int items;     // groups * S
+    int B, K, N;  // batch, d_model, d_ff
+    int C;        // 16-byte chunks per weight row (K / 8)
+    int groups;   // work items: row groups (ROW: per wave, COL: per workgroup)
 };
 
 struct DownArgs {
     const float *h;
     const uint16_t *wd;
     uint16_t *y;
-    float *partial;
-    unsigned *counters;
-    int B, K, M;   // batch, d_ff, d_model
-    int C, S, CS, groups, items;
+    int B, K, M;  // batch, d_ff, d_model
+    int C, groups;
 };
 
-// ==================================================== VALU gate-up kernel ==
+// ================================================== VALU building blocks ==
 //
-// Work item = (row group of R neurons, K panel).  The wave streams the R rows
-// of W_gate and the same R rows of W_up over the panel; lane l owns chunks
-// l, l+64, ... (8 elements each); x is resident in LDS for the whole kernel
-// (loaded once per workgroup) and each x chunk read serves 2R weight rows.
+// Lane l of a wave takes chunks c_beg + l, c_beg + l + 64, ... of each weight
+// row it streams: every load instruction moves 64 x 16 B = 1 KB of one row.
+// U groups of loads are in flight per lane; a group past the end of the range
+// is skipped by a wave-uniform branch, and the last partial group clamps its
+// addresses (in bounds) while the lanes past the end skip the arithmetic.
+
+// gate-up: R gate rows and the same R up rows; x from LDS ([B][C] chunks).
 template <int B, int R, int U>
-__global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpArgs a) {
+__device__ __forceinline__ void gu_valu_accumulate(const u32x4_t *const (&rg)[R], const u32x4_t *const (&ru)[R],
+                                                   const u32x4_t *xs, int C, int c_beg, int c_end, int lane,
+                                                   float (&ag)[R][B], float (&au)[R][B]) {
+    for (int c0 = c_beg; c0 < c_end; c0 += kWave * U) {
+        u32x4_t wgv[U][R], wuv[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u == 0 || c0 + kWave * u < c_end) {
+                const int c = min(c0 + kWave * u + lane, c_end - 1);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    wgv[u][r] = load_stream(rg[r] + c);
+                    wuv[u][r] = load_stream(ru[r] + c);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + kWave * u + lane;
+            if (c < c_end) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const u32x4_t xv = xs[b * C + c];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        ag[r][b] = dot8_bf16(wgv[u][r], xv, ag[r][b]);
+                        au[r][b] = dot8_bf16(wuv[u][r], xv, au[r][b]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// down: R rows of W_down; h from LDS (HLDS: all of h, [B][2C] f32x4) or
+// straight from global memory through the caches.
+template <int B, int R, int U, bool HLDS>
+__device__ __forceinline__ void dn_valu_accumulate(const u32x4_t *const (&rd)[R], const f32x4_t *hg,
+                                                   const f32x4_t *hl, int C, int c_beg, int c_end, int lane,
+                                                   float (&acc)[R][B]) {
+    for (int c0 = c_beg; c0 < c_end; c0 += kWave * U) {
+        u32x4_t wv[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u == 0 || c0 + kWave * u < c_end) {
+                const int c = min(c0 + kWave * u + lane, c_end - 1);
+#pragma unroll
+                for (int r = 0; r < R; ++r) wv[u][r] = load_stream(rd[r] + c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + kWave * u + lane;
+            if (c < c_end) {
+                f32x4_t hv[B][2];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const size_t o = (size_t)b * 2 * C + 2 * c;
+                    hv[b][0] = HLDS ? hl[o] : hg[o];
+                    hv[b][1] = HLDS ? hl[o + 1] : hg[o + 1];
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const u32x4_t w = wv[u][r];
+                    const float w0 = bf16_lo(w.x), w1 = bf16_hi(w.x), w2 = bf16_lo(w.y), w3 = bf16_hi(w.y),
+                                w4 = bf16_lo(w.z), w5 = bf16_hi(w.z), w6 = bf16_lo(w.w), w7 = bf16_hi(w.w);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const f32x4_t h0 = hv[b][0], h1 = hv[b][1];
+                        float t = acc[r][b];
+                        t = fmaf(w0, h0.x, t);
+                        t = fmaf(w1, h0.y, t);
+                        t = fmaf(w2, h0.z, t);
+                        t = fmaf(w3, h0.w, t);
+                        t = fmaf(w4, h1.x, t);
+                        t = fmaf(w5, h1.y, t);
+                        t = fmaf(w6, h1.z, t);
+                        t = fmaf(w7, h1.w, t);
+                        acc[r][b] = t;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Stage `n` 16-byte vectors from global memory into LDS (whole workgroup).
+template <typename T>
+__device__ __forceinline__ void stage_lds(T *dst, const T *src, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+    __syncthreads();
+}
+
+// ==================================================== VALU row kernels =====
+//
+// ROW: a wave owns R rows (gate-up: R neurons, i.e. R rows of W_gate and the
+// same R rows of W_up) for the whole of K; lane partials are summed with the
+// DPP butterfly and lane 63 runs the epilogue.  Persistent: wave w takes row
+// groups w, w + total_waves, ...
+
+template <int B, int R, int U>
+__global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs a) {
     extern __shared__ u32x4_t xs[];  // [B][C]
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
-    const int gw = blockIdx.x * waves + threadIdx.x / kWave;
     const int total_waves = gridDim.x * waves;
+    stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
 
-    const u32x4_t *xg = reinterpret_cast<const u32x4_t *>(a.x);
-    for (int i = threadIdx.x; i < B * a.C; i += blockDim.x) xs[i] = xg[i];
-    __syncthreads();
-
-    for (int item = gw; item < a.items; item += total_waves) {
-        const int gi = item / a.S;
-        const int s = item - gi * a.S;
-        const int c_beg = s * a.CS;
-        const int c_end = min(c_beg + a.CS, a.C);
+    for (int gi = blockIdx.x * waves + threadIdx.x / kWave; gi < a.groups; gi += total_waves) {
         const u32x4_t *rg[R];
         const u32x4_t *ru[R];
 #pragma unroll
@@ -199,35 +275,7 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpArgs a) 
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
-
-        for (int c0 = c_beg; c0 < c_end; c0 += kWave * U) {
-            u32x4_t wgv[U][R], wuv[U][R];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                // clamped so every load is in bounds; out-of-panel lanes skip the math
-                const int c = min(c0 + kWave * u + lane, c_end - 1);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    wgv[u][r] = load_stream(rg[r] + c);
-                    wuv[u][r] = load_stream(ru[r] + c);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + kWave * u + lane;
-                if (c < c_end) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        const u32x4_t xv = xs[b * a.C + c];
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            ag[r][b] = dot8_bf16(wgv[u][r], xv, ag[r][b]);
-                            au[r][b] = dot8_bf16(wuv[u][r], xv, au[r][b]);
-                        }
-                    }
-                }
-            }
-        }
+        gu_valu_accumulate<B, R, U>(rg, ru, xs, a.C, 0, a.C, lane, ag, au);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -235,66 +283,27 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_kernel(GateUpArgs a) 
                 ag[r][b] = wave_sum_to_lane63(ag[r][b]);
                 au[r][b] = wave_sum_to_lane63(au[r][b]);
             }
-
-        if (a.S == 1) {
-            if (lane == kWave - 1) {
+        if (lane == kWave - 1) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int n = gi * R + r;
-                    if (n < a.N)
+            for (int r = 0; r < R; ++r) {
+                const int n = gi * R + r;
+                if (n < a.N)
 #pragma unroll
-                        for (int b = 0; b < B; ++b) a.h[(size_t)b * a.N + n] = silu_mul(ag[r][b], au[r][b]);
-                }
-            }
-        } else {
-            constexpr int NV = 2 * R * B;
-            float *p = a.partial + ((size_t)gi * a.S + s) * NV;
-            if (lane == kWave - 1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        p[r * B + b] = ag[r][b];
-                        p[R * B + r * B + b] = au[r][b];
-                    }
-            }
-            if (arrive_last(a.counters + gi, a.S)) {
-                if (lane < R * B) {
-                    const int r = lane / B, b = lane - (lane / B) * B;
-                    const int n = gi * R + r;
-                    const float *q = a.partial + (size_t)gi * a.S * NV;
-                    float g = 0.0f, u = 0.0f;
-                    for (int t = 0; t < a.S; ++t) {
-                        g += q[(size_t)t * NV + lane];
-                        u += q[(size_t)t * NV + R * B + lane];
-                    }
-                    if (n < a.N) a.h[(size_t)b * a.N + n] = silu_mul(g, u);
-                }
-                if (lane == 0) a.counters[gi] = 0u;
+                    for (int b = 0; b < B; ++b) a.h[(size_t)b * a.N + n] = silu_mul(ag[r][b], au[r][b]);
             }
         }
     }
 }
 
-// ======================================================= VALU down kernel ==
-//
-// Work item = (group of R rows of W_down, K panel).  Lane l owns chunks l,
-// l+64, ...; for each chunk it widens 8 bf16 weights per row and does fp32
-// FMAs against 8 fp32 values of h per batch row (h read through the caches;
-// one h read serves R rows).
-template <int B, int R, int U>
-__global__ __launch_bounds__(kValuBlock) void down_valu_kernel(DownArgs a) {
+template <int B, int R, int U, bool HLDS>
+__global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
+    extern __shared__ f32x4_t hs[];  // HLDS: [B][2C]
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
-    const int gw = blockIdx.x * waves + threadIdx.x / kWave;
     const int total_waves = gridDim.x * waves;
-    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);  // [B][2C]
-
-    for (int item = gw; item < a.items; item += total_waves) {
-        const int gi = item / a.S;
-        const int s = item - gi * a.S;
-        const int c_beg = s * a.CS;
-        const int c_end = min(c_beg + a.CS, a.C);
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    if (HLDS) stage_lds(hs, hg, B * 2 * a.C);
+    for (int gi = blockIdx.x * waves + threadIdx.x / kWave; gi < a.groups; gi += total_waves) {
         const u32x4_t *rd[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -306,176 +315,359 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_kernel(DownArgs a) {
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
-        for (int c0 = c_beg; c0 < c_end; c0 += kWave * U) {
-            u32x4_t wv[U][R];
-            f32x4_t hv[U][B][2];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = min(c0 + kWave * u + lane, c_end - 1);
-#pragma unroll
-                for (int r = 0; r < R; ++r) wv[u][r] = load_stream(rd[r] + c);
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    hv[u][b][0] = hg[(size_t)b * 2 * a.C + 2 * c];
-                    hv[u][b][1] = hg[(size_t)b * 2 * a.C + 2 * c + 1];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + kWave * u + lane;
-                if (c < c_end) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const u32x4_t w = wv[u][r];
-                        const float w0 = bf16_lo(w.x), w1 = bf16_hi(w.x), w2 = bf16_lo(w.y),
-                                    w3 = bf16_hi(w.y), w4 = bf16_lo(w.z), w5 = bf16_hi(w.z),
-                                    w6 = bf16_lo(w.w), w7 = bf16_hi(w.w);
-#pragma unroll
-                        for (int b = 0; b < B; ++b) {
-                            const f32x4_t h0 = hv[u][b][0], h1 = hv[u][b][1];
-                            float t = acc[r][b];
-                            t = fmaf(w0, h0.x, t);
-                            t = fmaf(w1, h0.y, t);
-                            t = fmaf(w2, h0.z, t);
-                            t = fmaf(w3, h0.w, t);
-                            t = fmaf(w4, h1.x, t);
-                            t = fmaf(w5, h1.y, t);
-                            t = fmaf(w6, h1.z, t);
-                            t = fmaf(w7, h1.w, t);
-                            acc[r][b] = t;
-                        }
-                    }
-                }
-            }
-        }
+        dn_valu_accumulate<B, R, U, HLDS>(rd, hg, hs, a.C, 0, a.C, lane, acc);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][b] = wave_sum_to_lane63(acc[r][b]);
-
-        if (a.S == 1) {
-            if (lane == kWave - 1) {
+        if (lane == kWave - 1) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int m = gi * R + r;
-                    if (m < a.M)
+            for (int r = 0; r < R; ++r) {
+                const int m = gi * R + r;
+                if (m < a.M)
 #pragma unroll
-                        for (int b = 0; b < B; ++b) a.y[(size_t)b * a.M + m] = to_bf16_rne(acc[r][b]);
-                }
-            }
-        } else {
-            constexpr int NV = R * B;
-            float *p = a.partial + ((size_t)gi * a.S + s) * NV;
-            if (lane == kWave - 1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int b = 0; b < B; ++b) p[r * B + b] = acc[r][b];
-            }
-            if (arrive_last(a.counters + gi, a.S)) {
-                if (lane < R * B) {
-                    const int r = lane / B, b = lane - (lane / B) * B;
-                    const int m = gi * R + r;
-                    const float *q = a.partial + (size_t)gi * a.S * NV;
-                    float v = 0.0f;
-                    for (int t = 0; t < a.S; ++t) v += q[(size_t)t * NV + lane];
-                    if (m < a.M) a.y[(size_t)b * a.M + m] = to_bf16_rne(v);
-                }
-                if (lane == 0) a.counters[gi] = 0u;
+                    for (int b = 0; b < B; ++b) a.y[(size_t)b * a.M + m] = to_bf16_rne(acc[r][b]);
             }
         }
     }
 }
 
-// ==================================================== MFMA gate-up kernel ==
+// ==================================================== VALU col kernels =====
 //
-// Work item = (tile of 16*TR neurons, K panel), owned by a workgroup of 4
-// waves that split the panel's 32-wide K steps into 4 contiguous runs.
-// Lane l: r = l & 15 (tile row for A, batch column for B), q = l >> 4 (which
-// 8-element chunk of the 32-wide K step).  MFMA 16x16x32 bf16:
-//   A[i][k] = W[n0+i][k]   (lane (i, q) holds 8 consecutive k)
-//   B[k][j] = x[b0+j][k]   (same k assignment, so the sum pairs up correctly)
-//   D[i][j] -> lane (j, i/4) element i%4.
-// The 4 waves' accumulators are added in wave order through LDS; wave 0 runs
-// the epilogue (ROW) or stores the panel partials (COL).
-template <int BT, int TR, int U>
-__global__ __launch_bounds__(kMfmaBlock) void gate_up_mfma_kernel(GateUpArgs a) {
-    constexpr int NV = 2 * TR * BT * 4;  // accumulator floats per lane
-    extern __shared__ float red[];       // [waves-1][NV][64]
+// COL: a workgroup owns R rows; its waves split the columns (K) of those rows
+// into contiguous slices, each wave streams its slice of every row with lanes
+// along K, and the waves' DPP-reduced sums are added in wave order through
+// LDS before wave 0 runs the epilogue.  More waves per row than ROW: the
+// choice when rows are few or long.  Persistent over row groups.
+
+template <int B, int R, int U>
+__global__ __launch_bounds__(kValuBlock) void gate_up_valu_col_kernel(GateUpArgs a) {
+    constexpr int NV = 2 * R * B;
+    extern __shared__ u32x4_t smem[];  // x [B][C], then red [waves][NV] floats
+    u32x4_t *xs = smem;
+    float *red = reinterpret_cast<float *>(smem + (size_t)B * a.C);
     const int lane = threadIdx.x & (kWave - 1);
+    const int waves = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
-    const int lr = lane & 15;
-    const int lq = lane >> 4;
+    stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
+    const int cw = (a.C + waves - 1) / waves;
+    const int c_beg = min(wave * cw, a.C);
+    const int c_end = min(c_beg + cw, a.C);
 
-    for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
-        const int gi = item / a.S;
-        const int s = item - gi * a.S;
-        // panel in chunks -> in 32-wide steps (4 chunks each)
-        const int c_beg = s * a.CS;
-        const int c_end = min(c_beg + a.CS, a.C);
-        const int steps = (c_end - c_beg + 3) / 4;
-        const int per_wave = (steps + kMfmaWaves - 1) / kMfmaWaves;
-        const int st_beg = min(wave * per_wave, steps);
-        const int st_end = min(st_beg + per_wave, steps);
-
-        const u32x4_t *pg[TR];
-        const u32x4_t *pu[TR];
+    for (int gi = blockIdx.x; gi < a.groups; gi += gridDim.x) {
+        const u32x4_t *rg[R];
+        const u32x4_t *ru[R];
 #pragma unroll
-        for (int t = 0; t < TR; ++t) {
-            const int n = min(gi * 16 * TR + t * 16 + lr, a.N - 1);
-            pg[t] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
-            pu[t] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+        for (int r = 0; r < R; ++r) {
+            const int n = min(gi * R + r, a.N - 1);
+            rg[r] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
+            ru[r] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
         }
-        const u32x4_t *px[BT];
-        bool bvalid[BT];
+        float ag[R][B], au[R][B];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
+        gu_valu_accumulate<B, R, U>(rg, ru, xs, a.C, c_beg, c_end, lane, ag, au);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                ag[r][b] = wave_sum_to_lane63(ag[r][b]);
+                au[r][b] = wave_sum_to_lane63(au[r][b]);
+            }
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    red[wave * NV + r * B + b] = ag[r][b];
+                    red[wave * NV + R * B + r * B + b] = au[r][b];
+                }
+        }
+        __syncthreads();
+        if (wave == 0 && lane < R * B) {
+            const int r = lane / B, b = lane - (lane / B) * B;
+            float g = 0.0f, u = 0.0f;
+            for (int w = 0; w < waves; ++w) {
+                g += red[w * NV + lane];
+                u += red[w * NV + R * B + lane];
+            }
+            const int n = gi * R + r;
+            if (n < a.N) a.h[(size_t)b * a.N + n] = silu_mul(g, u);
+        }
+        __syncthreads();
+    }
+}
+
+template <int B, int R, int U, bool HLDS>
+__global__ __launch_bounds__(kValuBlock) void down_valu_col_kernel(DownArgs a) {
+    constexpr int NV = R * B;
+    extern __shared__ f32x4_t smem4[];  // HLDS: h [B][2C]; then red [waves][NV] floats
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = blockDim.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    float *red = reinterpret_cast<float *>(smem4 + (HLDS ? (size_t)B * 2 * a.C : 0));
+    if (HLDS) stage_lds(smem4, hg, B * 2 * a.C);
+    const int cw = (a.C + waves - 1) / waves;
+    const int c_beg = min(wave * cw, a.C);
+    const int c_end = min(c_beg + cw, a.C);
+
+    for (int gi = blockIdx.x; gi < a.groups; gi += gridDim.x) {
+        const u32x4_t *rd[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = min(gi * R + r, a.M - 1);
+            rd[r] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K);
+        }
+        float acc[R][B];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+        dn_valu_accumulate<B, R, U, HLDS>(rd, hg, smem4, a.C, c_beg, c_end, lane, acc);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = wave_sum_to_lane63(acc[r][b]);
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int b = 0; b < B; ++b) red[wave * NV + r * B + b] = acc[r][b];
+        }
+        __syncthreads();
+        if (wave == 0 && lane < R * B) {
+            const int r = lane / B, b = lane - (lane / B) * B;
+            float v = 0.0f;
+            for (int w = 0; w < waves; ++w) v += red[w * NV + lane];
+            const int m = gi * R + r;
+            if (m < a.M) a.y[(size_t)b * a.M + m] = to_bf16_rne(v);
+        }
+        __syncthreads();
+    }
+}
+
+// ================================================================ MFMA =====
+//
+// v_mfma_f32_16x16x32_bf16, lane l: r = l & 15, q = l >> 4.
+//   A[i][k]  = W[row0 + i][k]      lane (i, q) holds k = k0 + 8q .. 8q+7
+//   B[k][j]  = operand[b0 + j][k]  lane (j, q) holds the same 8 k
+//   D[i][j]  -> lane (j, i / 4), element i % 4
+// A 32-wide K step is 4 consecutive 16-byte chunks of a row: chunk c of the
+// row goes to lanes with q = c mod 4.  Any fixed assignment of k to
+// (q, element) works as long as A and B agree; this one keeps each weight
+// load instruction at 16 rows x 64 contiguous bytes.  The B operand is read
+// from global memory by the lanes whose batch column exists (x bf16, or fp32
+// h split into bf16 hi + lo on the fly); padded columns are zero.
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One tile group (TR tiles of 16 neurons, gate and up) over K steps
+// [st_beg, st_end).
+template <int BT, int TR, int U>
+__device__ __forceinline__ void gu_mfma_accumulate(const GateUpArgs &a, int row0, int st_beg, int st_end, int lr,
+                                                   int lq, f32x4_t (&accg)[TR][BT], f32x4_t (&accu)[TR][BT]) {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const u32x4_t *pg[TR];
+    const u32x4_t *pu[TR];
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+        const int n = min(row0 + t * 16 + lr, a.N - 1);
+        pg[t] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
+        pu[t] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+    }
+    const u32x4_t *px[BT];
+    bool bvalid[BT];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) {
+        const int b = bt * 16 + lr;
+        bvalid[bt] = b < a.B;
+        px[bt] = reinterpret_cast<const u32x4_t *>(a.x + (size_t)min(b, a.B - 1) * a.K);
+    }
+    for (int st = st_beg; st < st_end; st += U) {
+        u32x4_t ag[U][TR], au[U][TR], bx[U][BT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = min((st + u) * 4 + lq, a.C - 1);
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                ag[u][t] = load_stream(pg[t] + cc);
+                au[u][t] = load_stream(pu[t] + cc);
+            }
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) bx[u][bt] = bvalid[bt] ? px[bt][cc] : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool kv = ((st + u) * 4 + lq < a.C) && (st + u < st_end);
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                const bf16x8_t wa = as_bf16x8(kv ? ag[u][t] : zero);
+                const bf16x8_t wb = as_bf16x8(kv ? au[u][t] : zero);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const bf16x8_t xb = as_bf16x8(kv ? bx[u][bt] : zero);
+                    accg[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb, accg[t][bt], 0, 0, 0);
+                    accu[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, accu[t][bt], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+template <int BT, int TR, int U>
+__device__ __forceinline__ void dn_mfma_accumulate(const DownArgs &a, int row0, int st_beg, int st_end, int lr,
+                                                   int lq, f32x4_t (&acc)[TR][BT]) {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4_t *pw[TR];
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+        const int m = min(row0 + t * 16 + lr, a.M - 1);
+        pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K);
+    }
+    const f32x4_t *ph[BT];
+    bool bvalid[BT];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) {
+        const int b = bt * 16 + lr;
+        bvalid[bt] = b < a.B;
+        ph[bt] = reinterpret_cast<const f32x4_t *>(a.h + (size_t)min(b, a.B - 1) * a.K);
+    }
+    for (int st = st_beg; st < st_end; st += U) {
+        u32x4_t aw[U][TR];
+        f32x4_t hb[U][BT][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = min((st + u) * 4 + lq, a.C - 1);
+#pragma unroll
+            for (int t = 0; t < TR; ++t) aw[u][t] = load_stream(pw[t] + cc);
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                hb[u][bt][0] = bvalid[bt] ? ph[bt][2 * cc] : fzero;
+                hb[u][bt][1] = bvalid[bt] ? ph[bt][2 * cc + 1] : fzero;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool kv = ((st + u) * 4 + lq < a.C) && (st + u < st_end);
+            bf16x8_t hhi[BT], hlo[BT];
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt)
+                split_hi_lo(kv ? hb[u][bt][0] : fzero, kv ? hb[u][bt][1] : fzero, hhi[bt], hlo[bt]);
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                const bf16x8_t wa = as_bf16x8(kv ? aw[u][t] : zero);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hhi[bt], acc[t][bt], 0, 0, 0);
+                    acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hlo[bt], acc[t][bt], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// h[b][n..n+3] = SiLU(g) * u for one lane's four accumulator rows.
+template <int BT, int TR>
+__device__ __forceinline__ void gu_mfma_epilogue(const GateUpArgs &a, int row0, int lr, int lq,
+                                                 const f32x4_t (&accg)[TR][BT], const f32x4_t (&accu)[TR][BT]) {
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+        const int n = row0 + t * 16 + 4 * lq;  // 4 consecutive neurons
 #pragma unroll
         for (int bt = 0; bt < BT; ++bt) {
             const int b = bt * 16 + lr;
-            bvalid[bt] = b < a.B;
-            px[bt] = reinterpret_cast<const u32x4_t *>(a.x + (size_t)min(b, a.B - 1) * a.K);
+            if (b < a.B && n < a.N) {
+                f32x4_t o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[t][bt][e], accu[t][bt][e]);
+                *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
+            }
         }
+    }
+}
+
+template <int BT, int TR>
+__device__ __forceinline__ void dn_mfma_epilogue(const DownArgs &a, int row0, int lr, int lq,
+                                                 const f32x4_t (&acc)[TR][BT]) {
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+        const int m = row0 + t * 16 + 4 * lq;
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) {
+            const int b = bt * 16 + lr;
+            if (b < a.B && m < a.M) {
+                const unsigned lo = to_bf16_rne(acc[t][bt][0]) | ((unsigned)to_bf16_rne(acc[t][bt][1]) << 16);
+                const unsigned hi = to_bf16_rne(acc[t][bt][2]) | ((unsigned)to_bf16_rne(acc[t][bt][3]) << 16);
+                *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------- MFMA row ------
+// A wave owns a tile group of 16*TR rows for the whole of K; no LDS.
+
+template <int BT, int TR, int U>
+__global__ __launch_bounds__(kMfmaRowBlock) void gate_up_mfma_row_kernel(GateUpArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = blockDim.x / kWave;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int steps = (a.C + 3) / 4;
+    for (int tg = blockIdx.x * waves + threadIdx.x / kWave; tg < a.groups; tg += gridDim.x * waves) {
         f32x4_t accg[TR][BT], accu[TR][BT];
 #pragma unroll
         for (int t = 0; t < TR; ++t)
 #pragma unroll
             for (int bt = 0; bt < BT; ++bt) accg[t][bt] = accu[t][bt] = f32x4_t{0, 0, 0, 0};
+        gu_mfma_accumulate<BT, TR, U>(a, tg * 16 * TR, 0, steps, lr, lq, accg, accu);
+        gu_mfma_epilogue<BT, TR>(a, tg * 16 * TR, lr, lq, accg, accu);
+    }
+}
 
-        for (int st = st_beg; st < st_end; st += U) {
-            u32x4_t ag[U][TR], au[U][TR], bx[U][BT];
+template <int BT, int TR, int U>
+__global__ __launch_bounds__(kMfmaRowBlock) void down_mfma_row_kernel(DownArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = blockDim.x / kWave;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int steps = (a.C + 3) / 4;
+    for (int tg = blockIdx.x * waves + threadIdx.x / kWave; tg < a.groups; tg += gridDim.x * waves) {
+        f32x4_t acc[TR][BT];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c_beg + (st + u) * 4 + lq;
-                const int cc = min(c, c_end - 1);
+        for (int t = 0; t < TR; ++t)
 #pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    ag[u][t] = load_stream(pg[t] + cc);
-                    au[u][t] = load_stream(pu[t] + cc);
-                }
-#pragma unroll
-                for (int bt = 0; bt < BT; ++bt) bx[u][bt] = px[bt][cc];
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c_beg + (st + u) * 4 + lq;
-                const bool kv = (c < c_end) && (st + u < st_end);
-                const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, kv ? ag[u][t] : zero);
-                    const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, kv ? au[u][t] : zero);
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
-                        const bf16x8_t xb =
-                            __builtin_bit_cast(bf16x8_t, (kv && bvalid[bt]) ? bx[u][bt] : zero);
-                        accg[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb, accg[t][bt], 0, 0, 0);
-                        accu[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, accu[t][bt], 0, 0, 0);
-                    }
-                }
-            }
-        }
+            for (int bt = 0; bt < BT; ++bt) acc[t][bt] = f32x4_t{0, 0, 0, 0};
+        dn_mfma_accumulate<BT, TR, U>(a, tg * 16 * TR, 0, steps, lr, lq, acc);
+        dn_mfma_epilogue<BT, TR>(a, tg * 16 * TR, lr, lq, acc);
+    }
+}
 
-        // combine the 4 waves in order 0 + 1 + 2 + 3 through LDS
+// ---------------------------------------------------------- MFMA col ------
+// A workgroup owns a tile group; its WAVES waves split the K steps into
+// contiguous slices and their accumulators are added in wave order through
+// LDS; wave 0 runs the epilogue.
+
+template <int BT, int TR, int U, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_col_kernel(GateUpArgs a) {
+    constexpr int NV = 2 * TR * BT * 4;
+    extern __shared__ float red[];  // [WAVES-1][NV][64]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int steps = (a.C + 3) / 4;
+    const int per_wave = (steps + WAVES - 1) / WAVES;
+    const int st_beg = min(wave * per_wave, steps);
+    const int st_end = min(st_beg + per_wave, steps);
+    for (int tg = blockIdx.x; tg < a.groups; tg += gridDim.x) {
+        f32x4_t accg[TR][BT], accu[TR][BT];
+#pragma unroll
+        for (int t = 0; t < TR; ++t)
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) accg[t][bt] = accu[t][bt] = f32x4_t{0, 0, 0, 0};
+        gu_mfma_accumulate<BT, TR, U>(a, tg * 16 * TR, st_beg, st_end, lr, lq, accg, accu);
         if (wave > 0) {
             float *dst = red + (size_t)(wave - 1) * NV * kWave;
             int v = 0;
@@ -492,7 +684,7 @@ __global__ __launch_bounds__(kMfmaBlock) void gate_up_mfma_kernel(GateUpArgs a) 
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int w = 1; w < kMfmaWaves; ++w) {
+            for (int w = 1; w < WAVES; ++w) {
                 const float *src = red + (size_t)(w - 1) * NV * kWave;
                 int v = 0;
 #pragma unroll
@@ -505,148 +697,30 @@ __global__ __launch_bounds__(kMfmaBlock) void gate_up_mfma_kernel(GateUpArgs a) 
                             accu[t][bt][e] += src[(v++) * kWave + lane];
                         }
             }
-            if (a.S == 1) {
-#pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    const int n = gi * 16 * TR + t * 16 + 4 * lq;  // 4 consecutive neurons
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
-                        const int b = bt * 16 + lr;
-                        if (b < a.B && n < a.N) {
-                            f32x4_t o;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[t][bt][e], accu[t][bt][e]);
-                            *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
-                        }
-                    }
-                }
-            } else {
-                float *p = a.partial + ((size_t)gi * a.S + s) * NV * kWave;
-                int v = 0;
-#pragma unroll
-                for (int t = 0; t < TR; ++t)
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            p[(v++) * kWave + lane] = accg[t][bt][e];
-                            p[(v++) * kWave + lane] = accu[t][bt][e];
-                        }
-                if (arrive_last(a.counters + gi, a.S)) {
-                    const float *q = a.partial + (size_t)gi * a.S * NV * kWave;
-#pragma unroll
-                    for (int t = 0; t < TR; ++t) {
-                        const int n = gi * 16 * TR + t * 16 + 4 * lq;
-#pragma unroll
-                        for (int bt = 0; bt < BT; ++bt) {
-                            const int b = bt * 16 + lr;
-                            const int v0 = ((t * BT + bt) * 4) * 2;
-                            f32x4_t o;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float g = 0.0f, u = 0.0f;
-                                for (int pn = 0; pn < a.S; ++pn) {
-                                    const float *qq = q + (size_t)pn * NV * kWave;
-                                    g += qq[(v0 + 2 * e) * kWave + lane];
-                                    u += qq[(v0 + 2 * e + 1) * kWave + lane];
-                                }
-                                o[e] = silu_mul(g, u);
-                            }
-                            if (b < a.B && n < a.N)
-                                *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
-                        }
-                    }
-                    if (lane == 0) a.counters[gi] = 0u;
-                }
-            }
+            gu_mfma_epilogue<BT, TR>(a, tg * 16 * TR, lr, lq, accg, accu);
         }
-        __syncthreads();  // LDS reuse by the next item
+        __syncthreads();  // LDS reuse by the next tile group
     }
 }
 
-// ======================================================= MFMA down kernel ==
-//
-// Same tiling as the MFMA gate-up kernel with one weight matrix: A = W_down
-// tile (16*TR rows of d_model), B = h^T.  Each lane widens 8 fp32 h values,
-// splits them into bf16 hi + lo and issues two MFMAs per tile.
-template <int BT, int TR, int U>
-__global__ __launch_bounds__(kMfmaBlock) void down_mfma_kernel(DownArgs a) {
+template <int BT, int TR, int U, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void down_mfma_col_kernel(DownArgs a) {
     constexpr int NV = TR * BT * 4;
     extern __shared__ float red[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int lr = lane & 15;
-    const int lq = lane >> 4;
-
-    for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
-        const int gi = item / a.S;
-        const int s = item - gi * a.S;
-        const int c_beg = s * a.CS;
-        const int c_end = min(c_beg + a.CS, a.C);
-        const int steps = (c_end - c_beg + 3) / 4;
-        const int per_wave = (steps + kMfmaWaves - 1) / kMfmaWaves;
-        const int st_beg = min(wave * per_wave, steps);
-        const int st_end = min(st_beg + per_wave, steps);
-
-        const u32x4_t *pw[TR];
-#pragma unroll
-        for (int t = 0; t < TR; ++t) {
-            const int m = min(gi * 16 * TR + t * 16 + lr, a.M - 1);
-            pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K);
-        }
-        const f32x4_t *ph[BT];
-        bool bvalid[BT];
-#pragma unroll
-        for (int bt = 0; bt < BT; ++bt) {
-            const int b = bt * 16 + lr;
-            bvalid[bt] = b < a.B;
-            ph[bt] = reinterpret_cast<const f32x4_t *>(a.h + (size_t)min(b, a.B - 1) * a.K);
-        }
+    const int lr = lane & 15, lq = lane >> 4;
+    const int steps = (a.C + 3) / 4;
+    const int per_wave = (steps + WAVES - 1) / WAVES;
+    const int st_beg = min(wave * per_wave, steps);
+    const int st_end = min(st_beg + per_wave, steps);
+    for (int tg = blockIdx.x; tg < a.groups; tg += gridDim.x) {
         f32x4_t acc[TR][BT];
 #pragma unroll
         for (int t = 0; t < TR; ++t)
 #pragma unroll
             for (int bt = 0; bt < BT; ++bt) acc[t][bt] = f32x4_t{0, 0, 0, 0};
-
-        for (int st = st_beg; st < st_end; st += U) {
-            u32x4_t aw[U][TR];
-            f32x4_t hb[U][BT][2];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c_beg + (st + u) * 4 + lq;
-                const int cc = min(c, c_end - 1);
-#pragma unroll
-                for (int t = 0; t < TR; ++t) aw[u][t] = load_stream(pw[t] + cc);
-#pragma unroll
-                for (int bt = 0; bt < BT; ++bt) {
-                    hb[u][bt][0] = ph[bt][2 * cc];
-                    hb[u][bt][1] = ph[bt][2 * cc + 1];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c_beg + (st + u) * 4 + lq;
-                const bool kv = (c < c_end) && (st + u < st_end);
-                const u32x4_t zero = {0u, 0u, 0u, 0u};
-                const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
-                bf16x8_t hhi[BT], hlo[BT];
-#pragma unroll
-                for (int bt = 0; bt < BT; ++bt) {
-                    const bool ok = kv && bvalid[bt];
-                    split_hi_lo(ok ? hb[u][bt][0] : fzero, ok ? hb[u][bt][1] : fzero, hhi[bt], hlo[bt]);
-                }
-#pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, kv ? aw[u][t] : zero);
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
-                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hhi[bt], acc[t][bt], 0, 0, 0);
-                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hlo[bt], acc[t][bt], 0, 0, 0);
-                    }
-                }
-            }
-        }
-
+        dn_mfma_accumulate<BT, TR, U>(a, tg * 16 * TR, st_beg, st_end, lr, lq, acc);
         if (wave > 0) {
             float *dst = red + (size_t)(wave - 1) * NV * kWave;
             int v = 0;
@@ -660,7 +734,7 @@ __global__ __launch_bounds__(kMfmaBlock) void down_mfma_kernel(DownArgs a) {
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int w = 1; w < kMfmaWaves; ++w) {
+            for (int w = 1; w < WAVES; ++w) {
                 const float *src = red + (size_t)(w - 1) * NV * kWave;
                 int v = 0;
 #pragma unroll
@@ -670,133 +744,258 @@ __global__ __launch_bounds__(kMfmaBlock) void down_mfma_kernel(DownArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc[t][bt][e] += src[(v++) * kWave + lane];
             }
-            if (a.S == 1) {
-#pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    const int m = gi * 16 * TR + t * 16 + 4 * lq;
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
-                        const int b = bt * 16 + lr;
-                        if (b < a.B && m < a.M) {
-                            uint16_t *o = a.y + (size_t)b * a.M + m;
-                            const unsigned lo = to_bf16_rne(acc[t][bt][0]) | ((unsigned)to_bf16_rne(acc[t][bt][1]) << 16);
-                            const unsigned hi = to_bf16_rne(acc[t][bt][2]) | ((unsigned)to_bf16_rne(acc[t][bt][3]) << 16);
-                            *reinterpret_cast<uint2 *>(o) = make_uint2(lo, hi);
-                        }
-                    }
-                }
-            } else {
-                float *p = a.partial + ((size_t)gi * a.S + s) * NV * kWave;
-                int v = 0;
-#pragma unroll
-                for (int t = 0; t < TR; ++t)
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) p[(v++) * kWave + lane] = acc[t][bt][e];
-                if (arrive_last(a.counters + gi, a.S)) {
-                    const float *q = a.partial + (size_t)gi * a.S * NV * kWave;
-#pragma unroll
-                    for (int t = 0; t < TR; ++t) {
-                        const int m = gi * 16 * TR + t * 16 + 4 * lq;
-#pragma unroll
-                        for (int bt = 0; bt < BT; ++bt) {
-                            const int b = bt * 16 + lr;
-                            const int v0 = (t * BT + bt) * 4;
-                            float o[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float sum = 0.0f;
-                                for (int pn = 0; pn < a.S; ++pn)
-                                    sum += q[(size_t)pn * NV * kWave + (v0 + e) * kWave + lane];
-                                o[e] = sum;
-                            }
-                            if (b < a.B && m < a.M) {
-                                uint16_t *dst = a.y + (size_t)b * a.M + m;
-                                const unsigned lo = to_bf16_rne(o[0]) | ((unsigned)to_bf16_rne(o[1]) << 16);
-                                const unsigned hi = to_bf16_rne(o[2]) | ((unsigned)to_bf16_rne(o[3]) << 16);
-                                *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
-                            }
-                        }
-                    }
-                    if (lane == 0) a.counters[gi] = 0u;
-                }
-            }
+            dn_mfma_epilogue<BT, TR>(a, tg * 16 * TR, lr, lq, acc);
         }
         __syncthreads();
     }
 }
 
+// ------------------------------------------------------ MFMA K panels -----
+//
+// The down projection's column traversal for small batches: the K columns of
+// W_down are cut into S panels across workgroups.  Workgroup (s, part) stages
+// panel s of h in LDS once -- as bf16 hi/lo MFMA fragments, entry [chunk][b]
+// -- and its waves stream 16*TR-row tiles over that panel, so each h byte
+// crosses L2 once per panel instead of once per row tile.  Panel sums go to
+// partial[s][b][m]; the reduce kernel, next on the same stream, adds the S
+// panels in panel order and rounds to bf16.  Stream order is the only
+// synchronisation (no atomics, no cross-workgroup fences).
+
+template <int BT, int TR, int U>
+__global__ __launch_bounds__(kValuBlock) void down_mfma_panel_kernel(DownArgs a, float *partial, int S, int CS) {
+    extern __shared__ u32x4_t hf[];  // hi plane [CS][B], then lo plane [CS][B]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = blockDim.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int s = blockIdx.x % S;
+    const int part = blockIdx.x / S, parts = gridDim.x / S;
+    const int c_beg = s * CS;
+    const int nch = min(CS, a.C - c_beg);
+    const int steps = (nch + 3) / 4;
+    const size_t plane = (size_t)CS * a.B;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);  // [B][2C]
+    for (int i = threadIdx.x; i < a.B * nch; i += blockDim.x) {
+        const int b = i / nch;
+        const int ci = i - b * nch;
+        const size_t o = (size_t)b * 2 * a.C + 2 * (size_t)(c_beg + ci);
+        bf16x8_t hi, lo;
+        split_hi_lo(hg[o], hg[o + 1], hi, lo);
+        hf[(size_t)ci * a.B + b] = __builtin_bit_cast(u32x4_t, hi);
+        hf[plane + (size_t)ci * a.B + b] = __builtin_bit_cast(u32x4_t, lo);
+    }
+    __syncthreads();
+
+    bool bvalid[BT];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt) bvalid[bt] = bt * 16 + lr < a.B;
+
+    for (int tg = part * waves + wave; tg < a.groups; tg += parts * waves) {
+        const int row0 = tg * 16 * TR;
+        const u32x4_t *pw[TR];
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+            const int m = min(row0 + t * 16 + lr, a.M - 1);
+            pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K + (size_t)c_beg * 8);
+        }
+        f32x4_t acc[TR][BT];
+#pragma unroll
+        for (int t = 0; t < TR; ++t)
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) acc[t][bt] = f32x4_t{0, 0, 0, 0};
+
+        for (int st = 0; st < steps; st += U) {
+            u32x4_t aw[U][TR];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ci = min((st + u) * 4 + lq, nch - 1);
+#pragma unroll
+                for (int t = 0; t < TR; ++t) aw[u][t] = load_stream(pw[t] + ci);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ci = (st + u) * 4 + lq;
+                const bool kv = ci < nch;
+                bf16x8_t hhi[BT], hlo[BT];
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const bool ok = kv && bvalid[bt];
+                    const size_t o = (size_t)ci * a.B + bt * 16 + lr;
+                    hhi[bt] = as_bf16x8(ok ? hf[o] : zero);
+                    hlo[bt] = as_bf16x8(ok ? hf[plane + o] : zero);
+                }
+#pragma unroll
+                for (int t = 0; t < TR; ++t) {
+                    const bf16x8_t wa = as_bf16x8(kv ? aw[u][t] : zero);
+#pragma unroll
+                    for (int bt = 0; bt < BT; ++bt) {
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hhi[bt], acc[t][bt], 0, 0, 0);
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hlo[bt], acc[t][bt], 0, 0, 0);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+            const int m = row0 + t * 16 + 4 * lq;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (b < a.B && m < a.M)
+                    *reinterpret_cast<f32x4_t *>(partial + ((size_t)s * a.B + b) * a.M + m) = acc[t][bt];
+            }
+        }
+    }
+}
+
+// y[i] = RNE_bf16(sum_{s ascending} partial[s][i]) for i < n (n % 4 == 0),
+// four outputs per thread.
+__global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial, uint16_t *y, int S, int n) {
+    const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    f32x4_t v = *reinterpret_cast<const f32x4_t *>(partial + i);
+    for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4_t *>(partial + (size_t)s * n + i);
+    const unsigned lo = to_bf16_rne(v[0]) | ((unsigned)to_bf16_rne(v[1]) << 16);
+    const unsigned hi = to_bf16_rne(v[2]) | ((unsigned)to_bf16_rne(v[3]) << 16);
+    *reinterpret_cast<uint2 *>(y + i) = make_uint2(lo, hi);
+}
+
 // ======================================================== kernel tables ====
 //
-// Per-batch tile parameters.  VALU: R rows (pairs) per wave item, U
-// load-groups in flight per lane.  MFMA: BT batch tiles of 16, TR row tiles
-// of 16 per item, U K-steps per load group.
+// Tile parameters, overridable at compile time (-D) for sweeps.
+//   VALU: R rows (pairs) per item, U load groups in flight per lane.
+//   MFMA: TR row tiles of 16 per item, U K steps per load group, WAVES per
+//         workgroup of the col kernels (their LDS combine needs
+//         (WAVES-1) x NV x 256 bytes).  BT = ceil(B / 16) batch tiles.
+// (defaults from a sweep on the Llama-3-8B layer shape, MI355X)
+#ifndef DFK_GU_VALU_R
+#define DFK_GU_VALU_R(B) 1
+#endif
+#ifndef DFK_GU_VALU_U
+#define DFK_GU_VALU_U(B) 4
+#endif
+#ifndef DFK_DN_VALU_R
+#define DFK_DN_VALU_R(B) ((B) == 1 ? 1 : ((B) == 2 ? 2 : 4))
+#endif
+#ifndef DFK_DN_VALU_U
+#define DFK_DN_VALU_U(B) ((B) <= 2 ? 4 : 1)
+#endif
+#ifndef DFK_GU_MFMA_TR
+#define DFK_GU_MFMA_TR(BT) 1
+#endif
+#ifndef DFK_GU_MFMA_U
+#define DFK_GU_MFMA_U(BT) ((BT) <= 2 ? 4 : ((BT) <= 8 ? 2 : 1))
+#endif
+#ifndef DFK_GU_MFMA_WAVES
+#define DFK_GU_MFMA_WAVES(BT) ((BT) <= 4 ? 8 : 4)
+#endif
+#ifndef DFK_DN_MFMA_TR
+#define DFK_DN_MFMA_TR(BT) 1
+#endif
+#ifndef DFK_DN_MFMA_U
+#define DFK_DN_MFMA_U(BT) ((BT) <= 2 ? 4 : 2)
+#endif
+#ifndef DFK_DN_MFMA_WAVES
+#define DFK_DN_MFMA_WAVES(BT) ((BT) <= 4 ? 8 : 4)
+#endif
+// the down projection's col traversal uses K panels across workgroups up to
+// this batch (h panels in LDS), and the in-workgroup K split above it
+#ifndef DFK_DN_PANEL_MAX_B
+#define DFK_DN_PANEL_MAX_B 16
+#endif
+#ifndef DFK_DN_PANEL_U
+#define DFK_DN_PANEL_U 4
+#endif
 
-template <int B> struct ValuGU { static constexpr int R = (B <= 2) ? 1 : 2; static constexpr int U = (B <= 2) ? 4 : 2; };
-template <int B> struct ValuDn { static constexpr int R = (B <= 2) ? 2 : 4; static constexpr int U = (B <= 4) ? 2 : 1; };
-template <int BT> struct MfmaGU { static constexpr int TR = (BT <= 2) ? 2 : 1; static constexpr int U = (BT <= 2) ? 2 : 1; };
-template <int BT> struct MfmaDn { static constexpr int TR = (BT <= 2) ? 4 : (BT <= 4 ? 2 : 1); static constexpr int U = (BT <= 2) ? 2 : 1; };
+struct KernelInfo {
+    const void *fn;
+    int rows_per_group;
+    int block;
+    int waves_per_item;  // 1: wave items (ROW); block/64: workgroup items (COL)
+    int nv;              // COL combine floats per lane
+};
 
-typedef void (*GateUpFn)(GateUpArgs);
-typedef void (*DownFn)(DownArgs);
+template <int B> KernelInfo gu_valu_row() {
+    constexpr int R = DFK_GU_VALU_R(B), U = DFK_GU_VALU_U(B);
+    return {(const void *)gate_up_valu_row_kernel<B, R, U>, R, kValuBlock, 1, 0};
+}
+template <int B> KernelInfo gu_valu_col() {
+    constexpr int R = DFK_GU_VALU_R(B), U = DFK_GU_VALU_U(B);
+    return {(const void *)gate_up_valu_col_kernel<B, R, U>, R, kValuBlock, kValuBlock / kWave, 2 * R * B};
+}
+template <int B, bool HLDS> KernelInfo dn_valu_row_t() {
+    constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
+    return {(const void *)down_valu_row_kernel<B, R, U, HLDS>, R, kValuBlock, 1, 0};
+}
+template <int B, bool HLDS> KernelInfo dn_valu_col_t() {
+    constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
+    return {(const void *)down_valu_col_kernel<B, R, U, HLDS>, R, kValuBlock, kValuBlock / kWave, R * B};
+}
+template <int B> KernelInfo dn_valu_row() { return dn_valu_row_t<B, false>(); }
+template <int B> KernelInfo dn_valu_row_lds() { return dn_valu_row_t<B, true>(); }
+template <int B> KernelInfo dn_valu_col() { return dn_valu_col_t<B, false>(); }
+template <int B> KernelInfo dn_valu_col_lds() { return dn_valu_col_t<B, true>(); }
 
-template <int B> constexpr GateUpFn gu_valu_fn() { return gate_up_valu_kernel<B, ValuGU<B>::R, ValuGU<B>::U>; }
-template <int B> constexpr DownFn dn_valu_fn() { return down_valu_kernel<B, ValuDn<B>::R, ValuDn<B>::U>; }
-template <int BT> constexpr GateUpFn gu_mfma_fn() { return gate_up_mfma_kernel<BT, MfmaGU<BT>::TR, MfmaGU<BT>::U>; }
-template <int BT> constexpr DownFn dn_mfma_fn() { return down_mfma_kernel<BT, MfmaDn<BT>::TR, MfmaDn<BT>::U>; }
+template <int BT> KernelInfo gu_mfma_row() {
+    constexpr int TR = DFK_GU_MFMA_TR(BT), U = DFK_GU_MFMA_U(BT);
+    return {(const void *)gate_up_mfma_row_kernel<BT, TR, U>, 16 * TR, kMfmaRowBlock, 1, 0};
+}
+template <int BT> KernelInfo dn_mfma_row() {
+    constexpr int TR = DFK_DN_MFMA_TR(BT), U = DFK_DN_MFMA_U(BT);
+    return {(const void *)down_mfma_row_kernel<BT, TR, U>, 16 * TR, kMfmaRowBlock, 1, 0};
+}
+template <int BT> KernelInfo gu_mfma_col() {
+    constexpr int TR = DFK_GU_MFMA_TR(BT), U = DFK_GU_MFMA_U(BT), W = DFK_GU_MFMA_WAVES(BT);
+    return {(const void *)gate_up_mfma_col_kernel<BT, TR, U, W>, 16 * TR, W * kWave, W, 2 * TR * BT * 4};
+}
+template <int BT> KernelInfo dn_mfma_col() {
+    constexpr int TR = DFK_DN_MFMA_TR(BT), U = DFK_DN_MFMA_U(BT), W = DFK_DN_MFMA_WAVES(BT);
+    return {(const void *)down_mfma_col_kernel<BT, TR, U, W>, 16 * TR, W * kWave, W, TR * BT * 4};
+}
 
-static const GateUpFn kGuValu[kValuMaxBatch] = {gu_valu_fn<1>(), gu_valu_fn<2>(), gu_valu_fn<3>(), gu_valu_fn<4>(),
-                                                gu_valu_fn<5>(), gu_valu_fn<6>(), gu_valu_fn<7>(), gu_valu_fn<8>()};
-static const int kGuValuR[kValuMaxBatch] = {ValuGU<1>::R, ValuGU<2>::R, ValuGU<3>::R, ValuGU<4>::R,
-                                            ValuGU<5>::R, ValuGU<6>::R, ValuGU<7>::R, ValuGU<8>::R};
-static const DownFn kDnValu[kValuMaxBatch] = {dn_valu_fn<1>(), dn_valu_fn<2>(), dn_valu_fn<3>(), dn_valu_fn<4>(),
-                                              dn_valu_fn<5>(), dn_valu_fn<6>(), dn_valu_fn<7>(), dn_valu_fn<8>()};
-static const int kDnValuR[kValuMaxBatch] = {ValuDn<1>::R, ValuDn<2>::R, ValuDn<3>::R, ValuDn<4>::R,
-                                            ValuDn<5>::R, ValuDn<6>::R, ValuDn<7>::R, ValuDn<8>::R};
+static const void *kPanelFn = (const void *)down_mfma_panel_kernel<1, 1, DFK_DN_PANEL_U>;
+
+#define DFK_B_TABLE(F) {F<1>(), F<2>(), F<3>(), F<4>(), F<5>(), F<6>(), F<7>(), F<8>()}
+#define DFK_BT_TABLE(F)                                                                                 \
+    {F<1>(), F<2>(), F<3>(), F<4>(), F<5>(), F<6>(), F<7>(), F<8>(), F<9>(), F<10>(), F<11>(), F<12>(), \
+     F<13>(), F<14>(), F<15>(), F<16>()}
 
 constexpr int kMaxBT = 16;  // B <= 256
-static const GateUpFn kGuMfma[kMaxBT] = {
-    gu_mfma_fn<1>(), gu_mfma_fn<2>(), gu_mfma_fn<3>(), gu_mfma_fn<4>(), gu_mfma_fn<5>(), gu_mfma_fn<6>(),
-    gu_mfma_fn<7>(), gu_mfma_fn<8>(), gu_mfma_fn<9>(), gu_mfma_fn<10>(), gu_mfma_fn<11>(), gu_mfma_fn<12>(),
-    gu_mfma_fn<13>(), gu_mfma_fn<14>(), gu_mfma_fn<15>(), gu_mfma_fn<16>()};
-static const int kGuMfmaTR[kMaxBT] = {MfmaGU<1>::TR, MfmaGU<2>::TR, MfmaGU<3>::TR, MfmaGU<4>::TR,
-                                      MfmaGU<5>::TR, MfmaGU<6>::TR, MfmaGU<7>::TR, MfmaGU<8>::TR,
-                                      MfmaGU<9>::TR, MfmaGU<10>::TR, MfmaGU<11>::TR, MfmaGU<12>::TR,
-                                      MfmaGU<13>::TR, MfmaGU<14>::TR, MfmaGU<15>::TR, MfmaGU<16>::TR};
-static const DownFn kDnMfma[kMaxBT] = {
-    dn_mfma_fn<1>(), dn_mfma_fn<2>(), dn_mfma_fn<3>(), dn_mfma_fn<4>(), dn_mfma_fn<5>(), dn_mfma_fn<6>(),
-    dn_mfma_fn<7>(), dn_mfma_fn<8>(), dn_mfma_fn<9>(), dn_mfma_fn<10>(), dn_mfma_fn<11>(), dn_mfma_fn<12>(),
-    dn_mfma_fn<13>(), dn_mfma_fn<14>(), dn_mfma_fn<15>(), dn_mfma_fn<16>()};
-static const int kDnMfmaTR[kMaxBT] = {MfmaDn<1>::TR, MfmaDn<2>::TR, MfmaDn<3>::TR, MfmaDn<4>::TR,
-                                      MfmaDn<5>::TR, MfmaDn<6>::TR, MfmaDn<7>::TR, MfmaDn<8>::TR,
-                                      MfmaDn<9>::TR, MfmaDn<10>::TR, MfmaDn<11>::TR, MfmaDn<12>::TR,
-                                      MfmaDn<13>::TR, MfmaDn<14>::TR, MfmaDn<15>::TR, MfmaDn<16>::TR};
 
-// Blocks of a kernel that fit on one CU (cached; the answer depends only on
-// the kernel, block size and LDS).
+static const KernelInfo kGuValuRow[kValuMaxBatch] = DFK_B_TABLE(gu_valu_row);
+static const KernelInfo kGuValuCol[kValuMaxBatch] = DFK_B_TABLE(gu_valu_col);
+static const KernelInfo kDnValuRow[kValuMaxBatch] = DFK_B_TABLE(dn_valu_row);
+static const KernelInfo kDnValuRowLds[kValuMaxBatch] = DFK_B_TABLE(dn_valu_row_lds);
+static const KernelInfo kDnValuCol[kValuMaxBatch] = DFK_B_TABLE(dn_valu_col);
+static const KernelInfo kDnValuColLds[kValuMaxBatch] = DFK_B_TABLE(dn_valu_col_lds);
+static const KernelInfo kGuMfmaRow[kMaxBT] = DFK_BT_TABLE(gu_mfma_row);
+static const KernelInfo kDnMfmaRow[kMaxBT] = DFK_BT_TABLE(dn_mfma_row);
+static const KernelInfo kGuMfmaCol[kMaxBT] = DFK_BT_TABLE(gu_mfma_col);
+static const KernelInfo kDnMfmaCol[kMaxBT] = DFK_BT_TABLE(dn_mfma_col);
+
+// Blocks of a kernel that fit on one CU (cached per kernel, block and LDS).
 static int blocks_per_cu(const void *fn, int block, size_t lds) {
     static std::mutex mu;
     struct Entry { const void *fn; int block; size_t lds; int n; };
-    static Entry cache[256];
+    static Entry cache[512];
     static int ncache = 0;
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < ncache; ++i)
         if (cache[i].fn == fn && cache[i].block == block && cache[i].lds == lds) return cache[i].n;
-    // allow the kernel the dynamic LDS it asks for (the default cap is below
-    // the 160 KB a gfx950 CU has)
-    if (lds > 0)
-        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kValuLdsLimit);
+    // allow the kernel all the dynamic LDS a gfx950 CU has (the default cap is lower)
+    if (lds > 0) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block, lds) != hipSuccess || n < 1) n = 1;
     (void)hipGetLastError();
-    if (ncache < 256) cache[ncache++] = Entry{fn, block, lds, n};
+    if (ncache < 512) cache[ncache++] = Entry{fn, block, lds, n};
     return n;
 }
 
-static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+static long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *p) {
+bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out) {
     if (B < 1 || d_model < 8 || d_ff < 8 || (d_model % 8) || (d_ff % 8) || cus < 1) return false;
     Plan q{};
     q.op = op;
@@ -805,89 +1004,101 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
     q.B = B;
     q.rows = (op == OP_GATE_UP) ? d_ff : d_model;
     q.K = (op == OP_GATE_UP) ? d_model : d_ff;
-    const int C = q.K / 8;
-    const void *fn = nullptr;
-    int rows_per_group = 1;
-    int waves_per_item_block = 1;  // items per block-wave unit
-    int nv_per_item = 0;           // COL partial floats per item
+    const bool gu = (op == OP_GATE_UP);
+    const bool row = (trav == TRAV_ROW);
+    q.splits = 1;
+    q.chunks_per_split = q.K / 8;
+    KernelInfo ki{};
     if (engine == ENGINE_VALU) {
         if (B > kValuMaxBatch) return false;
-        q.block = kValuBlock;
-        if (op == OP_GATE_UP) {
-            q.lds_bytes = (size_t)B * d_model * 2;
-            if (q.lds_bytes > kValuLdsLimit) return false;
-            rows_per_group = kGuValuR[B - 1];
-            fn = (const void *)kGuValu[B - 1];
-            nv_per_item = 2 * rows_per_group * B;
+        if (gu) {
+            // x stays whole in LDS (+ the col combine buffer)
+            ki = row ? kGuValuRow[B - 1] : kGuValuCol[B - 1];
+            q.lds_bytes = (size_t)B * d_model * 2 + (size_t)(ki.block / kWave) * ki.nv * sizeof(float);
+            if (q.lds_bytes > kLdsLimit) return false;
+            q.kind = row ? KIND_GU_VALU_ROW : KIND_GU_VALU_COL;
         } else {
-            q.lds_bytes = 0;
-            rows_per_group = kDnValuR[B - 1];
-            fn = (const void *)kDnValu[B - 1];
-            nv_per_item = rows_per_group * B;
+            // keep all of h in LDS when it is small, else read it through the caches
+            const size_t whole = (size_t)B * q.K * 4;
+            const bool hlds = whole <= kHLdsLimit;
+            if (row) ki = hlds ? kDnValuRowLds[B - 1] : kDnValuRow[B - 1];
+            else ki = hlds ? kDnValuColLds[B - 1] : kDnValuCol[B - 1];
+            q.lds_bytes = (hlds ? whole : 0) + (size_t)(ki.block / kWave) * ki.nv * sizeof(float);
+            q.kind = row ? KIND_DN_VALU_ROW : KIND_DN_VALU_COL;
+            q.h_in_lds = hlds;
         }
-        q.kernel_id = B - 1;
-        waves_per_item_block = kValuBlock / kWave;  // one item per wave
     } else {
-        const int BT = ceil_div(B, 16);
+        const int BT = (int)ceil_div(B, 16);
         if (BT > kMaxBT) return false;
-        q.block = kMfmaBlock;
-        const int TR = (op == OP_GATE_UP) ? kGuMfmaTR[BT - 1] : kDnMfmaTR[BT - 1];
-        rows_per_group = 16 * TR;
-        const int nv = (op == OP_GATE_UP ? 2 : 1) * TR * BT * 4;
-        q.lds_bytes = (size_t)(kMfmaWaves - 1) * nv * kWave * sizeof(float);
-        fn = (op == OP_GATE_UP) ? (const void *)kGuMfma[BT - 1] : (const void *)kDnMfma[BT - 1];
-        nv_per_item = nv * kWave;
-        q.kernel_id = BT - 1;
-        waves_per_item_block = 1;  // one item per workgroup
+        if (!gu && !row && B <= DFK_DN_PANEL_MAX_B && B <= 16) {
+            // K panels across workgroups: the panel of h (bf16 hi + lo, 32 B per
+            // chunk and batch row) must fit the LDS budget; enough panels to give
+            // every CU a workgroup
+            const int C = q.K / 8;
+            const long max_cs = std::max<long>(4, (long)(kPanelLds / ((size_t)B * 32)) / 4 * 4);
+            const int groups = (int)ceil_div(q.rows, 16);
+            const long wg_per_panel = ceil_div(groups, kValuBlock / kWave);
+            long S = std::max(ceil_div(C, max_cs), ceil_div(cus, wg_per_panel));
+            S = std::min<long>(S, ceil_div(C, 4));
+            long cs = ceil_div(ceil_div(C, S), 4) * 4;
+            S = ceil_div(C, cs);
+            q.kind = KIND_DN_MFMA_PANEL;
+            q.splits = (int)S;
+            q.chunks_per_split = (int)cs;
+            q.block = kValuBlock;
+            q.rows_per_group = 16;
+            q.groups = groups;
+            q.lds_bytes = 2 * (size_t)cs * B * 16;
+            q.grid = (int)(S * wg_per_panel);
+            q.partial_floats = (size_t)S * B * q.rows;
+            q.fn = kPanelFn;
+            *out = q;
+            return true;
+        }
+        if (row) ki = gu ? kGuMfmaRow[BT - 1] : kDnMfmaRow[BT - 1];
+        else ki = gu ? kGuMfmaCol[BT - 1] : kDnMfmaCol[BT - 1];
+        q.lds_bytes = row ? 0 : (size_t)(ki.waves_per_item - 1) * ki.nv * kWave * sizeof(float);
+        q.kind = gu ? (row ? KIND_GU_MFMA_ROW : KIND_GU_MFMA_COL) : (row ? KIND_DN_MFMA_ROW : KIND_DN_MFMA_COL);
     }
-    q.groups = ceil_div(q.rows, rows_per_group);
-    const int occ = blocks_per_cu(fn, q.block, q.lds_bytes);
-    const long slots = (long)cus * occ * waves_per_item_block;  // concurrent items
-    if (trav == TRAV_ROW) {
-        q.splits = 1;
-    } else {
-        // Enough panels to give every item slot ~2 items, but keep each
-        // panel at least 4 KB of a weight row (256 chunks) so loads stay long.
-        int S = ceil_div(2 * slots, q.groups);
-        S = std::max(2, std::min(S, std::max(1, C / 256)));
-        S = std::min(S, C);
-        q.splits = std::max(1, S);
-    }
-    q.chunks_per_split = ceil_div(C, q.splits);
-    // make sure no panel is empty
-    q.splits = ceil_div(C, q.chunks_per_split);
-    const long items = (long)q.groups * q.splits;
-    q.grid = (int)std::max(1L, std::min((long)cus * occ, (items + waves_per_item_block - 1) / waves_per_item_block));
-    if (q.splits > 1) {
-        q.partial_floats = (size_t)items * nv_per_item;
-        q.counters = (size_t)q.groups;
-    }
-    *p = q;
+    q.block = ki.block;
+    q.rows_per_group = ki.rows_per_group;
+    q.groups = (int)ceil_div(q.rows, ki.rows_per_group);
+    const int occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
+    const long items_per_block = (ki.block / kWave) / ki.waves_per_item;
+    q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div(q.groups, items_per_block)));
+    q.fn = ki.fn;
+    *out = q;
     return true;
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
-                          float *h, float *partial, unsigned *counters, hipStream_t stream) {
+                          float *h, hipStream_t stream) {
     GateUpArgs a;
-    a.x = x; a.wg = w_gate; a.wu = w_up; a.h = h; a.partial = partial; a.counters = counters;
-    a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.S = p.splits; a.CS = p.chunks_per_split;
-    a.groups = p.groups; a.items = p.groups * p.splits;
-    GateUpFn fn = (p.engine == ENGINE_VALU) ? kGuValu[p.kernel_id] : kGuMfma[p.kernel_id];
-    void *args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(p.grid), dim3(p.block), args, p.lds_bytes,
-                           stream);
+    a.x = x; a.wg = w_gate; a.wu = w_up; a.h = h;
+    a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.groups = p.groups;
+    void *argv[] = {&a};
+    return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
 }
 
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y, float *partial,
-                       unsigned *counters, hipStream_t stream) {
+                       hipStream_t stream) {
     DownArgs a;
-    a.h = h; a.wd = w_down; a.y = y; a.partial = partial; a.counters = counters;
-    a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.S = p.splits; a.CS = p.chunks_per_split;
-    a.groups = p.groups; a.items = p.groups * p.splits;
-    DownFn fn = (p.engine == ENGINE_VALU) ? kDnValu[p.kernel_id] : kDnMfma[p.kernel_id];
-    void *args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(p.grid), dim3(p.block), args, p.lds_bytes,
-                           stream);
+    a.h = h; a.wd = w_down; a.y = y;
+    a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.groups = p.groups;
+    if (p.kind != KIND_DN_MFMA_PANEL) {
+        void *argv[] = {&a};
+        return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    }
+    if (!partial) return hipErrorInvalidValue;
+    int S = p.splits, CS = p.chunks_per_split;
+    void *argv[] = {&a, &partial, &S, &CS};
+    hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    if (e != hipSuccess) return e;
+    int n = p.B * p.rows;
+    const float *cpartial = partial;
+    void *rargv[] = {&cpartial, &y, &S, &n};
+    return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256), rargv,
+                           0, stream);
 }
 
 }  // namespace dfk

@@ -72,19 +72,17 @@ int device_cus(int dev) {
 
 // ------------------------------------------------------------ workspace ---
 //
-// Per (device, stream): a data buffer [h (swiglu_mlp only)] [COL partial sums]
-// and a separate counter buffer for the COL arrival counters.  Kernels on one
-// stream run in order, so the two kernels of a call share both.  The counter
-// buffer is zeroed when it is allocated and every kernel leaves the counters
-// it used at zero, so it is all-zero between calls.  Growing frees the old
-// buffer (hipFree waits for the device).
+// dfk_swiglu_mlp keeps h (fp32 [B, d_ff]) and the down projection's K-panel
+// partial sums (when its plan uses panels) in a library-owned buffer per
+// (device, stream).  Kernels on one stream run in order, so one buffer per
+// stream is enough; calls on one stream from several host threads serialise
+// on the slot's mutex while they enqueue.  Growing frees the old buffer
+// (hipFree waits for the device).
 
 struct Slot {
     std::mutex mu;
     void *data = nullptr;
-    size_t data_bytes = 0;
-    unsigned *counters = nullptr;
-    size_t n_counters = 0;
+    size_t bytes = 0;
 };
 
 std::mutex g_ws_mu;
@@ -97,52 +95,23 @@ Slot *slot_for(int dev, hipStream_t stream) {
     return p.get();
 }
 
-size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
-
-struct Carve {
-    float *h = nullptr;
-    float *partial = nullptr;
-    unsigned *counters = nullptr;
-};
-
 // Caller holds slot->mu.
-dfk_status_t ensure_workspace(Slot *slot, size_t h_floats, size_t partial_floats, size_t counters,
-                              hipStream_t stream, Carve *c) {
-    const size_t h_bytes = align256(h_floats * sizeof(float));
-    const size_t need = h_bytes + align256(partial_floats * sizeof(float));
-    if (need > slot->data_bytes) {
+dfk_status_t ensure_workspace(Slot *slot, size_t bytes, void **out) {
+    if (bytes > slot->bytes) {
         if (slot->data) {
             if (hipFree(slot->data) != hipSuccess) return DFK_ERR_HIP;
             slot->data = nullptr;
-            slot->data_bytes = 0;
+            slot->bytes = 0;
         }
-        const size_t grow = std::max(need, size_t(1) << 20);
+        const size_t grow = std::max(bytes, size_t(1) << 20);
         if (hipMalloc(&slot->data, grow) != hipSuccess) {
             slot->data = nullptr;
             (void)hipGetLastError();
             return DFK_ERR_OOM;
         }
-        slot->data_bytes = grow;
+        slot->bytes = grow;
     }
-    if (counters > slot->n_counters) {
-        if (slot->counters) {
-            if (hipFree(slot->counters) != hipSuccess) return DFK_ERR_HIP;
-            slot->counters = nullptr;
-            slot->n_counters = 0;
-        }
-        const size_t n = std::max(counters, size_t(4096));
-        if (hipMalloc(reinterpret_cast<void **>(&slot->counters), n * sizeof(unsigned)) != hipSuccess) {
-            slot->counters = nullptr;
-            (void)hipGetLastError();
-            return DFK_ERR_OOM;
-        }
-        if (hipMemsetAsync(slot->counters, 0, n * sizeof(unsigned), stream) != hipSuccess) return DFK_ERR_HIP;
-        slot->n_counters = n;
-    }
-    char *base = static_cast<char *>(slot->data);
-    c->h = h_floats ? reinterpret_cast<float *>(base) : nullptr;
-    c->partial = partial_floats ? reinterpret_cast<float *>(base + h_bytes) : nullptr;
-    c->counters = counters ? slot->counters : nullptr;
+    *out = slot->data;
     return DFK_OK;
 }
 
@@ -447,9 +416,12 @@ dfk_status_t resolve(Op op, dfk_layout_t layout, int B, int d_model, int d_ff, i
 
 void log_plan(const char *what, const Plan &p) {
     if (log_level() < 2) return;
-    std::fprintf(stderr, "[dfk] %s: %s/%s B=%d rows=%d K=%d groups=%d splits=%d grid=%d block=%d lds=%zu\n",
+    std::fprintf(stderr,
+                 "[dfk] %s: %s/%s kind=%d B=%d rows=%d K=%d rows/group=%d groups=%d panels=%d grid=%d block=%d "
+                 "lds=%zu scratch=%zu%s\n",
                  what, p.engine == dfk::ENGINE_VALU ? "valu" : "mfma", p.trav == dfk::TRAV_ROW ? "row" : "col",
-                 p.B, p.rows, p.K, p.groups, p.splits, p.grid, p.block, p.lds_bytes);
+                 (int)p.kind, p.B, p.rows, p.K, p.rows_per_group, p.groups, p.splits, p.grid, p.block, p.lds_bytes,
+                 p.partial_floats * sizeof(float), p.h_in_lds ? " h-in-lds" : "");
 }
 
 // Current device, or an error status.
@@ -508,7 +480,7 @@ dfk_status_t dfk_schedule_select(int B, int d_model, int d_ff, dfk_layout_t *gat
         // the VALU limit: keep its traversal, move it to the matrix cores
         if (g.engine == dfk::ENGINE_VALU && B > dfk::kValuMaxBatch) g.engine = dfk::ENGINE_MFMA;
         if (d.engine == dfk::ENGINE_VALU && B > dfk::kValuMaxBatch) d.engine = dfk::ENGINE_MFMA;
-        if (g.engine == dfk::ENGINE_VALU && (size_t)B * d_model * 2 > dfk::kValuLdsLimit)
+        if (g.engine == dfk::ENGINE_VALU && (size_t)B * d_model * 2 > dfk::kLdsLimit)
             g.engine = dfk::ENGINE_MFMA;
         *gate_up_layout = layout_of(g);
         *down_layout = layout_of(d);
@@ -559,12 +531,7 @@ dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate, con
         Plan p;
         if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
         log_plan("gate_up", p);
-        Slot *slot = slot_for(dev, stream);
-        std::lock_guard<std::mutex> lock(slot->mu);
-        Carve c;
-        if (p.splits > 1 && (st = ensure_workspace(slot, 0, p.partial_floats, p.counters, stream, &c)) != DFK_OK)
-            return st;
-        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, c.partial, c.counters, stream) != hipSuccess) return DFK_ERR_HIP;
+        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {
         return DFK_ERR_HIP;
@@ -583,12 +550,17 @@ dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out
         Plan p;
         if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
         log_plan("down", p);
-        Slot *slot = slot_for(dev, stream);
-        std::lock_guard<std::mutex> lock(slot->mu);
-        Carve c;
-        if (p.splits > 1 && (st = ensure_workspace(slot, 0, p.partial_floats, p.counters, stream, &c)) != DFK_OK)
-            return st;
-        if (dfk::launch_down(p, h, W_down, out, c.partial, c.counters, stream) != hipSuccess) return DFK_ERR_HIP;
+        float *partial = nullptr;
+        Slot *slot = nullptr;
+        std::unique_lock<std::mutex> lock;
+        if (p.partial_floats) {
+            slot = slot_for(dev, stream);
+            lock = std::unique_lock<std::mutex>(slot->mu);
+            void *ws = nullptr;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            partial = static_cast<float *>(ws);
+        }
+        if (dfk::launch_down(p, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {
         return DFK_ERR_HIP;
@@ -612,15 +584,15 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
         if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
         log_plan("gate_up", pg);
         log_plan("down", pd);
-        const size_t partial = std::max(pg.splits > 1 ? pg.partial_floats : 0, pd.splits > 1 ? pd.partial_floats : 0);
-        const size_t counters = std::max(pg.splits > 1 ? pg.counters : 0, pd.splits > 1 ? pd.counters : 0);
         Slot *slot = slot_for(dev, stream);
         std::lock_guard<std::mutex> lock(slot->mu);
-        Carve c;
-        if ((st = ensure_workspace(slot, (size_t)B * d_ff, partial, counters, stream, &c)) != DFK_OK) return st;
-        if (dfk::launch_gate_up(pg, x, W_gate, W_up, c.h, c.partial, c.counters, stream) != hipSuccess)
-            return DFK_ERR_HIP;
-        if (dfk::launch_down(pd, c.h, W_down, out, c.partial, c.counters, stream) != hipSuccess) return DFK_ERR_HIP;
+        void *ws = nullptr;
+        const size_t h_bytes = ((size_t)B * d_ff * sizeof(float) + 255) & ~size_t(255);
+        if ((st = ensure_workspace(slot, h_bytes + pd.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+        float *h = static_cast<float *>(ws);
+        float *partial = pd.partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
+        if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
+        if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {
         return DFK_ERR_HIP;
@@ -642,9 +614,8 @@ dfk_status_t dfk_release_workspace(void) {
             {
                 std::lock_guard<std::mutex> l2(it->second->mu);
                 if (it->second->data && hipFree(it->second->data) != hipSuccess) st = DFK_ERR_HIP;
-                if (it->second->counters && hipFree(it->second->counters) != hipSuccess) st = DFK_ERR_HIP;
                 it->second->data = nullptr;
-                it->second->counters = nullptr;
+                it->second->bytes = 0;
             }
             it = g_ws.erase(it);
         }

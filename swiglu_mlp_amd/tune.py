@@ -1,0 +1,240 @@
+"""Profiler-driven tuning of the row / column kernel variants.
+
+    python -m swiglu_mlp_amd.tune [--shapes 4096x14336,...] [--batches 1,2,4,...]
+                                  [--timer rocprof|events] [--out PATH]
+
+For every (d_model, d_ff) shape, batch B and op (gate_up, down), each variant
+that can run the shape (row_valu, col_valu, row_mfma, col_mfma) is launched
+back to back with rotating weight copies (at least 1.5 GB of distinct weights,
+so every launch streams from HBM rather than the 256 MB Infinity Cache).  The
+winner is the variant with the lowest median kernel time; variants within 2 %
+of the best count as a tie and the row variant wins a tie.  The result is the
+JSON table that dfk_schedule_select reads.
+
+Timers:
+  rocprof  (default) the worker runs under `rocprofv3 --kernel-trace` and the
+           per-dispatch kernel durations come from the profiler's trace;
+  events   HIP events around groups of back-to-back launches (no profiler).
+
+This is the runtime scheduling across row-major and column-major variants of
+"Deep Kernel Fusion for Transformer Decoding" (podcast episode page, episode
+summary), with the profiler as the measuring instrument.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import math
+import os
+import shutil
+import statistics
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_SHAPES = [(2048, 5632), (3072, 8192), (4096, 14336), (5120, 13824), (8192, 28672)]
+DEFAULT_BATCHES = [1, 2, 4, 8, 16, 32, 64]
+VARIANTS = ["row_valu", "col_valu", "row_mfma", "col_mfma"]
+TIE = 0.02
+ROTATE_BYTES = 1.5e9
+
+
+def layer_bytes(d_model, d_ff):
+    return 3 * d_model * d_ff * 2
+
+
+def runnable(variant, op, B, d_model):
+    if variant.endswith("valu"):
+        if B > 8:
+            return False
+        if op == "gate_up" and B * d_model * 2 > 160 * 1024:
+            return False
+    return True
+
+
+def plan_blocks(shapes, batches, reps):
+    """The launch sequence: (shape, B, op, variant, reps) blocks in order."""
+    blocks = []
+    for (dm, dff) in shapes:
+        for B in batches:
+            for op in ("gate_up", "down"):
+                for v in VARIANTS:
+                    if runnable(v, op, B, dm):
+                        blocks.append({"d_model": dm, "d_ff": dff, "B": B, "op": op, "variant": v, "reps": reps})
+    return blocks
+
+
+def run_worker(blocks, warmup, use_events):
+    """Launch every block; returns per-block event timings (ms per launch) if asked."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import Layout, inputs
+
+    dev = torch.device("cuda:0")
+    dfk.lib()
+    layout_of = {"row_valu": Layout.ROW_VALU, "col_valu": Layout.COL_VALU,
+                 "row_mfma": Layout.ROW_MFMA, "col_mfma": Layout.COL_MFMA}
+    results = []
+    cur_shape, sets = None, None
+    for blk in blocks:
+        shape = (blk["d_model"], blk["d_ff"])
+        if shape != cur_shape:
+            sets = None
+            torch.cuda.empty_cache()
+            dm, dff = shape
+            R = max(2, math.ceil(ROTATE_BYTES / layer_bytes(dm, dff)))
+            sets = [(inputs.randn_bf16_device((dff, dm), 0.02, 9000 + 10 * r + 1, dev),
+                     inputs.randn_bf16_device((dff, dm), 0.02, 9000 + 10 * r + 2, dev),
+                     inputs.randn_bf16_device((dm, dff), 0.02, 9000 + 10 * r + 3, dev)) for r in range(R)]
+            cur_shape = shape
+        dm, dff = shape
+        B = blk["B"]
+        x = inputs.randn_bf16_device((B, dm), 1.0, 9500 + B, dev)
+        h = torch.randn((B, dff), device=dev, dtype=torch.float32)
+        y = torch.empty((B, dm), device=dev, dtype=torch.bfloat16)
+        lay = layout_of[blk["variant"]]
+        R = len(sets)
+        if blk["op"] == "gate_up":
+            def call(i):
+                wg, wu, _ = sets[i % R]
+                dfk.dfk_gate_up_silu_mul(x, wg, wu, h, layout=lay)
+        else:
+            def call(i):
+                dfk.dfk_down_proj(h, sets[i % R][2], y, layout=lay)
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        times = []
+        if use_events:
+            group = 10
+            for g in range(max(1, blk["reps"] // group)):
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                for i in range(group):
+                    call(g * group + i)
+                e.record()
+                e.synchronize()
+                times.append(s.elapsed_time(e) / group)
+        else:
+            # marker launches are not needed: the parent maps dispatches to
+            # blocks by order (warmup + reps per block)
+            for i in range(blk["reps"]):
+                call(warmup + i)
+            torch.cuda.synchronize()
+        results.append(times)
+    return results
+
+
+def parse_rocprof(outdir):
+    """One record per library call, in dispatch order: list of (name, ns).
+
+    A call is one kernel, except the down projection's K-panel variant, whose
+    panel kernel is followed by a reduce kernel: that call's time runs from
+    the panel kernel's start to the reduce kernel's end (the gap included)."""
+    files = glob.glob(os.path.join(outdir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise RuntimeError(f"no kernel_trace.csv under {outdir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                if "dfk::" not in name:
+                    continue
+                rows.append((int(r.get("Dispatch_Id", 0)), int(r["Start_Timestamp"]),
+                             int(r["End_Timestamp"]), name))
+    rows.sort()
+    calls = []
+    for _, start, end, name in rows:
+        if "panel_reduce_kernel" in name and calls:
+            first_name, first_start, _ = calls[-1]
+            calls[-1] = (first_name, first_start, end)
+        else:
+            calls.append((name, start, end))
+    return [(n, e - s) for n, s, e in calls]
+
+
+def choose(timings_us):
+    """Winner by median; within TIE of the best, prefer a row variant."""
+    best = min(timings_us.values())
+    close = [v for v, t in timings_us.items() if t <= best * (1 + TIE)]
+    for v in ("row_valu", "row_mfma"):
+        if v in close:
+            return v
+    return min(timings_us, key=timings_us.get)
+
+
+def build_table(blocks, per_block_us):
+    table = {}
+    for blk, us in zip(blocks, per_block_us):
+        key = (blk["op"], blk["B"], blk["d_model"], blk["d_ff"])
+        table.setdefault(key, {})[blk["variant"]] = round(us, 3)
+    entries = []
+    for (op, B, dm, dff), t in sorted(table.items(), key=lambda kv: (kv[0][2], kv[0][3], kv[0][1], kv[0][0])):
+        entries.append({"op": op, "B": B, "d_model": dm, "d_ff": dff, "winner": choose(t), "us": t})
+    return entries
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--shapes", default=",".join(f"{a}x{b}" for a, b in DEFAULT_SHAPES))
+    ap.add_argument("--batches", default=",".join(map(str, DEFAULT_BATCHES)))
+    ap.add_argument("--reps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--timer", choices=["rocprof", "events"], default="rocprof")
+    ap.add_argument("--out", default=os.path.join(PKG, "tuning", "gfx950.json"))
+    ap.add_argument("--worker", help=argparse.SUPPRESS)
+    args = ap.parse_args()
+
+    shapes = [tuple(int(v) for v in s.split("x")) for s in args.shapes.split(",") if s]
+    batches = [int(b) for b in args.batches.split(",") if b]
+    blocks = plan_blocks(shapes, batches, args.reps)
+
+    if args.worker:  # child under rocprofv3: launch only
+        run_worker(blocks, args.warmup, use_events=False)
+        return
+
+    if args.timer == "events":
+        res = run_worker(blocks, args.warmup, use_events=True)
+        per_block = [statistics.median(t) * 1e3 for t in res]
+    else:
+        rocprof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+        outdir = tempfile.mkdtemp(prefix="dfk_tune_", dir=os.environ.get("TMPDIR", "/tmp"))
+        cmd = [rocprof, "--kernel-trace", "--output-format", "csv", "-d", outdir, "-o", "tune", "--",
+               sys.executable, "-m", "swiglu_mlp_amd.tune", "--worker", "1", "--shapes", args.shapes,
+               "--batches", args.batches, "--reps", str(args.reps), "--warmup", str(args.warmup)]
+        print("running:", " ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, cwd=ROOT)
+        disp = parse_rocprof(outdir)
+        expect = sum(args.warmup + b["reps"] for b in blocks)
+        if len(disp) != expect:
+            raise RuntimeError(f"expected {expect} library calls in the trace, found {len(disp)}")
+        per_block, i = [], 0
+        for b in blocks:
+            durs = [d for _, d in disp[i + args.warmup:i + args.warmup + b["reps"]]]
+            per_block.append(statistics.median(durs) / 1e3)
+            i += args.warmup + b["reps"]
+        shutil.rmtree(outdir, ignore_errors=True)
+
+    entries = build_table(blocks, per_block)
+    out = {"format": "dfk-tuning-v1", "arch": "gfx950", "timer": args.timer,
+           "tie_rule": f"within {int(TIE * 100)}% of the best median -> row variant",
+           "entries": entries}
+    os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    for e in entries:
+        ts = " ".join(f"{k}={v:8.2f}" for k, v in e["us"].items())
+        print(f"{e['op']:8s} B={e['B']:3d} {e['d_model']}x{e['d_ff']}: {e['winner']:9s} | {ts}", flush=True)
+    print(f"wrote {args.out} ({len(entries)} entries)")
+
+
+if __name__ == "__main__":
+    main()
