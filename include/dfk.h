@@ -96,7 +96,9 @@ typedef enum {
  *     g = sum_k x[b,k] W_gate[n,k],  u = sum_k x[b,k] W_up[n,k],
  *     h[b,n] = g / (1 + exp(-g)) * u
  * with fp32 accumulation; h is written in fp32 (not rounded to bf16).
- * Each weight matrix is read from HBM once per call; g and u never touch HBM.
+ * Each weight matrix is read from HBM once per call, and g and u never touch
+ * HBM: they stay in registers (and LDS, where the waves of one workgroup split
+ * K) until SiLU * u is written.  One launch per call; no scratch memory.
  */
 dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate,
                                   const uint16_t *W_up, float *h, int B, int d_model,
@@ -106,9 +108,10 @@ dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate,
  * Down projection, a separate kernel (same passage: the down projection stays
  * out of the fused kernel).  out[b,m] = RNE_bf16( sum_n h[b,n] W_down[m,n] ),
  * fp32 accumulation from the fp32 h.  The column traversal on the matrix
- * cores (B <= 16) cuts K into panels across workgroups and adds the panel
- * sums with a second, small kernel on the same stream; its scratch
+ * cores for 9 <= B <= 16 cuts K into panels across workgroups and adds the
+ * panel sums with a second, small kernel on the same stream; its scratch
  * (panels * B * d_model * 4 bytes) is library-owned per (device, stream).
+ * Every other variant is one launch with no scratch memory.
  */
 dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out, int B,
                            int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream);

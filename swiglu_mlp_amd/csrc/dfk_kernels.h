@@ -33,7 +33,9 @@ enum Kind {
     KIND_GU_MFMA_COL = 5,
     KIND_DN_MFMA_ROW = 6,
     KIND_DN_MFMA_COL = 7,
-    KIND_DN_MFMA_PANEL = 8  // down col traversal, K panels across workgroups + a reduce kernel
+    KIND_DN_MFMA_PANEL = 8,  // down col traversal, K panels across workgroups + a reduce kernel
+    KIND_GU_MFMA_LT = 10,    // gate-up, weights streamed through a wave-private LDS transpose
+    KIND_DN_MFMA_LT = 11
 };
 
 // A fully resolved launch: which kernel and how the weight matrix is cut.
@@ -51,7 +53,7 @@ struct Plan {
     int block;           // threads per workgroup
     size_t lds_bytes;    // dynamic LDS per workgroup
     bool h_in_lds;       // VALU down: all of h staged in LDS
-    int splits;          // K panels (KIND_DN_MFMA_PANEL), else 1
+    int splits;          // K panels (panel kinds), else 1
     int chunks_per_split;     // 16-byte chunks per panel
     size_t partial_floats;    // scratch the plan needs (panel partial sums), else 0
     const void *fn;      // the kernel
@@ -64,8 +66,9 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
                Plan *plan);
 
 // Enqueue the kernel of a plan on `stream`.
+// `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate,
-                          const uint16_t *w_up, float *h, hipStream_t stream);
+                          const uint16_t *w_up, float *h, float *partial, hipStream_t stream);
 // `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y,
                        float *partial, hipStream_t stream);

@@ -50,7 +50,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kValuBlock = 512;  // 8 waves
+#ifndef DFK_VALU_BLOCK
+#define DFK_VALU_BLOCK 512
+#endif
+constexpr int kValuBlock = DFK_VALU_BLOCK;  // 8 waves
 constexpr int kMfmaRowBlock = 256;  // 4 waves, one tile group each
 
 // ---------------------------------------------------------------- helpers --
@@ -608,6 +611,335 @@ __device__ __forceinline__ void dn_mfma_epilogue(const DownArgs &a, int row0, in
     }
 }
 
+// ------------------------------------------------- MFMA, LDS-transposed -----
+//
+// Streaming weights at full HBM rate needs few rows per load instruction: on
+// MI355X a 16-row x 64-byte load (the MFMA A-fragment shape) streams ~20 %
+// slower than 2 rows x 512 bytes.  These kernels load each block of a 16-row
+// weight tile (16 rows x 256 elements) as 8 instructions of 2 rows x 512 B,
+// park it in a wave-private, bank-padded LDS tile, and read it back in MFMA
+// A-fragment order while the next block's loads are in flight.  A workgroup
+// owns WAVES / KSPLIT tiles; the KSPLIT waves of a tile take contiguous runs
+// of its blocks and are combined through LDS (KSPLIT = 1: the row traversal).
+
+// A block is 16 rows x KBC chunks of 16 B (KBC = 32: 256 elements, loaded as
+// 8 instructions of 2 rows x 512 B; KBC = 64: 512 elements, 16 instructions
+// of 1 row x 1 KB).  The LDS tile pitch is KBC + 1 chunks (bank padding).
+template <int KBC> struct Lt {
+    static constexpr int kRowsPerInst = 64 / KBC;
+    static constexpr int kInsts = 16 / kRowsPerInst;
+    static constexpr int kPitch = KBC + 1;
+    static constexpr int kTile = 16 * kPitch;  // 16-byte chunks of LDS per matrix per wave
+    static constexpr int kSteps = KBC / 4;     // MFMA K steps per block
+
+    // Issue the loads of block kb (rows and chunks clamped into the matrix).
+    static __device__ __forceinline__ void load(u32x4_t (&v)[kInsts], const uint16_t *w, int K, int C, int row0,
+                                                int rows, int kb, int lane) {
+        const int c = min(kb * KBC + lane % KBC, C - 1);
+#pragma unroll
+        for (int i = 0; i < kInsts; ++i) {
+            const int row = min(row0 + i * kRowsPerInst + lane / KBC, rows - 1);
+            v[i] = load_stream(reinterpret_cast<const u32x4_t *>(w + (size_t)row * K) + c);
+        }
+    }
+    // Park block kb in the wave's LDS tile, zeroing chunks past the row end.
+    static __device__ __forceinline__ void store(u32x4_t *lt, const u32x4_t (&v)[kInsts], int kb, int C, int lane) {
+        const bool ok = kb * KBC + lane % KBC < C;
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kInsts; ++i) lt[(i * kRowsPerInst + lane / KBC) * kPitch + lane % KBC] = ok ? v[i] : zero;
+    }
+    // A fragment of step j (chunks 4j..4j+3 of the block): lane (r, q) -> row r, chunk 4j + q.
+    static __device__ __forceinline__ bf16x8_t frag(const u32x4_t *lt, int j, int lr, int lq) {
+        return as_bf16x8(lt[lr * kPitch + 4 * j + lq]);
+    }
+};
+
+// The B operand (x, or h as bf16 hi + lo) is read as MFMA B fragments straight
+// from global memory (it is small and L2-resident).  Loads return in issue
+// order, so a fragment load issued after the next weight block would make the
+// wave wait for that whole block: for BT <= kPreBT the fragments of a whole
+// block are issued before the next block's weights (one register buffer),
+// otherwise one step ahead.  Fragment reads are never predicated: rows past B
+// read row B - 1 (their output columns are dropped) and chunks past the row
+// end read the last chunk, masked to zero in the tail block only.
+template <int BT, int KSPLIT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpArgs a) {
+    using L = Lt<32>;
+    constexpr int KBC = 32;
+    constexpr bool kPre = BT <= 2;
+    constexpr int XS = kPre ? L::kSteps : 2;
+    constexpr int TPW = WAVES / KSPLIT;  // tiles per workgroup
+    constexpr int NV = 2 * BT * 4;
+    extern __shared__ u32x4_t smem[];    // [WAVES][2][L::kTile], then red [WAVES][NV][64] floats
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int slot = wave / KSPLIT, ks = wave - slot * KSPLIT;
+    u32x4_t *ltg = smem + (size_t)wave * 2 * L::kTile;
+    u32x4_t *ltu = ltg + L::kTile;
+    float *red = reinterpret_cast<float *>(smem + (size_t)WAVES * 2 * L::kTile);
+    const int nb = (a.C + KBC - 1) / KBC;
+    const int per = (nb + KSPLIT - 1) / KSPLIT;
+    const int kb_beg = min(ks * per, nb), kb_end = min(kb_beg + per, nb);
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const u32x4_t *px[BT];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt)
+        px[bt] = reinterpret_cast<const u32x4_t *>(a.x + (size_t)min(bt * 16 + lr, a.B - 1) * a.K);
+    const int wg_items = (a.groups + TPW - 1) / TPW;
+
+    for (int g = blockIdx.x; g < wg_items; g += gridDim.x) {
+        const int tile = g * TPW + slot;
+        const bool active = tile < a.groups;
+        const int row0 = tile * 16;
+        f32x4_t accg[BT], accu[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) accg[bt] = accu[bt] = f32x4_t{0, 0, 0, 0};
+
+        u32x4_t xf[XS][BT];
+        auto load_x = [&](int kb, int j, u32x4_t (&xb)[BT]) {
+            const int c = min(kb * KBC + 4 * j + lq, a.C - 1);
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) xb[bt] = px[bt][c];
+        };
+        auto load_block = [&](int kb) {
+            if constexpr (kPre) {
+#pragma unroll
+                for (int j = 0; j < L::kSteps; ++j) load_x(kb, j, xf[j]);
+            } else {
+                load_x(kb, 0, xf[0]);
+            }
+        };
+        auto compute = [&](int kb) {
+            const bool tail = (kb + 1) * KBC > a.C;
+#pragma unroll
+            for (int j = 0; j < L::kSteps; ++j) {
+                const int slotj = kPre ? j : (j & 1);
+                if constexpr (!kPre) {
+                    if (j + 1 < L::kSteps) load_x(kb, j + 1, xf[(j + 1) & 1]);
+                }
+                const bool cok = !tail || kb * KBC + 4 * j + lq < a.C;
+                const bf16x8_t ag = L::frag(ltg, j, lr, lq);
+                const bf16x8_t au = L::frag(ltu, j, lr, lq);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const bf16x8_t xb = as_bf16x8(cok ? xf[slotj][bt] : zero);
+                    accg[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb, accg[bt], 0, 0, 0);
+                    accu[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb, accu[bt], 0, 0, 0);
+                }
+            }
+        };
+        if (active && kb_beg < kb_end) {
+            u32x4_t vg0[L::kInsts], vu0[L::kInsts], vg1[L::kInsts], vu1[L::kInsts];
+            auto load_w = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
+                L::load(vg, a.wg, a.K, a.C, row0, a.N, kb, lane);
+                L::load(vu, a.wu, a.K, a.C, row0, a.N, kb, lane);
+            };
+            auto step = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
+                L::store(ltg, vg, kb, a.C, lane);
+                L::store(ltu, vu, kb, a.C, lane);
+                if constexpr (!kPre) load_block(kb);
+                compute(kb);
+            };
+            // Software pipeline, one weight block ahead.  The steady loop has
+            // no conditional loads, so every wait is for the oldest block only.
+            if constexpr (kPre) load_block(kb_beg);
+            load_w(vg0, vu0, kb_beg);
+            int kb = kb_beg;
+            for (; kb + 2 < kb_end; kb += 2) {
+                load_w(vg1, vu1, kb + 1);
+                step(vg0, vu0, kb);
+                if constexpr (kPre) load_block(kb + 1);
+                load_w(vg0, vu0, kb + 2);
+                step(vg1, vu1, kb + 1);
+                if constexpr (kPre) load_block(kb + 2);
+            }
+            if (kb + 1 < kb_end) {
+                load_w(vg1, vu1, kb + 1);
+                step(vg0, vu0, kb);
+                if constexpr (kPre) load_block(kb + 1);
+                step(vg1, vu1, kb + 1);
+            } else {
+                step(vg0, vu0, kb);
+            }
+        }
+        if (KSPLIT > 1) {
+            if (ks > 0) {
+                float *dst = red + (size_t)wave * NV * kWave;
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dst[((bt * 4 + e) * 2) * kWave + lane] = accg[bt][e];
+                        dst[((bt * 4 + e) * 2 + 1) * kWave + lane] = accu[bt][e];
+                    }
+            }
+            __syncthreads();
+            if (ks == 0) {
+#pragma unroll
+                for (int w = 1; w < KSPLIT; ++w) {
+                    const float *src = red + (size_t)(wave + w) * NV * kWave;
+#pragma unroll
+                    for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            accg[bt][e] += src[((bt * 4 + e) * 2) * kWave + lane];
+                            accu[bt][e] += src[((bt * 4 + e) * 2 + 1) * kWave + lane];
+                        }
+                }
+            }
+            __syncthreads();
+        }
+        if (ks == 0 && active) {
+            const int n = row0 + 4 * lq;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (b < a.B && n < a.N) {
+                    f32x4_t o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
+                }
+            }
+        }
+    }
+}
+
+template <int BT, int KSPLIT, int WAVES, int KBC>
+__global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a) {
+    using L = Lt<KBC>;
+    constexpr bool kPre = BT <= 1;
+    constexpr int HS = kPre ? L::kSteps : 2;
+    constexpr int TPW = WAVES / KSPLIT;
+    constexpr int NV = BT * 4;
+    extern __shared__ u32x4_t smem[];    // [WAVES][L::kTile], then red [WAVES][NV][64] floats
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int slot = wave / KSPLIT, ks = wave - slot * KSPLIT;
+    u32x4_t *ltw = smem + (size_t)wave * L::kTile;
+    float *red = reinterpret_cast<float *>(smem + (size_t)WAVES * L::kTile);
+    const int nb = (a.C + KBC - 1) / KBC;
+    const int per = (nb + KSPLIT - 1) / KSPLIT;
+    const int kb_beg = min(ks * per, nb), kb_end = min(kb_beg + per, nb);
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t *ph[BT];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt)
+        ph[bt] = reinterpret_cast<const f32x4_t *>(a.h + (size_t)min(bt * 16 + lr, a.B - 1) * a.K);
+    const int wg_items = (a.groups + TPW - 1) / TPW;
+
+    for (int g = blockIdx.x; g < wg_items; g += gridDim.x) {
+        const int tile = g * TPW + slot;
+        const bool active = tile < a.groups;
+        const int row0 = tile * 16;
+        f32x4_t acc[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) acc[bt] = f32x4_t{0, 0, 0, 0};
+
+        f32x4_t hf[HS][BT][2];
+        auto load_h = [&](int kb, int j, f32x4_t (&hb)[BT][2]) {
+            const int c = min(kb * KBC + 4 * j + lq, a.C - 1);
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                hb[bt][0] = ph[bt][2 * c];
+                hb[bt][1] = ph[bt][2 * c + 1];
+            }
+        };
+        auto load_block = [&](int kb) {
+            if constexpr (kPre) {
+#pragma unroll
+                for (int j = 0; j < L::kSteps; ++j) load_h(kb, j, hf[j]);
+            } else {
+                load_h(kb, 0, hf[0]);
+            }
+        };
+        auto compute = [&](int kb) {
+            const bool tail = (kb + 1) * KBC > a.C;
+#pragma unroll
+            for (int j = 0; j < L::kSteps; ++j) {
+                const int slotj = kPre ? j : (j & 1);
+                if constexpr (!kPre) {
+                    if (j + 1 < L::kSteps) load_h(kb, j + 1, hf[(j + 1) & 1]);
+                }
+                const bool cok = !tail || kb * KBC + 4 * j + lq < a.C;
+                const bf16x8_t aw = L::frag(ltw, j, lr, lq);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    bf16x8_t hi, lo;
+                    split_hi_lo(cok ? hf[slotj][bt][0] : fzero, cok ? hf[slotj][bt][1] : fzero, hi, lo);
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, hi, acc[bt], 0, 0, 0);
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, lo, acc[bt], 0, 0, 0);
+                }
+            }
+        };
+        if (active && kb_beg < kb_end) {
+            u32x4_t v0[L::kInsts], v1[L::kInsts];
+            auto step = [&](u32x4_t (&v)[L::kInsts], int kb) {
+                L::store(ltw, v, kb, a.C, lane);
+                if constexpr (!kPre) load_block(kb);
+                compute(kb);
+            };
+            // software pipeline, one weight block ahead, no conditional loads
+            // in the steady loop
+            if constexpr (kPre) load_block(kb_beg);
+            L::load(v0, a.wd, a.K, a.C, row0, a.M, kb_beg, lane);
+            int kb = kb_beg;
+            for (; kb + 2 < kb_end; kb += 2) {
+                L::load(v1, a.wd, a.K, a.C, row0, a.M, kb + 1, lane);
+                step(v0, kb);
+                if constexpr (kPre) load_block(kb + 1);
+                L::load(v0, a.wd, a.K, a.C, row0, a.M, kb + 2, lane);
+                step(v1, kb + 1);
+                if constexpr (kPre) load_block(kb + 2);
+            }
+            if (kb + 1 < kb_end) {
+                L::load(v1, a.wd, a.K, a.C, row0, a.M, kb + 1, lane);
+                step(v0, kb);
+                if constexpr (kPre) load_block(kb + 1);
+                step(v1, kb + 1);
+            } else {
+                step(v0, kb);
+            }
+        }
+        if (KSPLIT > 1) {
+            if (ks > 0) {
+                float *dst = red + (size_t)wave * NV * kWave;
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(bt * 4 + e) * kWave + lane] = acc[bt][e];
+            }
+            __syncthreads();
+            if (ks == 0) {
+#pragma unroll
+                for (int w = 1; w < KSPLIT; ++w) {
+                    const float *src = red + (size_t)(wave + w) * NV * kWave;
+#pragma unroll
+                    for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[bt][e] += src[(bt * 4 + e) * kWave + lane];
+                }
+            }
+            __syncthreads();
+        }
+        if (ks == 0 && active) {
+            const int m = row0 + 4 * lq;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (b < a.B && m < a.M) {
+                    const unsigned lo = to_bf16_rne(acc[bt][0]) | ((unsigned)to_bf16_rne(acc[bt][1]) << 16);
+                    const unsigned hi = to_bf16_rne(acc[bt][2]) | ((unsigned)to_bf16_rne(acc[bt][3]) << 16);
+                    *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------- MFMA row ------
 // A wave owns a tile group of 16*TR rows for the whole of K; no LDS.
 
@@ -752,15 +1084,18 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_col_kernel(DownArgs a
 
 // ------------------------------------------------------ MFMA K panels -----
 //
-// The down projection's column traversal for small batches: the K columns of
-// W_down are cut into S panels across workgroups.  Workgroup (s, part) stages
-// panel s of h in LDS once -- as bf16 hi/lo MFMA fragments, entry [chunk][b]
-// -- and its waves stream 16*TR-row tiles over that panel, so each h byte
-// crosses L2 once per panel instead of once per row tile.  Panel sums go to
-// partial[s][b][m]; the reduce kernel, next on the same stream, adds the S
-// panels in panel order and rounds to bf16.  Stream order is the only
-// synchronisation (no atomics, no cross-workgroup fences).
+// Down-projection column traversal on the matrix cores for batches 9..16: the
+// K columns of W_down are cut into S panels across workgroups.  Workgroup (s, part)
+// stages panel s of its operand in LDS once, already in MFMA fragment order
+// (entry [chunk][b] is the 16 bytes lane (b mod 16, chunk mod 4) needs), and
+// its waves stream 16-row tiles over that panel, so each operand byte crosses
+// L2 once per panel instead of once per row tile, and there are S times more
+// work items than row tiles.  Panel sums go to a partial buffer; a reduce
+// kernel, next on the same stream, adds the S panels in panel order and runs
+// the epilogue.  Stream order is the only synchronisation (no atomics, no
+// cross-workgroup fences).
 
+// down: partial[s][b][m] = panel-s sum; h staged as bf16 hi + lo fragments.
 template <int BT, int TR, int U>
 __global__ __launch_bounds__(kValuBlock) void down_mfma_panel_kernel(DownArgs a, float *partial, int S, int CS) {
     extern __shared__ u32x4_t hf[];  // hi plane [CS][B], then lo plane [CS][B]
@@ -900,13 +1235,55 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_DN_MFMA_WAVES
 #define DFK_DN_MFMA_WAVES(BT) ((BT) <= 4 ? 8 : 4)
 #endif
+// all of h stays in LDS for the VALU down kernels up to this many bytes
+#ifndef DFK_HLDS_LIMIT
+#define DFK_HLDS_LIMIT kHLdsLimit
+#endif
+// 0: persistent grid (at most the blocks that fit the machine at once);
+// 1: one block per group of work items (the hardware dispatcher balances)
+#ifndef DFK_GRID_MODE
+#define DFK_GRID_MODE 0
+#endif
 // the down projection's col traversal uses K panels across workgroups up to
 // this batch (h panels in LDS), and the in-workgroup K split above it
+// MFMA row/col kernels: the LDS-transposed weight stream (1) or the direct
+// 16-row fragment loads (0); the transposed kernels cover B <= 128
+#ifndef DFK_MFMA_LT
+#define DFK_MFMA_LT 1
+#endif
+// waves per workgroup and K split of the transposed kernels (LDS: 8.25 KB
+// per wave and weight matrix, plus the K-split combine)
+#ifndef DFK_LT_GU_WAVES
+#define DFK_LT_GU_WAVES(BT) 4
+#endif
+#ifndef DFK_LT_GU_KSPLIT
+#define DFK_LT_GU_KSPLIT(BT) 4
+#endif
+#ifndef DFK_LT_DN_WAVES
+#define DFK_LT_DN_WAVES(BT) 4
+#endif
+#ifndef DFK_LT_DN_KBC
+#define DFK_LT_DN_KBC 32
+#endif
+#ifndef DFK_LT_DN_KSPLIT
+#define DFK_LT_DN_KSPLIT(BT) 4
+#endif
+#ifndef DFK_DN_PANEL_MIN_B
+#define DFK_DN_PANEL_MIN_B 9
+#endif
 #ifndef DFK_DN_PANEL_MAX_B
 #define DFK_DN_PANEL_MAX_B 16
 #endif
 #ifndef DFK_DN_PANEL_U
 #define DFK_DN_PANEL_U 4
+#endif
+// K panels are chosen so that panels x row tiles >= CUs x this many waves
+#ifndef DFK_PANEL_WAVES_PER_CU
+#define DFK_PANEL_WAVES_PER_CU 16
+#endif
+// ... but no panel shorter than this many 16-byte chunks
+#ifndef DFK_PANEL_MIN_CHUNKS
+#define DFK_PANEL_MIN_CHUNKS 32
 #endif
 
 struct KernelInfo {
@@ -955,7 +1332,48 @@ template <int BT> KernelInfo dn_mfma_col() {
     return {(const void *)down_mfma_col_kernel<BT, TR, U, W>, 16 * TR, W * kWave, W, TR * BT * 4};
 }
 
+static long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
 static const void *kPanelFn = (const void *)down_mfma_panel_kernel<1, 1, DFK_DN_PANEL_U>;
+
+// K panels for a panel kernel: each panel's operand (bytes_per_chunk per
+// 16-byte weight chunk) must fit the LDS budget, panels x row tiles should
+// give every CU DFK_PANEL_WAVES_PER_CU waves, panels stay >= the minimum
+// length (unless the LDS forces them shorter).
+static void plan_panels(int C, size_t bytes_per_chunk, int groups, int cus, Plan *q) {
+    const long max_cs = std::max<long>(4, (long)(kPanelLds / bytes_per_chunk) / 4 * 4);
+    const long s_lds = ceil_div(C, max_cs);
+    const long s_par = ceil_div((long)cus * DFK_PANEL_WAVES_PER_CU, groups);
+    const long s_len = std::max(1L, (long)C / DFK_PANEL_MIN_CHUNKS);
+    long S = std::max(s_lds, std::min(s_par, s_len));
+    S = std::min<long>(S, ceil_div(C, 4));
+    const long cs = ceil_div(ceil_div(C, S), 4) * 4;
+    S = ceil_div(C, cs);
+    q->splits = (int)S;
+    q->chunks_per_split = (int)cs;
+    q->block = kValuBlock;
+    q->rows_per_group = 16;
+    q->groups = groups;
+    q->lds_bytes = bytes_per_chunk * cs;
+    q->grid = (int)(S * ceil_div(groups, kValuBlock / kWave));
+}
+
+template <int BT> KernelInfo gu_lt_row() {
+    constexpr int W = DFK_LT_GU_WAVES(BT);
+    return {(const void *)gate_up_mfma_lt_kernel<BT, 1, W>, 16, W * kWave, 1, 2 * BT * 4};
+}
+template <int BT> KernelInfo gu_lt_col() {
+    constexpr int W = DFK_LT_GU_WAVES(BT), KS = DFK_LT_GU_KSPLIT(BT);
+    return {(const void *)gate_up_mfma_lt_kernel<BT, KS, W>, 16, W * kWave, KS, 2 * BT * 4};
+}
+template <int BT> KernelInfo dn_lt_row() {
+    constexpr int W = DFK_LT_DN_WAVES(BT);
+    return {(const void *)down_mfma_lt_kernel<BT, 1, W, DFK_LT_DN_KBC>, 16, W * kWave, 1, BT * 4};
+}
+template <int BT> KernelInfo dn_lt_col() {
+    constexpr int W = DFK_LT_DN_WAVES(BT), KS = DFK_LT_DN_KSPLIT(BT);
+    return {(const void *)down_mfma_lt_kernel<BT, KS, W, DFK_LT_DN_KBC>, 16, W * kWave, KS, BT * 4};
+}
 
 #define DFK_B_TABLE(F) {F<1>(), F<2>(), F<3>(), F<4>(), F<5>(), F<6>(), F<7>(), F<8>()}
 #define DFK_BT_TABLE(F)                                                                                 \
@@ -974,6 +1392,11 @@ static const KernelInfo kGuMfmaRow[kMaxBT] = DFK_BT_TABLE(gu_mfma_row);
 static const KernelInfo kDnMfmaRow[kMaxBT] = DFK_BT_TABLE(dn_mfma_row);
 static const KernelInfo kGuMfmaCol[kMaxBT] = DFK_BT_TABLE(gu_mfma_col);
 static const KernelInfo kDnMfmaCol[kMaxBT] = DFK_BT_TABLE(dn_mfma_col);
+constexpr int kLtMaxBT = 8;
+static const KernelInfo kGuLtRow[kLtMaxBT] = DFK_B_TABLE(gu_lt_row);
+static const KernelInfo kGuLtCol[kLtMaxBT] = DFK_B_TABLE(gu_lt_col);
+static const KernelInfo kDnLtRow[kLtMaxBT] = DFK_B_TABLE(dn_lt_row);
+static const KernelInfo kDnLtCol[kLtMaxBT] = DFK_B_TABLE(dn_lt_col);
 
 // Blocks of a kernel that fit on one CU (cached per kernel, block and LDS).
 static int blocks_per_cu(const void *fn, int block, size_t lds) {
@@ -993,7 +1416,6 @@ static int blocks_per_cu(const void *fn, int block, size_t lds) {
     return n;
 }
 
-static long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out) {
     if (B < 1 || d_model < 8 || d_ff < 8 || (d_model % 8) || (d_ff % 8) || cus < 1) return false;
@@ -1020,7 +1442,7 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
         } else {
             // keep all of h in LDS when it is small, else read it through the caches
             const size_t whole = (size_t)B * q.K * 4;
-            const bool hlds = whole <= kHLdsLimit;
+            const bool hlds = whole <= DFK_HLDS_LIMIT;
             if (row) ki = hlds ? kDnValuRowLds[B - 1] : kDnValuRow[B - 1];
             else ki = hlds ? kDnValuColLds[B - 1] : kDnValuCol[B - 1];
             q.lds_bytes = (hlds ? whole : 0) + (size_t)(ki.block / kWave) * ki.nv * sizeof(float);
@@ -1030,28 +1452,35 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
     } else {
         const int BT = (int)ceil_div(B, 16);
         if (BT > kMaxBT) return false;
-        if (!gu && !row && B <= DFK_DN_PANEL_MAX_B && B <= 16) {
-            // K panels across workgroups: the panel of h (bf16 hi + lo, 32 B per
-            // chunk and batch row) must fit the LDS budget; enough panels to give
-            // every CU a workgroup
-            const int C = q.K / 8;
-            const long max_cs = std::max<long>(4, (long)(kPanelLds / ((size_t)B * 32)) / 4 * 4);
-            const int groups = (int)ceil_div(q.rows, 16);
-            const long wg_per_panel = ceil_div(groups, kValuBlock / kWave);
-            long S = std::max(ceil_div(C, max_cs), ceil_div(cus, wg_per_panel));
-            S = std::min<long>(S, ceil_div(C, 4));
-            long cs = ceil_div(ceil_div(C, S), 4) * 4;
-            S = ceil_div(C, cs);
+        const int C = q.K / 8;
+        if (!gu && !row && B >= DFK_DN_PANEL_MIN_B && B <= DFK_DN_PANEL_MAX_B && B <= 16) {
+            // down column traversal as K panels across workgroups (+ a reduce
+            // kernel); the h panel sits in LDS as bf16 hi + lo (32 B per chunk
+            // and batch row)
+            plan_panels(C, (size_t)B * 32, (int)ceil_div(q.rows, 16), cus, &q);
             q.kind = KIND_DN_MFMA_PANEL;
-            q.splits = (int)S;
-            q.chunks_per_split = (int)cs;
-            q.block = kValuBlock;
-            q.rows_per_group = 16;
-            q.groups = groups;
-            q.lds_bytes = 2 * (size_t)cs * B * 16;
-            q.grid = (int)(S * wg_per_panel);
-            q.partial_floats = (size_t)S * B * q.rows;
+            q.partial_floats = (size_t)q.splits * B * q.rows;
             q.fn = kPanelFn;
+            *out = q;
+            return true;
+        }
+        if (DFK_MFMA_LT && BT <= kLtMaxBT) {
+            // LDS-transposed weight stream; waves_per_item = the K split
+            if (row) ki = gu ? kGuLtRow[BT - 1] : kDnLtRow[BT - 1];
+            else ki = gu ? kGuLtCol[BT - 1] : kDnLtCol[BT - 1];
+            const int waves = ki.block / kWave;
+            q.lds_bytes = (size_t)waves * (gu ? 2 * Lt<32>::kTile : Lt<DFK_LT_DN_KBC>::kTile) * 16 +
+                          (ki.waves_per_item > 1 ? (size_t)waves * ki.nv * kWave * sizeof(float) : 0);
+            if (q.lds_bytes > kLdsLimit) return false;
+            q.kind = gu ? KIND_GU_MFMA_LT : KIND_DN_MFMA_LT;
+            q.block = ki.block;
+            q.rows_per_group = 16;
+            q.groups = (int)ceil_div(q.rows, 16);
+            const int occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
+            const long tiles_per_wg = waves / ki.waves_per_item;
+            const long wg_items = ceil_div(q.groups, tiles_per_wg);
+            q.grid = (int)std::max(1L, DFK_GRID_MODE ? wg_items : std::min((long)cus * occ, wg_items));
+            q.fn = ki.fn;
             *out = q;
             return true;
         }
@@ -1065,17 +1494,19 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
     q.groups = (int)ceil_div(q.rows, ki.rows_per_group);
     const int occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
     const long items_per_block = (ki.block / kWave) / ki.waves_per_item;
-    q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div(q.groups, items_per_block)));
+    const long all_items = ceil_div(q.groups, items_per_block);
+    q.grid = (int)std::max(1L, DFK_GRID_MODE ? all_items : std::min((long)cus * occ, all_items));
     q.fn = ki.fn;
     *out = q;
     return true;
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
-                          float *h, hipStream_t stream) {
+                          float *h, float *partial, hipStream_t stream) {
     GateUpArgs a;
     a.x = x; a.wg = w_gate; a.wu = w_up; a.h = h;
     a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.groups = p.groups;
+    (void)partial;
     void *argv[] = {&a};
     return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
 }

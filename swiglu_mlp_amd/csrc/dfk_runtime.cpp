@@ -72,9 +72,8 @@ int device_cus(int dev) {
 
 // ------------------------------------------------------------ workspace ---
 //
-// dfk_swiglu_mlp keeps h (fp32 [B, d_ff]) and the down projection's K-panel
-// partial sums (when its plan uses panels) in a library-owned buffer per
-// (device, stream).  Kernels on one stream run in order, so one buffer per
+// dfk_swiglu_mlp keeps h (fp32 [B, d_ff]) in a library-owned buffer per
+// (device, stream), and the K-panel kernels keep their partial sums there.  Kernels on one stream run in order, so one buffer per
 // stream is enough; calls on one stream from several host threads serialise
 // on the slot's mutex while they enqueue.  Growing frees the old buffer
 // (hipFree waits for the device).
@@ -357,7 +356,7 @@ void ensure_table_loaded() {
 }
 
 // The built-in choice when the table has nothing for a shape: VALU row
-// traversal while the batch is small, MFMA with K panels above.
+// traversal while the batch is small, the MFMA column traversal above.
 Variant heuristic(Op op, int B) {
     if (B <= dfk::kValuMaxBatch) return {dfk::ENGINE_VALU, dfk::TRAV_ROW};
     (void)op;
@@ -531,7 +530,17 @@ dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate, con
         Plan p;
         if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
         log_plan("gate_up", p);
-        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
+        float *partial = nullptr;
+        Slot *slot = nullptr;
+        std::unique_lock<std::mutex> lock;
+        if (p.partial_floats) {
+            slot = slot_for(dev, stream);
+            lock = std::unique_lock<std::mutex>(slot->mu);
+            void *ws = nullptr;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            partial = static_cast<float *>(ws);
+        }
+        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {
         return DFK_ERR_HIP;
@@ -588,10 +597,12 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
         std::lock_guard<std::mutex> lock(slot->mu);
         void *ws = nullptr;
         const size_t h_bytes = ((size_t)B * d_ff * sizeof(float) + 255) & ~size_t(255);
-        if ((st = ensure_workspace(slot, h_bytes + pd.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+        // the two kernels run in stream order, so their panel partials share one region
+        const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
+        if ((st = ensure_workspace(slot, h_bytes + partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
         float *h = static_cast<float *>(ws);
-        float *partial = pd.partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
-        if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
+        float *partial = partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
+        if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {
