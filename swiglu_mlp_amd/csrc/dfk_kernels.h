@@ -35,7 +35,9 @@ enum Kind {
     KIND_DN_MFMA_COL = 7,
     KIND_DN_MFMA_PANEL = 8,  // down col traversal, K panels across workgroups + a reduce kernel
     KIND_GU_MFMA_LT = 10,    // gate-up, weights streamed through a wave-private LDS transpose
-    KIND_DN_MFMA_LT = 11
+    KIND_DN_MFMA_LT = 11,
+    KIND_GU_MFMA_STAGED = 12,  // gate-up, B operand staged in LDS per workgroup (B > 16)
+    KIND_DN_MFMA_STAGED = 13   // down, the same, K split across workgroups + a reduce kernel
 };
 
 // A fully resolved launch: which kernel and how the weight matrix is cut.

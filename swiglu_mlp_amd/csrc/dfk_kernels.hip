@@ -1082,6 +1082,269 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_col_kernel(DownArgs a
     }
 }
 
+// ------------------------------------------ MFMA, B operand staged in LDS --
+//
+// Above 16 batch rows the B operand (x, or h) is the larger stream out of L2:
+// every 16-row weight tile needs all of it.  In these kernels the WAVES tiles
+// of a workgroup walk K together in blocks of 256 elements.  Each block of the
+// B operand is loaded once per workgroup with wide, coalesced loads, zeroed
+// past B and outside the K range, and parked in LDS with a padded pitch; the
+// waves read their MFMA B fragments from there.  Weights arrive as A fragments
+// straight from HBM, one block ahead in registers, and every load of the
+// steady loop is unconditional.  The last block of a K range is shifted back
+// to end at the range end (the chunks it repeats are zeroed in the staged
+// block), so weight loads stay inside their row.  The down kernel may also
+// split K across S workgroups: partial sums, then the panel reduce kernel.
+// NBUF = 2 double-buffers the staged block (one barrier per block), NBUF = 1
+// halves the LDS (two barriers).
+
+constexpr int kStKbc = 32;            // 16-byte chunks per K block (256 elements)
+constexpr int kStPitch = kStKbc + 1;  // LDS pitch of one staged row, in chunks
+
+// First chunk of block kb of the K range [c0, c1)
+__device__ __forceinline__ int st_block_start(int kb, int c0, int c1) {
+    return c1 - c0 >= kStKbc ? min(c0 + kb * kStKbc, c1 - kStKbc) : c0;
+}
+
+template <int BT, int WAVES, int NBUF, int WPE>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void gate_up_mfma_staged_kernel(
+    GateUpArgs a) {
+    constexpr int NT = WAVES * kWave;
+    constexpr int XR = 16 * BT;                   // staged rows: the padded batch
+    constexpr int XPT = XR * kStKbc / NT;         // staged chunks per thread
+    static_assert(XR * kStKbc % NT == 0, "staging split");
+    constexpr int XBUF = XR * kStPitch;
+    extern __shared__ u32x4_t smem[];             // [NBUF][XR][kStPitch]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int nb = (a.C + kStKbc - 1) / kStKbc;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const u32x4_t *xg = reinterpret_cast<const u32x4_t *>(a.x);
+    const int wg_items = (a.groups + WAVES - 1) / WAVES;
+
+    auto load_x = [&](u32x4_t (&xr)[XPT], int kb) {
+        const int cs = st_block_start(kb, 0, a.C);
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+            const int i = t * NT + tid;
+            const int b = min(i / kStKbc, a.B - 1);
+            const int c = min(cs + i % kStKbc, a.C - 1);
+            xr[t] = xg[(size_t)b * a.C + c];
+        }
+    };
+    auto store_x = [&](const u32x4_t (&xr)[XPT], int kb) {
+        const int cs = st_block_start(kb, 0, a.C);
+        u32x4_t *dst = smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+            const int i = t * NT + tid;
+            const int b = i / kStKbc, cc = i % kStKbc;
+            const int c = cs + cc;
+            const bool ok = b < a.B && c >= kb * kStKbc && c < a.C;
+            dst[b * kStPitch + cc] = ok ? xr[t] : zero;
+        }
+    };
+
+    for (int g = blockIdx.x; g < wg_items; g += gridDim.x) {
+        const int tile = g * WAVES + wave;
+        const int row = min(tile * 16 + lr, a.N - 1);
+        const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)row * a.K);
+        const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)row * a.K);
+        f32x4_t accg[BT], accu[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) accg[bt] = accu[bt] = f32x4_t{0, 0, 0, 0};
+
+        auto load_w = [&](u32x4_t (&wgr)[8], u32x4_t (&wur)[8], int kb) {
+            const int cs = st_block_start(kb, 0, a.C);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = min(cs + 4 * j + lq, a.C - 1);
+                wgr[j] = load_stream(pg + c);
+                wur[j] = load_stream(pu + c);
+            }
+        };
+        auto compute = [&](const u32x4_t (&wgr)[8], const u32x4_t (&wur)[8], int kb) {
+            const u32x4_t *xs = smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const bf16x8_t xb = as_bf16x8(xs[(bt * 16 + lr) * kStPitch + 4 * j + lq]);
+                    accg[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wgr[j]), xb, accg[bt], 0, 0, 0);
+                    accu[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wur[j]), xb, accu[bt], 0, 0, 0);
+                }
+        };
+        u32x4_t xr[XPT];
+        u32x4_t wg0[8], wu0[8], wg1[8], wu1[8];
+        // prefetch block kb + 1 (x first, then the weights), multiply block kb,
+        // then park x(kb + 1) in LDS
+        auto step = [&](auto &cg, auto &cu, auto &ng, auto &nu, int kb) {
+            load_x(xr, kb + 1);
+            load_w(ng, nu, kb + 1);
+            compute(cg, cu, kb);
+            if constexpr (NBUF == 1) __syncthreads();
+            store_x(xr, kb + 1);
+            __syncthreads();
+        };
+        auto last = [&](auto &cg, auto &cu, int kb) {
+            compute(cg, cu, kb);
+            __syncthreads();
+        };
+        load_x(xr, 0);
+        load_w(wg0, wu0, 0);
+        store_x(xr, 0);
+        __syncthreads();
+        int kb = 0;
+        for (; kb + 2 < nb; kb += 2) {
+            step(wg0, wu0, wg1, wu1, kb);
+            step(wg1, wu1, wg0, wu0, kb + 1);
+        }
+        if (kb + 1 < nb) {
+            step(wg0, wu0, wg1, wu1, kb);
+            last(wg1, wu1, kb + 1);
+        } else {
+            last(wg0, wu0, kb);
+        }
+        if (tile < a.groups) {
+            const int n = tile * 16 + 4 * lq;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (b < a.B && n < a.N) {
+                    f32x4_t o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
+                }
+            }
+        }
+    }
+}
+
+// down: h staged as bf16 hi + lo planes; work item = (row-tile group, K split)
+template <int BT, int WAVES, int NBUF, int WPE>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_staged_kernel(
+    DownArgs a, float *partial, int S, int CS) {
+    constexpr int NT = WAVES * kWave;
+    constexpr int XR = 16 * BT;
+    constexpr int XPT = XR * kStKbc / NT;
+    static_assert(XR * kStKbc % NT == 0, "staging split");
+    constexpr int PLANE = XR * kStPitch;
+    extern __shared__ u32x4_t smem[];  // [NBUF][hi, lo][XR][kStPitch]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    const int row_groups = (a.groups + WAVES - 1) / WAVES;
+    const int items = row_groups * S;
+
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int sp = it % S, g = it / S;
+        const int c0 = sp * CS, c1 = min(c0 + CS, a.C);
+        const int nb = (c1 - c0 + kStKbc - 1) / kStKbc;
+        const int tile = g * WAVES + wave;
+        const int row = min(tile * 16 + lr, a.M - 1);
+        const u32x4_t *pw = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)row * a.K);
+        f32x4_t acc[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) acc[bt] = f32x4_t{0, 0, 0, 0};
+
+        auto load_h = [&](f32x4_t (&hr)[XPT][2], int kb) {
+            const int cs = st_block_start(kb, c0, c1);
+#pragma unroll
+            for (int t = 0; t < XPT; ++t) {
+                const int i = t * NT + tid;
+                const int b = min(i / kStKbc, a.B - 1);
+                const int c = min(cs + i % kStKbc, a.C - 1);
+                hr[t][0] = hg[(size_t)b * 2 * a.C + 2 * c];
+                hr[t][1] = hg[(size_t)b * 2 * a.C + 2 * c + 1];
+            }
+        };
+        auto store_h = [&](const f32x4_t (&hr)[XPT][2], int kb) {
+            const int cs = st_block_start(kb, c0, c1);
+            u32x4_t *dhi = smem + (NBUF == 2 ? (kb & 1) : 0) * 2 * PLANE;
+            u32x4_t *dlo = dhi + PLANE;
+#pragma unroll
+            for (int t = 0; t < XPT; ++t) {
+                const int i = t * NT + tid;
+                const int b = i / kStKbc, cc = i % kStKbc;
+                const int c = cs + cc;
+                const bool ok = b < a.B && c >= c0 + kb * kStKbc && c < c1;
+                bf16x8_t hi, lo;
+                split_hi_lo(ok ? hr[t][0] : fzero, ok ? hr[t][1] : fzero, hi, lo);
+                dhi[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, hi);
+                dlo[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, lo);
+            }
+        };
+        auto load_w = [&](u32x4_t (&wr)[8], int kb) {
+            const int cs = st_block_start(kb, c0, c1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wr[j] = load_stream(pw + min(cs + 4 * j + lq, a.C - 1));
+        };
+        auto compute = [&](const u32x4_t (&wr)[8], int kb) {
+            const u32x4_t *shi = smem + (NBUF == 2 ? (kb & 1) : 0) * 2 * PLANE;
+            const u32x4_t *slo = shi + PLANE;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const int o = (bt * 16 + lr) * kStPitch + 4 * j + lq;
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[j]), as_bf16x8(shi[o]), acc[bt], 0, 0, 0);
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[j]), as_bf16x8(slo[o]), acc[bt], 0, 0, 0);
+                }
+        };
+        f32x4_t hr[XPT][2];
+        u32x4_t w0[8], w1[8];
+        auto step = [&](auto &cw, auto &nw, int kb) {
+            load_h(hr, kb + 1);
+            load_w(nw, kb + 1);
+            compute(cw, kb);
+            if constexpr (NBUF == 1) __syncthreads();
+            store_h(hr, kb + 1);
+            __syncthreads();
+        };
+        auto last = [&](auto &cw, int kb) {
+            compute(cw, kb);
+            __syncthreads();
+        };
+        load_h(hr, 0);
+        load_w(w0, 0);
+        store_h(hr, 0);
+        __syncthreads();
+        int kb = 0;
+        for (; kb + 2 < nb; kb += 2) {
+            step(w0, w1, kb);
+            step(w1, w0, kb + 1);
+        }
+        if (kb + 1 < nb) {
+            step(w0, w1, kb);
+            last(w1, kb + 1);
+        } else {
+            last(w0, kb);
+        }
+        if (tile < a.groups) {
+            const int m = tile * 16 + 4 * lq;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (b < a.B && m < a.M) {
+                    if (S == 1) {
+                        const unsigned lo = to_bf16_rne(acc[bt][0]) | ((unsigned)to_bf16_rne(acc[bt][1]) << 16);
+                        const unsigned hi = to_bf16_rne(acc[bt][2]) | ((unsigned)to_bf16_rne(acc[bt][3]) << 16);
+                        *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
+                    } else {
+                        *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = acc[bt];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------ MFMA K panels -----
 //
 // Down-projection column traversal on the matrix cores for batches 9..16: the
@@ -1277,6 +1540,30 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_DN_PANEL_U
 #define DFK_DN_PANEL_U 4
 #endif
+// B-operand-staged MFMA kernels: used from this many batch tiles up to
+// kStMaxBT (gate-up ROW traversal, down COL traversal); waves per workgroup
+// and LDS buffers per staged block
+#ifndef DFK_ST_GU_MIN_BT
+#define DFK_ST_GU_MIN_BT 3
+#endif
+#ifndef DFK_ST_DN_MIN_BT
+#define DFK_ST_DN_MIN_BT 2
+#endif
+#ifndef DFK_ST_GU_NBUF
+#define DFK_ST_GU_NBUF(BT) ((BT) <= 4 ? 2 : 1)
+#endif
+#ifndef DFK_ST_DN_NBUF
+#define DFK_ST_DN_NBUF(BT) ((BT) <= 2 ? 2 : 1)
+#endif
+// Workgroups of 8 waves share each staged block among more tiles; they are
+// used when they still give (almost) every CU a workgroup, i.e. when
+// ceil(tiles / 8) >= 7/8 of the CUs (gate-up), and for down when BT >= 3 or
+// the row tiles number at least two per CU (its K split fills the machine).
+// the staged down kernel splits K so that (row groups x splits) fills every
+// CU's resident workgroups, with no split shorter than this many chunks
+#ifndef DFK_ST_DN_MIN_CHUNKS
+#define DFK_ST_DN_MIN_CHUNKS 128
+#endif
 // K panels are chosen so that panels x row tiles >= CUs x this many waves
 #ifndef DFK_PANEL_WAVES_PER_CU
 #define DFK_PANEL_WAVES_PER_CU 16
@@ -1375,6 +1662,19 @@ template <int BT> KernelInfo dn_lt_col() {
     return {(const void *)down_mfma_lt_kernel<BT, KS, W, DFK_LT_DN_KBC>, 16, W * kWave, KS, BT * 4};
 }
 
+template <int W, int BT> KernelInfo gu_staged_w() {
+    constexpr int NB = DFK_ST_GU_NBUF(BT);
+    return {(const void *)gate_up_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1)>, 16, W * kWave, NB, 0};
+}
+template <int W, int BT> KernelInfo dn_staged_w() {
+    constexpr int NB = DFK_ST_DN_NBUF(BT);
+    return {(const void *)down_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1)>, 16, W * kWave, NB, 0};
+}
+template <int BT> KernelInfo gu_staged4() { return gu_staged_w<4, BT>(); }
+template <int BT> KernelInfo gu_staged8() { return gu_staged_w<8, BT>(); }
+template <int BT> KernelInfo dn_staged4() { return dn_staged_w<4, BT>(); }
+template <int BT> KernelInfo dn_staged8() { return dn_staged_w<8, BT>(); }
+
 #define DFK_B_TABLE(F) {F<1>(), F<2>(), F<3>(), F<4>(), F<5>(), F<6>(), F<7>(), F<8>()}
 #define DFK_BT_TABLE(F)                                                                                 \
     {F<1>(), F<2>(), F<3>(), F<4>(), F<5>(), F<6>(), F<7>(), F<8>(), F<9>(), F<10>(), F<11>(), F<12>(), \
@@ -1397,6 +1697,12 @@ static const KernelInfo kGuLtRow[kLtMaxBT] = DFK_B_TABLE(gu_lt_row);
 static const KernelInfo kGuLtCol[kLtMaxBT] = DFK_B_TABLE(gu_lt_col);
 static const KernelInfo kDnLtRow[kLtMaxBT] = DFK_B_TABLE(dn_lt_row);
 static const KernelInfo kDnLtCol[kLtMaxBT] = DFK_B_TABLE(dn_lt_col);
+constexpr int kStMaxBT = 8;
+// (waves_per_item holds the staged kernels' LDS buffer count)
+static const KernelInfo kGuStaged4[kStMaxBT] = DFK_B_TABLE(gu_staged4);
+static const KernelInfo kGuStaged8[kStMaxBT] = DFK_B_TABLE(gu_staged8);
+static const KernelInfo kDnStaged4[kStMaxBT] = DFK_B_TABLE(dn_staged4);
+static const KernelInfo kDnStaged8[kStMaxBT] = DFK_B_TABLE(dn_staged8);
 
 // Blocks of a kernel that fit on one CU (cached per kernel, block and LDS).
 static int blocks_per_cu(const void *fn, int block, size_t lds) {
@@ -1464,6 +1770,37 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
+        if (BT >= (gu ? DFK_ST_GU_MIN_BT : DFK_ST_DN_MIN_BT) && BT <= kStMaxBT && (gu ? row : !row)) {
+            // B operand staged in LDS per workgroup: gate-up ROW, down COL
+            const long tiles = ceil_div(q.rows, 16);
+            const bool wide = gu ? ceil_div(tiles, 8L) * 8 >= 7L * cus : (BT >= 3 || tiles >= 2L * cus);
+            ki = gu ? (wide ? kGuStaged8 : kGuStaged4)[BT - 1] : (wide ? kDnStaged8 : kDnStaged4)[BT - 1];
+            const int waves = ki.block / kWave;
+            q.lds_bytes = (size_t)ki.waves_per_item * (gu ? 1 : 2) * 16 * BT * kStPitch * 16;
+            if (q.lds_bytes > kLdsLimit) return false;
+            q.kind = gu ? KIND_GU_MFMA_STAGED : KIND_DN_MFMA_STAGED;
+            q.block = ki.block;
+            q.rows_per_group = 16;
+            q.groups = (int)ceil_div(q.rows, 16);
+            const long occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
+            const long row_groups = ceil_div(q.groups, waves);
+            const long target = (long)cus * occ;
+            long S = 1;
+            if (!gu) {
+                const long max_s = std::max(1L, (long)C / DFK_ST_DN_MIN_CHUNKS);
+                S = std::min(max_s, std::max(1L, ceil_div(target, row_groups)));
+                long cs = ceil_div((long)C, S);
+                if (C >= kStKbc) cs = ceil_div(cs, (long)kStKbc) * kStKbc;
+                S = ceil_div((long)C, cs);
+                q.chunks_per_split = (int)cs;
+            }
+            q.splits = (int)S;
+            q.partial_floats = S > 1 ? (size_t)S * B * q.rows : 0;
+            q.grid = (int)std::max(1L, std::min(target, row_groups * S));
+            q.fn = ki.fn;
+            *out = q;
+            return true;
+        }
         if (DFK_MFMA_LT && BT <= kLtMaxBT) {
             // LDS-transposed weight stream; waves_per_item = the K split
             if (row) ki = gu ? kGuLtRow[BT - 1] : kDnLtRow[BT - 1];
@@ -1516,12 +1853,17 @@ hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, ui
     DownArgs a;
     a.h = h; a.wd = w_down; a.y = y;
     a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.groups = p.groups;
-    if (p.kind != KIND_DN_MFMA_PANEL) {
+    if (p.kind != KIND_DN_MFMA_PANEL && p.kind != KIND_DN_MFMA_STAGED) {
         void *argv[] = {&a};
         return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
     }
-    if (!partial) return hipErrorInvalidValue;
     int S = p.splits, CS = p.chunks_per_split;
+    if (p.kind == KIND_DN_MFMA_STAGED && S == 1) {
+        float *none = nullptr;
+        void *argv[] = {&a, &none, &S, &CS};
+        return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    }
+    if (!partial) return hipErrorInvalidValue;
     void *argv[] = {&a, &partial, &S, &CS};
     hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
     if (e != hipSuccess) return e;
