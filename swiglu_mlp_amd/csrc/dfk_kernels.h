@@ -37,7 +37,8 @@ enum Kind {
     KIND_GU_MFMA_LT = 10,    // gate-up, weights streamed through a wave-private LDS transpose
     KIND_DN_MFMA_LT = 11,
     KIND_GU_MFMA_STAGED = 12,  // gate-up, B operand staged in LDS per workgroup (B > 16)
-    KIND_DN_MFMA_STAGED = 13   // down, the same, K split across workgroups + a reduce kernel
+    KIND_DN_MFMA_STAGED = 13,  // down, the same, K split across workgroups + a reduce kernel
+    KIND_DN_MFMA_COOP = 15     // down ROW (B <= 16), workgroup-cooperative LDS weight tile
 };
 
 // A fully resolved launch: which kernel and how the weight matrix is cut.

@@ -1345,6 +1345,164 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
     }
 }
 
+// ----------------------- MFMA, workgroup-cooperative weight tile (down) -----
+//
+// The down projection's row traversal on the matrix cores, for batches up to
+// 16.  A workgroup owns whole rows: a tile of 16 rows of W_down, walked over
+// all of K in stages of KSC 16-byte chunks per row.  In a stage every wave
+// loads whole runs of its RPW rows, one row x 1 KB per load instruction (the
+// access shape that streams at full HBM rate), and parks them in a shared,
+// double-buffered LDS tile (pitch KSC + 1).  After one barrier each wave
+// multiplies its own K slice of the stage (KSC / WAVES chunks) over the 16 rows
+// on the matrix cores, with B fragments (h split into bf16 hi + lo) from
+// registers.  Two register buffers (weights and B fragments) alternate between
+// the halves of a loop unrolled by two: a stage's B fragments and then its
+// weights are issued before the previous stage's weights are waited for, and
+// since loads complete in issue order every wait is for the oldest loads only
+// (scheduling barriers keep that issue order).  At the end of a tile the
+// waves' partial sums are added in wave order through the LDS tile just used.
+// A workgroup takes tiles in sequence and the pipeline runs across tile
+// boundaries; the last one or two stages are peeled, so no load in the loop is
+// conditional.  K spans at least one stage (the plan guarantees it) and the
+// last stage is shifted back to end at the row end, the chunks it repeats
+// zeroed in the tile and in the B fragments: no load leaves its row and none
+// needs a clamp.
+
+template <int WAVES, int KSC> struct Coop {
+    static constexpr int RPW = 16 / WAVES;     // tile rows loaded per wave
+    static constexpr int NI = RPW * KSC / 64;  // load instructions per wave and stage
+    static constexpr int PITCH = KSC + 1;      // LDS tile pitch, chunks
+    static constexpr int SL = KSC / WAVES;     // chunks of a wave's K slice
+    static constexpr int STEPS = SL / 4;       // MFMA K steps per wave and stage
+    static constexpr int TILE = 16 * PITCH;    // one LDS tile, chunks
+    static_assert(RPW * WAVES == 16 && NI * 64 == RPW * KSC && STEPS * 4 * WAVES == KSC && KSC % 64 == 0,
+                  "cooperative tile shape");
+    static_assert(WAVES * 4 * 64 * 4 <= TILE * 16, "the combine area fits a tile");
+};
+
+template <int WAVES, int KSC>
+__global__ __launch_bounds__(WAVES * kWave) void down_mfma_coop_kernel(DownArgs a) {
+    using T = Coop<WAVES, KSC>;
+    extern __shared__ u32x4_t smem[];  // tiles [2][16][PITCH]; the tile-end combine reuses one
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int ns = (a.C + KSC - 1) / KSC;  // stages per tile
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    // stage st of tile t: first chunk (the last stage ends at the row end) and
+    // the first chunk not counted by an earlier stage
+    auto start = [&](int st) { return min(st * KSC, a.C - KSC); };
+    auto load_w = [&](u32x4_t (&wv)[T::NI], int t, int st) {
+        const int cs = start(st);
+        const int row0 = t * 16 + wave * T::RPW;
+#pragma unroll
+        for (int i = 0; i < T::NI; ++i) {
+            const int row = min(row0 + i * kWave / KSC, a.M - 1);
+            const u32x4_t *pw = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)row * a.K) + cs + (i * kWave) % KSC;
+            wv[i] = load_stream(pw + lane);
+        }
+    };
+    // B fragments of this wave's K slice: h[b][8 floats] per lane and step
+    const char *hlane = reinterpret_cast<const char *>(a.h) + ((size_t)min(lr, a.B - 1) * a.K + 8 * lq) * 4;
+    auto load_h = [&](f32x4_t (&hb)[T::STEPS][2], int st) {
+        const int cs = start(st);
+#pragma unroll
+        for (int j = 0; j < T::STEPS; ++j) {
+            const f32x4_t *ph = reinterpret_cast<const f32x4_t *>(hlane + (size_t)(cs + wave * T::SL + 4 * j) * 32);
+            hb[j][0] = ph[0];
+            hb[j][1] = ph[1];
+        }
+    };
+    f32x4_t acc = fzero;
+    // park the stage's weights, then multiply this wave's slice; after the
+    // tile's last stage combine the waves and write y
+    auto half = [&](const u32x4_t (&wv)[T::NI], const f32x4_t (&hb)[T::STEPS][2], int t, int st, int buf) {
+        const int cs = start(st), lo = st * KSC;  // chunks below lo belong to earlier stages
+        u32x4_t *tile = smem + buf * T::TILE;
+#pragma unroll
+        for (int i = 0; i < T::NI; ++i) {
+            const int cc = (i * kWave) % KSC + lane;
+            tile[(wave * T::RPW + i * kWave / KSC) * T::PITCH + cc] = cs + cc >= lo ? wv[i] : zero;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < T::STEPS; ++j) {
+            const int cc = wave * T::SL + 4 * j + lq;
+            const bool ok = cs + cc >= lo;
+            bf16x8_t hi, lo8;
+            split_hi_lo(ok ? hb[j][0] : fzero, ok ? hb[j][1] : fzero, hi, lo8);
+            const bf16x8_t aw = as_bf16x8(tile[lr * T::PITCH + cc]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, hi, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, lo8, acc, 0, 0, 0);
+        }
+        if (st + 1 == ns) {
+            float *red = reinterpret_cast<float *>(tile);
+            __syncthreads();  // every wave is done with the tile
+            float *dst = red + (size_t)wave * 4 * kWave;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e * kWave + lane] = acc[e];
+            __syncthreads();
+            if (wave == 0) {
+                f32x4_t sum = fzero;
+                for (int w = 0; w < WAVES; ++w)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum[e] += red[((size_t)w * 4 + e) * kWave + lane];
+                const int m = t * 16 + 4 * lq;
+                if (lr < a.B && m < a.M) {
+                    const unsigned l2 = to_bf16_rne(sum[0]) | ((unsigned)to_bf16_rne(sum[1]) << 16);
+                    const unsigned h2 = to_bf16_rne(sum[2]) | ((unsigned)to_bf16_rne(sum[3]) << 16);
+                    *reinterpret_cast<uint2 *>(a.y + (size_t)lr * a.M + m) = make_uint2(l2, h2);
+                }
+            }
+            acc = fzero;
+        }
+    };
+    if ((int)blockIdx.x >= a.groups) return;
+    // the workgroup's stages: tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+    const int total = ((a.groups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * ns;
+    u32x4_t w0[T::NI], w1[T::NI];
+    f32x4_t h0[T::STEPS][2], h1[T::STEPS][2];
+    int t0 = blockIdx.x, s0 = 0;
+    auto next = [&](int &t, int &st) {
+        if (++st == ns) {
+            st = 0;
+            t += gridDim.x;
+        }
+    };
+    load_h(h0, s0);
+    load_w(w0, t0, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    int g = 0;
+    for (; g + 2 < total; g += 2) {
+        int t1 = t0, s1 = s0;
+        next(t1, s1);
+        load_h(h1, s1);
+        load_w(w1, t1, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        half(w0, h0, t0, s0, 0);
+        int t2 = t1, s2 = s1;
+        next(t2, s2);
+        load_h(h0, s2);
+        load_w(w0, t2, s2);
+        __builtin_amdgcn_sched_barrier(0);
+        half(w1, h1, t1, s1, 1);
+        t0 = t2;
+        s0 = s2;
+    }
+    if (g + 1 < total) {
+        int t1 = t0, s1 = s0;
+        next(t1, s1);
+        load_h(h1, s1);
+        load_w(w1, t1, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        half(w0, h0, t0, s0, 0);
+        half(w1, h1, t1, s1, 1);
+    } else {
+        half(w0, h0, t0, s0, 0);
+    }
+}
+
 // ------------------------------------------------------ MFMA K panels -----
 //
 // Down-projection column traversal on the matrix cores for batches 9..16: the
@@ -1564,6 +1722,17 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_ST_DN_MIN_CHUNKS
 #define DFK_ST_DN_MIN_CHUNKS 128
 #endif
+// Workgroup-cooperative down kernel (ROW traversal, B <= 16): waves per
+// workgroup and K chunks per stage
+#ifndef DFK_COOP
+#define DFK_COOP 1
+#endif
+#ifndef DFK_COOP_DN_WAVES
+#define DFK_COOP_DN_WAVES 8
+#endif
+#ifndef DFK_COOP_DN_KSC
+#define DFK_COOP_DN_KSC 128
+#endif
 // K panels are chosen so that panels x row tiles >= CUs x this many waves
 #ifndef DFK_PANEL_WAVES_PER_CU
 #define DFK_PANEL_WAVES_PER_CU 16
@@ -1759,6 +1928,24 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
         const int BT = (int)ceil_div(B, 16);
         if (BT > kMaxBT) return false;
         const int C = q.K / 8;
+        constexpr int dw = DFK_COOP_DN_WAVES, dk = DFK_COOP_DN_KSC;
+        const size_t coop_lds = (size_t)2 * Coop<dw, dk>::TILE * 16;
+        if (DFK_COOP && BT == 1 && !gu && row && C >= dk && coop_lds <= kLdsLimit) {
+            // down ROW: workgroup-cooperative 16-row tile over all of K (K must
+            // span at least one stage)
+            const void *fn = (const void *)down_mfma_coop_kernel<dw, dk>;
+            q.kind = KIND_DN_MFMA_COOP;
+            q.block = dw * kWave;
+            q.lds_bytes = coop_lds;
+            q.rows_per_group = 16;
+            q.groups = (int)ceil_div(q.rows, 16);
+            const long slots = (long)cus * blocks_per_cu(fn, q.block, q.lds_bytes);
+            const long per_wg = ceil_div((long)q.groups, slots);  // tiles per workgroup, balanced
+            q.grid = (int)std::max(1L, ceil_div((long)q.groups, per_wg));
+            q.fn = fn;
+            *out = q;
+            return true;
+        }
         if (!gu && !row && B >= DFK_DN_PANEL_MIN_B && B <= DFK_DN_PANEL_MAX_B && B <= 16) {
             // down column traversal as K panels across workgroups (+ a reduce
             // kernel); the h panel sits in LDS as bf16 hi + lo (32 B per chunk

@@ -12,8 +12,11 @@ of the best count as a tie and the row variant wins a tie.  The result is the
 JSON table that dfk_schedule_select reads.
 
 Timers:
-  rocprof  (default) the worker runs under `rocprofv3 --kernel-trace` and the
-           per-dispatch kernel durations come from the profiler's trace;
+  rocprof  (default) the worker runs under `rocprofv3 --kernel-trace`; a call's
+           cost is the spacing between its last kernel's end and the previous
+           call's (a block's calls run back to back, so this is the kernel
+           time plus the launch gap before it: what a stream of decode calls
+           pays per call);
   events   HIP events around groups of back-to-back launches (no profiler).
 
 This is the runtime scheduling across row-major and column-major variants of
@@ -133,11 +136,11 @@ def run_worker(blocks, warmup, use_events):
 
 
 def parse_rocprof(outdir):
-    """One record per library call, in dispatch order: list of (name, ns).
+    """One record per library call, in dispatch order: list of (name, start_ns, end_ns).
 
-    A call is one kernel, except the down projection's K-panel variant, whose
-    panel kernel is followed by a reduce kernel: that call's time runs from
-    the panel kernel's start to the reduce kernel's end (the gap included)."""
+    A call is one kernel, except the down projection's K-split variants, whose
+    kernel is followed by a reduce kernel: that call runs from the first
+    kernel's start to the reduce kernel's end."""
     files = glob.glob(os.path.join(outdir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise RuntimeError(f"no kernel_trace.csv under {outdir}")
@@ -158,7 +161,24 @@ def parse_rocprof(outdir):
             calls[-1] = (first_name, first_start, end)
         else:
             calls.append((name, start, end))
-    return [(n, e - s) for n, s, e in calls]
+    return calls
+
+
+def block_costs(calls, blocks, warmup):
+    """Median per-call cost (us) of each block from the trace's calls, in
+    dispatch order: the spacing between consecutive call ends, taken over a
+    block's timed calls (the first of them measured from the last warm-up)."""
+    if warmup < 1:
+        raise RuntimeError("the rocprof timer needs at least one warm-up call per block")
+    expect = sum(warmup + b["reps"] for b in blocks)
+    if len(calls) != expect:
+        raise RuntimeError(f"expected {expect} library calls in the trace, found {len(calls)}")
+    out, i = [], 0
+    for b in blocks:
+        ends = [e for _, _, e in calls[i + warmup - 1:i + warmup + b["reps"]]]
+        out.append(statistics.median(ends[k] - ends[k - 1] for k in range(1, len(ends))) / 1e3)
+        i += warmup + b["reps"]
+    return out
 
 
 def choose(timings_us):
@@ -212,15 +232,7 @@ def main():
                "--batches", args.batches, "--reps", str(args.reps), "--warmup", str(args.warmup)]
         print("running:", " ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, cwd=ROOT)
-        disp = parse_rocprof(outdir)
-        expect = sum(args.warmup + b["reps"] for b in blocks)
-        if len(disp) != expect:
-            raise RuntimeError(f"expected {expect} library calls in the trace, found {len(disp)}")
-        per_block, i = [], 0
-        for b in blocks:
-            durs = [d for _, d in disp[i + args.warmup:i + args.warmup + b["reps"]]]
-            per_block.append(statistics.median(durs) / 1e3)
-            i += args.warmup + b["reps"]
+        per_block = block_costs(parse_rocprof(outdir), blocks, args.warmup)
         shutil.rmtree(outdir, ignore_errors=True)
 
     entries = build_table(blocks, per_block)

@@ -78,6 +78,10 @@ SMALL_SHAPES = [
     (1, 256, 688), (1, 520, 1000), (2, 264, 72), (3, 1032, 200), (5, 136, 264),
     (8, 8, 8), (8, 520, 1000), (13, 128, 136), (16, 520, 1000), (17, 264, 456),
     (33, 1032, 200), (64, 136, 264), (256, 64, 48),
+    # K long enough for the workgroup-cooperative kernels: ragged stage counts
+    # (shifted last stages), a two-way K split with a short last split, and a
+    # ragged last row tile
+    (2, 4104, 264), (4, 264, 4104), (5, 600, 1096), (16, 1032, 2056),
 ]
 
 

@@ -1,0 +1,65 @@
+"""Host logic of the profiler-driven tuner (no GPU): trace parsing, the
+per-call cost taken from kernel-end spacing, and the winner rule."""
+import csv
+import os
+
+import pytest
+
+from swiglu_mlp_amd import tune
+
+
+def write_trace(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_parse_merges_reduce_kernels_and_skips_foreign(tmp_path):
+    d = tmp_path / "run"
+    d.mkdir()
+    write_trace(d / "x_kernel_trace.csv", [
+        {"Dispatch_Id": 3, "Kernel_Name": "void dfk::panel_reduce_kernel(float const*)", "Start_Timestamp": 250, "End_Timestamp": 260},
+        {"Dispatch_Id": 1, "Kernel_Name": "void dfk::down_valu_row_kernel<1>(dfk::DownArgs)", "Start_Timestamp": 0, "End_Timestamp": 100},
+        {"Dispatch_Id": 2, "Kernel_Name": "void dfk::down_mfma_panel_kernel<1>(dfk::DownArgs)", "Start_Timestamp": 120, "End_Timestamp": 240},
+        {"Dispatch_Id": 4, "Kernel_Name": "__amd_rocclr_fillBufferAligned", "Start_Timestamp": 300, "End_Timestamp": 310},
+    ])
+    calls = tune.parse_rocprof(str(d))
+    assert [(s, e) for _, s, e in calls] == [(0, 100), (120, 260)]
+    assert "panel_kernel" in calls[1][0]
+
+
+def test_block_costs_use_end_spacing():
+    blocks = [{"reps": 3}, {"reps": 2}]
+    # warm-up 1 per block; block 0 ends at 10, 20, 31, 43 (spacings 10, 11, 12);
+    # block 1 ends at 100, 150, 205 (spacings 50, 55)
+    ends = [10, 20, 31, 43, 100, 150, 205]
+    calls = [("k", e - 5, e) for e in ends]
+    out = tune.block_costs(calls, blocks, warmup=1)
+    assert out == pytest.approx([11e-3, 52.5e-3])
+
+
+def test_block_costs_check_counts():
+    with pytest.raises(RuntimeError):
+        tune.block_costs([("k", 0, 1)] * 3, [{"reps": 3}], warmup=1)
+    with pytest.raises(RuntimeError):
+        tune.block_costs([("k", 0, 1)] * 3, [{"reps": 3}], warmup=0)
+
+
+def test_choose_tie_goes_to_row():
+    assert tune.choose({"row_valu": 10.15, "col_valu": 10.0}) == "row_valu"     # within 2 %
+    assert tune.choose({"row_valu": 10.5, "col_valu": 10.0}) == "col_valu"      # beyond 2 %
+    assert tune.choose({"col_mfma": 9.0, "row_mfma": 9.1, "row_valu": 12.0}) == "row_mfma"
+    assert tune.choose({"col_mfma": 9.0, "row_mfma": 9.5}) == "col_mfma"
+
+
+def test_table_entries_are_sorted_and_complete():
+    blocks = tune.plan_blocks([(256, 688)], [1, 16], reps=5)
+    ops = {(b["op"], b["B"]) for b in blocks}
+    assert ops == {("gate_up", 1), ("down", 1), ("gate_up", 16), ("down", 16)}
+    # VALU variants only up to B = 8
+    assert not any(b["variant"].endswith("valu") and b["B"] > 8 for b in blocks)
+    entries = tune.build_table(blocks, [float(i + 1) for i in range(len(blocks))])
+    assert all(e["winner"] in e["us"] for e in entries)
+    assert [e["B"] for e in entries] == sorted(e["B"] for e in entries)
