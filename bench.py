@@ -11,8 +11,11 @@ beyond the 256 MB Infinity Cache) so every call streams its weights from HBM.
 
 Printed: one JSON line with the metric (us per MLP call; lower is better),
 the dominant kernel's roofline (algorithmic bytes / measured launch duration
-vs the 8 TB/s HBM peak), per-batch figures for B = 1..64, and the fp64 CPU
-oracle timed on the host cores over a bounded sample.
+vs the 8 TB/s HBM peak), per-batch figures for B = 1..64 (and, as context,
+for the Llama-3-70B layer shape), the 32-layer Llama-3-8B MLP stack per layer
+(eager calls, and the same chain captured once into a HIP graph and
+replayed), and the fp64 CPU oracle timed on the host cores over a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -132,6 +135,82 @@ def time_batch(B, sets, steps, warmup, device):
     return ms_call, ms_gu, ms_dn, (dfk.layout_name(gl), dfk.layout_name(dl))
 
 
+def time_stack(device, B=1, layers=32, steps=20, warmup=3):
+    """The 32-layer Llama-3-8B MLP stack (11.3 GB of distinct weights, cold by
+    construction), each layer's y the next layer's x: us per layer, eager and
+    as one captured HIP graph replayed."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import inputs
+
+    W = [inputs.stack_layer_weights_device(l, device) for l in range(layers)]
+    x0 = inputs.randn_bf16_device((B, D_MODEL), 1.0, 3000, device)
+    outs = [torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device) for _ in range(layers)]
+    s = torch.cuda.Stream()
+
+    def chain():
+        cur = x0
+        for w, o in zip(W, outs):
+            dfk.dfk_swiglu_mlp(cur, *w, out=o)
+            cur = o
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            chain()
+        s.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            chain()
+        e1.record(s)
+    e1.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        chain()
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            g.replay()
+        s.synchronize()
+        e0.record(s)
+        for _ in range(steps):
+            g.replay()
+        e1.record(s)
+    e1.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+    bytes_layer = mlp_bytes(B)
+    del g, W
+    torch.cuda.empty_cache()
+    return {"layers": layers, "batch": B, "weights_GB": round(layers * 3 * D_MODEL * D_FF * 2 / 1e9, 2),
+            "eager_us_per_layer": round(eager_us, 2), "graph_us_per_layer": round(graph_us, 2),
+            "graph_GBps": round(bytes_layer / (graph_us * 1e-6) / 1e9, 1)}
+
+
+def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
+    """Context: whole-MLP us per call at the Llama-3-70B layer shape
+    (d_model 8192, d_ff 28672), two weight sets rotated (2.8 GB)."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import inputs
+
+    dm, dff = 8192, 28672
+    sets = [(inputs.randn_bf16_device((dff, dm), 0.02, 7000 + 10 * r + 1, device),
+             inputs.randn_bf16_device((dff, dm), 0.02, 7000 + 10 * r + 2, device),
+             inputs.randn_bf16_device((dm, dff), 0.02, 7000 + 10 * r + 3, device)) for r in range(2)]
+    res = {}
+    for B in batches:
+        x = inputs.randn_bf16_device((B, dm), 1.0, 7100 + B, device)
+        out = torch.empty((B, dm), dtype=torch.bfloat16, device=device)
+        ms = _timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % 2], out), steps, warmup)
+        gbps = mlp_bytes(B, dm, dff) / (ms * 1e-3) / 1e9
+        res[str(B)] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(sets, budget_s=12.0, max_calls=400):
     """The fp64 oracle on the host cores: whole-MLP calls at B=1 on weight set 0."""
     import numpy as np
@@ -166,7 +245,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-batch sweep, the 70B-shape context and the 32-layer stack")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes)")
@@ -217,6 +297,11 @@ def main():
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
 
+    stack, shape70b = None, None
+    if not args.no_sweep:
+        shape70b = time_70b(device)
+        stack = time_stack(device)
+
     result = {
         "metric": METRIC,
         "value": round(us_per_call, 3),
@@ -252,6 +337,8 @@ def main():
             "algorithmic_bytes_per_launch": gate_up_bytes(B),
         },
         "per_batch": per_batch,
+        "per_batch_llama70b_shape": shape70b,
+        "stack32_llama8b": stack,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets)
