@@ -243,9 +243,22 @@ __device__ __forceinline__ void dn_valu_accumulate(const u32x4_t *const (&rd)[R]
 }
 
 // Stage `n` 16-byte vectors from global memory into LDS (whole workgroup).
+// Up to 8 loads per thread are issued before their stores, so the staging
+// costs about one memory latency per 8 x blockDim vectors, not one per
+// blockDim.
 template <typename T>
 __device__ __forceinline__ void stage_lds(T *dst, const T *src, int n) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+    constexpr int kBatch = 8;
+    const int step = blockDim.x;
+    for (int base = threadIdx.x; base < n; base += kBatch * step) {
+        T v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (base + q * step < n) v[q] = src[base + q * step];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (base + q * step < n) dst[base + q * step] = v[q];
+    }
     __syncthreads();
 }
 
@@ -256,29 +269,63 @@ __device__ __forceinline__ void stage_lds(T *dst, const T *src, int n) {
 // DPP butterfly and lane 63 runs the epilogue.  Persistent: wave w takes row
 // groups w, w + total_waves, ...
 
+// The row kernels walk a wave's (row group, load group) sequence flattened,
+// with two register buffers: the next load group (possibly the next row
+// group's first) is issued before the current one is multiplied, so loads
+// stay in flight across row boundaries and under the reductions.  Loads are
+// unconditional (addresses clamped into the row, the lanes past its end
+// masked at use) and the last one or two groups are peeled, so every wait in
+// the loop is for the oldest loads only.
 template <int B, int R, int U>
 __global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs a) {
     extern __shared__ u32x4_t xs[];  // [B][C]
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
     const int total_waves = gridDim.x * waves;
-    stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
-
-    for (int gi = blockIdx.x * waves + threadIdx.x / kWave; gi < a.groups; gi += total_waves) {
-        const u32x4_t *rg[R];
-        const u32x4_t *ru[R];
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    constexpr int G = kWave * U;                     // chunks per load group
+    const int gpr = (a.C + G - 1) / G;               // load groups per row group
+    const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
+    const int total = rows * gpr;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    float ag[R][B], au[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
+    auto load = [&](u32x4_t (&wg)[U][R], u32x4_t (&wu)[U][R], int k, int j) {
+        const int gi = wave_id + k * total_waves;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = min(gi * R + r, a.N - 1);
-            rg[r] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
-            ru[r] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+            const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
+            const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = min(j * G + kWave * u + lane, a.C - 1);
+                wg[u][r] = load_stream(pg + c);
+                wu[u][r] = load_stream(pu + c);
+            }
         }
-        float ag[R][B], au[R][B];
+    };
+    auto compute = [&](const u32x4_t (&wg)[U][R], const u32x4_t (&wu)[U][R], int j) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int u = 0; u < U; ++u) {
+            const int c = j * G + kWave * u + lane;
+            const bool ok = c < a.C;
 #pragma unroll
-            for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
-        gu_valu_accumulate<B, R, U>(rg, ru, xs, a.C, 0, a.C, lane, ag, au);
+            for (int b = 0; b < B; ++b) {
+                const u32x4_t xv = ok ? xs[b * a.C + c] : zero;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    ag[r][b] = dot8_bf16(wg[u][r], xv, ag[r][b]);
+                    au[r][b] = dot8_bf16(wu[u][r], xv, au[r][b]);
+                }
+            }
+        }
+    };
+    auto finish = [&](int k) {  // a row group's last load group is done: reduce, SiLU * u, store
+        const int gi = wave_id + k * total_waves;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -295,30 +342,140 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs
                     for (int b = 0; b < B; ++b) a.h[(size_t)b * a.N + n] = silu_mul(ag[r][b], au[r][b]);
             }
         }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
+    };
+    auto step = [&](const u32x4_t (&wg)[U][R], const u32x4_t (&wu)[U][R], int k, int j) {
+        compute(wg, wu, j);
+        if (j == gpr - 1) finish(k);
+    };
+    auto next = [&](int &k, int &j) {
+        if (++j == gpr) {
+            j = 0;
+            ++k;
+        }
+    };
+    u32x4_t g0[U][R], u0[U][R], g1[U][R], u1[U][R];
+    int k0 = 0, j0 = 0;
+    // the first weight loads go out before x is staged (they do not need it;
+    // a wave without work loads a clamped row and leaves after the barrier)
+    load(g0, u0, k0, j0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
+    if (wave_id >= a.groups) return;
+    int t = 0;
+    for (; t + 2 < total; t += 2) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(g1, u1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(g0, u0, k0, j0);
+        int k2 = k1, j2 = j1;
+        next(k2, j2);
+        load(g0, u0, k2, j2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(g1, u1, k1, j1);
+        k0 = k2;
+        j0 = j2;
+    }
+    if (t + 1 < total) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(g1, u1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(g0, u0, k0, j0);
+        step(g1, u1, k1, j1);
+    } else {
+        step(g0, u0, k0, j0);
     }
 }
 
+// (same flattened, double-buffered walk as the gate-up row kernel; without h
+// in LDS a load group also carries its h values, issued before its weights)
 template <int B, int R, int U, bool HLDS>
 __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
     extern __shared__ f32x4_t hs[];  // HLDS: [B][2C]
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
     const int total_waves = gridDim.x * waves;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
     const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
-    if (HLDS) stage_lds(hs, hg, B * 2 * a.C);
-    for (int gi = blockIdx.x * waves + threadIdx.x / kWave; gi < a.groups; gi += total_waves) {
-        const u32x4_t *rd[R];
+    constexpr int G = kWave * U;
+    constexpr int HU = HLDS ? 1 : U;  // h registers per group (none used with h in LDS)
+    const int gpr = (a.C + G - 1) / G;
+    const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
+    const int total = rows * gpr;
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    auto load = [&](u32x4_t (&wv)[U][R], f32x4_t (&hv)[HU][B][2], int k, int j) {
+        if constexpr (!HLDS) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = min(j * G + kWave * u + lane, a.C - 1);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    hv[u][b][0] = hg[(size_t)b * 2 * a.C + 2 * c];
+                    hv[u][b][1] = hg[(size_t)b * 2 * a.C + 2 * c + 1];
+                }
+            }
+        }
+        const int gi = wave_id + k * total_waves;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int m = min(gi * R + r, a.M - 1);
-            rd[r] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K);
+            const u32x4_t *pw = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K);
+#pragma unroll
+            for (int u = 0; u < U; ++u) wv[u][r] = load_stream(pw + min(j * G + kWave * u + lane, a.C - 1));
         }
-        float acc[R][B];
+    };
+    auto compute = [&](const u32x4_t (&wv)[U][R], const f32x4_t (&hv)[HU][B][2], int j) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int u = 0; u < U; ++u) {
+            const int c = j * G + kWave * u + lane;
+            const bool ok = c < a.C;
+            f32x4_t h2[B][2];
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-        dn_valu_accumulate<B, R, U, HLDS>(rd, hg, hs, a.C, 0, a.C, lane, acc);
+            for (int b = 0; b < B; ++b) {
+                if constexpr (HLDS) {
+                    const int cc = min(c, a.C - 1);
+                    h2[b][0] = hs[(size_t)b * 2 * a.C + 2 * cc];
+                    h2[b][1] = hs[(size_t)b * 2 * a.C + 2 * cc + 1];
+                } else {
+                    h2[b][0] = hv[u][b][0];
+                    h2[b][1] = hv[u][b][1];
+                }
+                if (!ok) h2[b][0] = h2[b][1] = fzero;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const u32x4_t w = wv[u][r];
+                const float w0 = bf16_lo(w.x), w1 = bf16_hi(w.x), w2 = bf16_lo(w.y), w3 = bf16_hi(w.y),
+                            w4 = bf16_lo(w.z), w5 = bf16_hi(w.z), w6 = bf16_lo(w.w), w7 = bf16_hi(w.w);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const f32x4_t h0 = h2[b][0], h1 = h2[b][1];
+                    float t = acc[r][b];
+                    t = fmaf(w0, h0.x, t);
+                    t = fmaf(w1, h0.y, t);
+                    t = fmaf(w2, h0.z, t);
+                    t = fmaf(w3, h0.w, t);
+                    t = fmaf(w4, h1.x, t);
+                    t = fmaf(w5, h1.y, t);
+                    t = fmaf(w6, h1.z, t);
+                    t = fmaf(w7, h1.w, t);
+                    acc[r][b] = t;
+                }
+            }
+        }
+    };
+    auto finish = [&](int k) {
+        const int gi = wave_id + k * total_waves;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -332,6 +489,54 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
                     for (int b = 0; b < B; ++b) a.y[(size_t)b * a.M + m] = to_bf16_rne(acc[r][b]);
             }
         }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    };
+    auto step = [&](const u32x4_t (&wv)[U][R], const f32x4_t (&hv)[HU][B][2], int k, int j) {
+        compute(wv, hv, j);
+        if (j == gpr - 1) finish(k);
+    };
+    auto next = [&](int &k, int &j) {
+        if (++j == gpr) {
+            j = 0;
+            ++k;
+        }
+    };
+    u32x4_t w0[U][R], w1[U][R];
+    f32x4_t h0[HU][B][2], h1[HU][B][2];
+    int k0 = 0, j0 = 0;
+    // the first loads go out before h is staged (a wave without work loads a
+    // clamped row and leaves after the barrier)
+    load(w0, h0, k0, j0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (HLDS) stage_lds(hs, hg, B * 2 * a.C);
+    if (wave_id >= a.groups) return;
+    int t = 0;
+    for (; t + 2 < total; t += 2) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(w1, h1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(w0, h0, k0, j0);
+        int k2 = k1, j2 = j1;
+        next(k2, j2);
+        load(w0, h0, k2, j2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(w1, h1, k1, j1);
+        k0 = k2;
+        j0 = j2;
+    }
+    if (t + 1 < total) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(w1, h1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(w0, h0, k0, j0);
+        step(w1, h1, k1, j1);
+    } else {
+        step(w0, h0, k0, j0);
     }
 }
 
@@ -1633,7 +1838,7 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #define DFK_GU_VALU_U(B) 4
 #endif
 #ifndef DFK_DN_VALU_R
-#define DFK_DN_VALU_R(B) ((B) == 1 ? 1 : ((B) == 2 ? 2 : 4))
+#define DFK_DN_VALU_R(B) ((B) <= 2 ? 2 : 4)
 #endif
 #ifndef DFK_DN_VALU_U
 #define DFK_DN_VALU_U(B) ((B) <= 2 ? 4 : 1)
@@ -1664,6 +1869,10 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 // 1: one block per group of work items (the hardware dispatcher balances)
 #ifndef DFK_GRID_MODE
 #define DFK_GRID_MODE 0
+#endif
+// 1: size persistent grids so every work item slot gets the same item count
+#ifndef DFK_BALANCE
+#define DFK_BALANCE 1
 #endif
 // the down projection's col traversal uses K panels across workgroups up to
 // this batch (h panels in LDS), and the in-workgroup K split above it
@@ -2020,6 +2229,13 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
     const long items_per_block = (ki.block / kWave) / ki.waves_per_item;
     const long all_items = ceil_div(q.groups, items_per_block);
     q.grid = (int)std::max(1L, DFK_GRID_MODE ? all_items : std::min((long)cus * occ, all_items));
+    if (DFK_BALANCE && !DFK_GRID_MODE) {
+        // persistent grid sized so that every work item slot gets the same
+        // number of items: no last round run by a fraction of the waves
+        const long slots = (long)q.grid * items_per_block;
+        const long per_slot = ceil_div((long)q.groups, slots);
+        q.grid = (int)std::max(1L, ceil_div(ceil_div((long)q.groups, per_slot), items_per_block));
+    }
     q.fn = ki.fn;
     *out = q;
     return true;

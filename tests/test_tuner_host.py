@@ -48,8 +48,9 @@ def test_block_costs_check_counts():
 
 
 def test_choose_tie_goes_to_row():
-    assert tune.choose({"row_valu": 10.15, "col_valu": 10.0}) == "row_valu"     # within 2 %
-    assert tune.choose({"row_valu": 10.5, "col_valu": 10.0}) == "col_valu"      # beyond 2 %
+    assert tune.choose({"row_valu": 10.25, "col_valu": 10.0}) == "row_valu"     # within 3 %
+    assert tune.choose({"row_valu": 10.5, "col_valu": 10.0}) == "col_valu"      # beyond 3 %
+    assert tune.choose({"row_valu": 10.25, "row_mfma": 10.0}) == "row_valu"     # VALU first in a tie
     assert tune.choose({"col_mfma": 9.0, "row_mfma": 9.1, "row_valu": 12.0}) == "row_mfma"
     assert tune.choose({"col_mfma": 9.0, "row_mfma": 9.5}) == "col_mfma"
 
