@@ -18,9 +18,10 @@ constexpr int kValuMaxBatch = 8;
 // LDS of one gfx950 CU: the most a workgroup may ask for (the VALU gate-up
 // kernels keep all of x there).
 constexpr size_t kLdsLimit = 160 * 1024;
-// The VALU down kernels keep all of h in LDS up to this size (two workgroups
-// per CU), else they read it through the caches.
-constexpr size_t kHLdsLimit = 64 * 1024;
+// The VALU down kernels keep all of h in LDS up to this size (one workgroup
+// per CU at the top; measured faster than reading h through the caches), else
+// they read it through the caches.
+constexpr size_t kHLdsLimit = 128 * 1024;
 // LDS budget of one h panel of the K-panel down kernel (two workgroups per CU).
 constexpr size_t kPanelLds = 64 * 1024;
 

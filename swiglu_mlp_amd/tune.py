@@ -8,7 +8,7 @@ that can run the shape (row_valu, col_valu, row_mfma, col_mfma) is launched
 back to back with rotating weight copies (at least 1.5 GB of distinct weights,
 so every launch streams from HBM rather than the 256 MB Infinity Cache).  The
 winner is the variant with the lowest median per-call cost; variants within
-3 % of the best count as a tie, which goes to a row variant (VALU first).  The result is the
+2 % of the best count as a tie, which goes to a row variant (VALU first).  The result is the
 JSON table that dfk_schedule_select reads.
 
 Timers:
@@ -16,8 +16,10 @@ Timers:
            cost is the spacing between its last kernel's end and the previous
            call's (a block's calls run back to back, so this is the kernel
            time plus the launch gap before it: what a stream of decode calls
-           pays per call);
-  events   HIP events around groups of back-to-back launches (no profiler).
+           pays per call).  The profile ranks every variant; those within
+           10 % of its best are then re-timed untraced (HIP events around
+           back-to-back calls) and the confirmation picks among them;
+  events   HIP events around groups of back-to-back launches only.
 
 This is the runtime scheduling across row-major and column-major variants of
 "Deep Kernel Fusion for Transformer Decoding" (podcast episode page, episode
@@ -45,11 +47,15 @@ if ROOT not in sys.path:
 DEFAULT_SHAPES = [(2048, 5632), (3072, 8192), (4096, 14336), (5120, 13824), (8192, 28672)]
 DEFAULT_BATCHES = [1, 2, 4, 8, 16, 32, 64]
 VARIANTS = ["row_valu", "col_valu", "row_mfma", "col_mfma"]
-# Variants within this fraction of the best count as a tie.  Measured on
-# MI355X, the trace's spacing reads the LDS-transposed MFMA kernels 2-3 %
-# faster, relative to the VALU kernels, than back-to-back event timing of the
-# same calls does; the band keeps that from flipping a choice.
-TIE = 0.03
+# Variants within this fraction of the best count as a tie (a row variant,
+# VALU first, wins a tie).
+TIE = 0.02
+# Variants within this fraction of the profile's best are re-timed back to
+# back with HIP events and no profiler attached, and that decides among them:
+# measured on MI355X, the traced run reads the LDS-transposed MFMA kernels up
+# to ~5 % faster, relative to the VALU kernels, than the same calls run
+# untraced.
+CONFIRM_BAND = 0.10
 ROTATE_BYTES = 1.5e9
 
 
@@ -195,14 +201,39 @@ def choose(timings_us):
     return min(timings_us, key=timings_us.get)
 
 
-def build_table(blocks, per_block_us):
+def _key(blk):
+    return (blk["op"], blk["B"], blk["d_model"], blk["d_ff"])
+
+
+def near_ties(blocks, per_block_us, band=CONFIRM_BAND):
+    """Blocks whose variant is within `band` of the best for its (op, B,
+    shape), for keys with more than one such variant."""
+    best = {}
+    for blk, us in zip(blocks, per_block_us):
+        best[_key(blk)] = min(us, best.get(_key(blk), float("inf")))
+    cand = [blk for blk, us in zip(blocks, per_block_us) if us <= best[_key(blk)] * (1 + band)]
+    count = {}
+    for blk in cand:
+        count[_key(blk)] = count.get(_key(blk), 0) + 1
+    return [blk for blk in cand if count[_key(blk)] > 1]
+
+
+def build_table(blocks, per_block_us, confirm=None):
+    """Table entries; `confirm` maps (op, B, d_model, d_ff) -> {variant: us}
+    from the untraced re-timing, which then decides among its variants."""
     table = {}
     for blk, us in zip(blocks, per_block_us):
-        key = (blk["op"], blk["B"], blk["d_model"], blk["d_ff"])
-        table.setdefault(key, {})[blk["variant"]] = round(us, 3)
+        table.setdefault(_key(blk), {})[blk["variant"]] = round(us, 3)
     entries = []
-    for (op, B, dm, dff), t in sorted(table.items(), key=lambda kv: (kv[0][2], kv[0][3], kv[0][1], kv[0][0])):
-        entries.append({"op": op, "B": B, "d_model": dm, "d_ff": dff, "winner": choose(t), "us": t})
+    for key, t in sorted(table.items(), key=lambda kv: (kv[0][2], kv[0][3], kv[0][1], kv[0][0])):
+        op, B, dm, dff = key
+        e = {"op": op, "B": B, "d_model": dm, "d_ff": dff, "us": t}
+        if confirm and key in confirm:
+            e["confirm_us"] = {v: round(u, 3) for v, u in confirm[key].items()}
+            e["winner"] = choose(confirm[key])
+        else:
+            e["winner"] = choose(t)
+        entries.append(e)
     return entries
 
 
@@ -239,16 +270,29 @@ def main():
         per_block = block_costs(parse_rocprof(outdir), blocks, args.warmup)
         shutil.rmtree(outdir, ignore_errors=True)
 
-    entries = build_table(blocks, per_block)
+    confirm = None
+    if args.timer == "rocprof":
+        cand = near_ties(blocks, per_block)
+        if cand:
+            cblocks = [dict(b, reps=max(b["reps"], 100)) for b in cand]
+            print(f"confirming {len(cblocks)} near-tie variants untraced", flush=True)
+            res = run_worker(cblocks, args.warmup, use_events=True)
+            confirm = {}
+            for b, t in zip(cblocks, res):
+                confirm.setdefault(_key(b), {})[b["variant"]] = statistics.median(t) * 1e3
+
+    entries = build_table(blocks, per_block, confirm)
     out = {"format": "dfk-tuning-v1", "arch": "gfx950", "timer": args.timer,
-           "tie_rule": f"within {int(TIE * 100)}% of the best median -> row variant",
+           "tie_rule": f"within {int(TIE * 100)}% of the best median -> row variant (VALU first)",
+           "confirm_band": CONFIRM_BAND if args.timer == "rocprof" else None,
            "entries": entries}
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
     for e in entries:
         ts = " ".join(f"{k}={v:8.2f}" for k, v in e["us"].items())
-        print(f"{e['op']:8s} B={e['B']:3d} {e['d_model']}x{e['d_ff']}: {e['winner']:9s} | {ts}", flush=True)
+        cs = " | confirm " + " ".join(f"{k}={v:8.2f}" for k, v in e["confirm_us"].items()) if "confirm_us" in e else ""
+        print(f"{e['op']:8s} B={e['B']:3d} {e['d_model']}x{e['d_ff']}: {e['winner']:9s} | {ts}{cs}", flush=True)
     print(f"wrote {args.out} ({len(entries)} entries)")
 
 

@@ -48,9 +48,9 @@ def test_block_costs_check_counts():
 
 
 def test_choose_tie_goes_to_row():
-    assert tune.choose({"row_valu": 10.25, "col_valu": 10.0}) == "row_valu"     # within 3 %
-    assert tune.choose({"row_valu": 10.5, "col_valu": 10.0}) == "col_valu"      # beyond 3 %
-    assert tune.choose({"row_valu": 10.25, "row_mfma": 10.0}) == "row_valu"     # VALU first in a tie
+    assert tune.choose({"row_valu": 10.15, "col_valu": 10.0}) == "row_valu"     # within 2 %
+    assert tune.choose({"row_valu": 10.3, "col_valu": 10.0}) == "col_valu"      # beyond 2 %
+    assert tune.choose({"row_valu": 10.15, "row_mfma": 10.0}) == "row_valu"     # VALU first in a tie
     assert tune.choose({"col_mfma": 9.0, "row_mfma": 9.1, "row_valu": 12.0}) == "row_mfma"
     assert tune.choose({"col_mfma": 9.0, "row_mfma": 9.5}) == "col_mfma"
 
@@ -64,3 +64,23 @@ def test_table_entries_are_sorted_and_complete():
     entries = tune.build_table(blocks, [float(i + 1) for i in range(len(blocks))])
     assert all(e["winner"] in e["us"] for e in entries)
     assert [e["B"] for e in entries] == sorted(e["B"] for e in entries)
+
+
+def test_near_ties_and_confirmed_winner():
+    blocks = tune.plan_blocks([(4096, 14336)], [4], reps=5)
+    # profile: gate_up row_mfma best, row_valu 3 % behind, the rest far behind
+    prof = {("gate_up", "row_mfma"): 39.0, ("gate_up", "row_valu"): 40.2, ("gate_up", "col_valu"): 45.0,
+            ("gate_up", "col_mfma"): 42.8, ("down", "row_valu"): 41.0, ("down", "col_valu"): 35.0,
+            ("down", "row_mfma"): 26.0, ("down", "col_mfma"): 26.1}
+    per = [prof[(b["op"], b["variant"])] for b in blocks]
+    cand = tune.near_ties(blocks, per, band=0.10)
+    got = {(b["op"], b["variant"]) for b in cand}
+    assert got == {("gate_up", "row_mfma"), ("gate_up", "row_valu"), ("gate_up", "col_mfma"),
+                   ("down", "row_mfma"), ("down", "col_mfma")}
+    # untraced re-timing reverses the gate-up order: it decides
+    confirm = {("gate_up", 4, 4096, 14336): {"row_mfma": 41.5, "row_valu": 39.6, "col_mfma": 43.0},
+               ("down", 4, 4096, 14336): {"row_mfma": 26.0, "col_mfma": 26.2}}
+    entries = {(e["op"]): e for e in tune.build_table(blocks, per, confirm)}
+    assert entries["gate_up"]["winner"] == "row_valu"
+    assert entries["down"]["winner"] == "row_mfma"
+    assert "confirm_us" in entries["gate_up"]
