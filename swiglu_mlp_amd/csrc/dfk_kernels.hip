@@ -1886,6 +1886,11 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_LT_GU_WAVES
 #define DFK_LT_GU_WAVES(BT) 4
 #endif
+// the row traversal (no K split) runs one tile per workgroup: more, smaller
+// workgroups spread the 16-neuron tiles over every CU
+#ifndef DFK_LT_GU_ROW_WAVES
+#define DFK_LT_GU_ROW_WAVES(BT) 1
+#endif
 #ifndef DFK_LT_GU_KSPLIT
 #define DFK_LT_GU_KSPLIT(BT) 4
 #endif
@@ -2024,7 +2029,7 @@ static void plan_panels(int C, size_t bytes_per_chunk, int groups, int cus, Plan
 }
 
 template <int BT> KernelInfo gu_lt_row() {
-    constexpr int W = DFK_LT_GU_WAVES(BT);
+    constexpr int W = DFK_LT_GU_ROW_WAVES(BT);
     return {(const void *)gate_up_mfma_lt_kernel<BT, 1, W>, 16, W * kWave, 1, 2 * BT * 4};
 }
 template <int BT> KernelInfo gu_lt_col() {
