@@ -68,6 +68,22 @@ extern "C" {
  * *_VALU / *_MFMA values force an engine (DFK_ERR_UNSUPPORTED where that
  * engine cannot run the shape).
  */
+/*
+ * Weight-traversal variant ("Deep Kernel Fusion for Transformer Decoding",
+ * episode summary: row-major and column-major kernel variants).  Weights are
+ * always stored row-major ([out, in], as nn.Linear keeps them); the layout
+ * picks how a kernel walks them.  ROW: a wave or workgroup owns whole output
+ * rows and walks all of K.  COL: K is split, among the waves of a workgroup or
+ * across workgroups, and the partial sums are added in a fixed order.
+ *   AUTO       the scheduler's choice for the shape (dfk_schedule_select)
+ *   ROW, COL   that traversal; the engine is VALU below 16 batch rows, else
+ *              the matrix cores (and the matrix cores when VALU cannot hold
+ *              the shape)
+ *   *_VALU     that traversal on the vector ALUs (bf16 dot2 / fp32 FMA),
+ *              B <= 8; DFK_ERR_UNSUPPORTED beyond what the engine holds
+ *   *_MFMA     that traversal on the matrix cores (bf16 MFMA, fp32
+ *              accumulation), any B <= 256
+ */
 typedef enum {
     DFK_LAYOUT_AUTO = 0,
     DFK_LAYOUT_ROW = 1,
