@@ -84,6 +84,8 @@ class Oracle:
         lib.oracle_rms_rescale.restype = ctypes.c_int
         lib.oracle_rms_rescale.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                            _u16p]
+        lib.oracle_rmsnorm.restype = ctypes.c_int
+        lib.oracle_rmsnorm.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _u16p]
 
     # -- scalars -----------------------------------------------------------
     def silu(self, z: float) -> float:
@@ -145,6 +147,19 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle_mlp failed ({rc})")
         return y, h
+
+    def rmsnorm(self, x, gain, eps: float = 1e-5) -> np.ndarray:
+        """RMS normalization ahead of the gate-up projections; returns bf16 bits [B, d_model]."""
+        x, g = _bits(x, "x"), _bits(gain, "gain")
+        B, d_model = x.shape
+        g = g.reshape(-1)
+        if g.shape != (d_model,):
+            raise ValueError("gain must be [d_model]")
+        out = np.empty_like(x)
+        rc = self._lib.oracle_rmsnorm(_p16(x), _p16(np.ascontiguousarray(g)), B, d_model, float(eps), _p16(out))
+        if rc != 0:
+            raise RuntimeError(f"oracle_rmsnorm failed ({rc})")
+        return out
 
     def rms_rescale(self, y_bits, eps: float = 1e-6) -> np.ndarray:
         """Between-layer rescale of the chained workload; returns bf16 bits."""

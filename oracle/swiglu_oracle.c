@@ -9,7 +9,8 @@
  *         swiglu_oracle.c -o liboracle.so -lm
  *
  * What it computes (each function names the passage it follows):
- *   g = x . W_gate^T,  u = x . W_up^T,  h = SiLU(g) * u,  y = h . W_down^T
+ *   g = x . W_gate^T,  u = x . W_up^T,  h = SiLU(g) * u,  y = h . W_down^T,
+ * and the RMS normalization that may precede the gate and up projections
  * with x [B, d_model], W_gate and W_up [d_ff, d_model], W_down [d_model, d_ff],
  * all given as bf16 bit patterns and widened exactly to fp64.  Every dot product
  * is summed in fp64 in ascending index order; nothing is rounded until the
@@ -285,6 +286,36 @@ int oracle_rms_rescale(const uint16_t *y_bits, int B, int d_model, double eps,
         double inv = 1.0 / sqrt(ss / (double)d_model + eps);
         for (int k = 0; k < d_model; ++k)
             x_next[(size_t)b * d_model + k] = oracle_bf16_rne(widen_bf16(row[k]) * inv);
+    }
+    return 0;
+}
+
+/*
+ * RMS normalization ahead of the gate and up projections.  "[FP16] Improved
+ * performance by fusing dequantize with compute in kernels" (GPULlama3.java
+ * pull-request page, commit list) fuses RMS normalization with the gate and
+ * up projections into one task and then merges that with the gated SiLU.  The
+ * page does not write the normalization out.  Reading taken: the RMSNorm of
+ * Llama-style models, per batch row b and column k,
+ *     xn[b,k] = bf16_RNE( (x[b,k] * inv_b) * gain[k] ),
+ *     inv_b   = 1 / sqrt( (sum_k x[b,k]^2) / d_model + eps ),
+ * with a bf16 gain [d_model].  Everything in fp64 (ascending-k sum of squares),
+ * one rounding to bf16 at the end: the normalized activations feed bf16
+ * projections.
+ */
+int oracle_rmsnorm(const uint16_t *x, const uint16_t *gain, int B, int d_model, double eps,
+                   uint16_t *xn) {
+    if (B < 0 || d_model <= 0 || !x || !gain || !xn) return -1;
+    for (int b = 0; b < B; ++b) {
+        const uint16_t *row = x + (size_t)b * d_model;
+        double ss = 0.0;
+        for (int k = 0; k < d_model; ++k) {
+            double v = widen_bf16(row[k]);
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)d_model + eps);
+        for (int k = 0; k < d_model; ++k)
+            xn[(size_t)b * d_model + k] = oracle_bf16_rne((widen_bf16(row[k]) * inv) * widen_bf16(gain[k]));
     }
     return 0;
 }

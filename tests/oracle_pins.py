@@ -276,9 +276,60 @@ def check_rms_rescale(orc):
     assert np.all(widen(orc.rms_rescale(ones, eps=0.0)) == 1.0)
 
 
+def _mp_rne_bf16_bits(v):
+    """Round an mpmath real to bf16 bits, ties to even, for normal-range values
+    (an implementation independent of the oracle's)."""
+    import mpmath
+    if v == 0:
+        return 0x8000 if mpmath.sign(v) < 0 else 0
+    m, e = mpmath.frexp(v)            # v = m * 2^e, 0.5 <= |m| < 1
+    q = mpmath.ldexp(1, int(e) - 8)   # one unit in the 8th significant bit
+    r = mpmath.nint(v / q) * q        # nint: nearest integer, ties to even
+    return int(np.float32(float(r)).view(np.uint32) >> 16)
+
+
+def check_rmsnorm_bruteforce(orc):
+    """Tiny rows against 60-digit arithmetic and an independent bf16 rounding."""
+    import mpmath
+    mpmath.mp.dps = 60
+    x = inputs.randn_bf16((3, 7), 1.5, seed=810)
+    g = inputs.randn_bf16((7,), 1.0, seed=811)
+    for eps in (0.0, 1e-5, 0.25):
+        xn = orc.rmsnorm(x, g, eps=eps)
+        xf, gf = widen(x), widen(g)
+        for b in range(3):
+            ss = mpmath.fsum(mpmath.mpf(float(v)) ** 2 for v in xf[b])
+            inv = 1 / mpmath.sqrt(ss / 7 + mpmath.mpf(eps))
+            for k in range(7):
+                want = _mp_rne_bf16_bits(mpmath.mpf(float(xf[b, k])) * inv * mpmath.mpf(float(gf[k])))
+                assert int(xn[b, k]) == want, (eps, b, k)
+
+
+def check_rmsnorm_invariants(orc):
+    """Exact invariants: power-of-two scaling of x (eps = 0) changes nothing;
+    doubling the gain doubles the output; a constant row maps to the gain
+    itself; rows are independent; eps dominates a tiny row."""
+    x = inputs.randn_bf16((4, 96), 2.0, seed=820)
+    g = inputs.randn_bf16((96,), 1.0, seed=821)
+    base = orc.rmsnorm(x, g, eps=0.0)
+    assert np.array_equal(orc.rmsnorm(bf16_of(8 * widen(x)), g, eps=0.0), base)
+    assert np.array_equal(orc.rmsnorm(x, bf16_of(2 * widen(g)), eps=0.0), bf16_of(2 * widen(base)))
+    const = bf16_of(np.full((2, 96), 8.0))
+    assert np.array_equal(orc.rmsnorm(const, g, eps=0.0), np.stack([g, g]))
+    for b in range(4):
+        assert np.array_equal(orc.rmsnorm(x[b:b + 1], g, eps=1e-5)[0], orc.rmsnorm(x, g, eps=1e-5)[b])
+    tiny = bf16_of(np.full((1, 96), 2.0 ** -12))
+    ones = bf16_of(np.ones(96))
+    want = bf16_of(np.full((1, 96), 2.0 ** -12 / np.sqrt(2.0 ** -24 + 1.0)))
+    assert np.array_equal(orc.rmsnorm(tiny, ones, eps=1.0), want)
+    # unit gain: mean square 1 up to the bf16 rounding
+    assert np.allclose((widen(orc.rmsnorm(x, ones, eps=0.0)) ** 2).mean(axis=1), 1.0, rtol=1e-2)
+
+
 ALL_CHECKS = [
     check_silu_tanh_form, check_silu_lambert_minimum, check_silu_identities,
     check_silu_limits, check_bf16_rne, check_worked_example, check_bruteforce_tiny,
     check_extended_precision, check_zero_invariants, check_linearity_in_wdown,
     check_batch_and_permutation, check_threads_deterministic, check_rms_rescale,
+    check_rmsnorm_bruteforce, check_rmsnorm_invariants,
 ]

@@ -27,6 +27,14 @@ MUTANTS = {
     "y_stored_transposed": ("c->y[(size_t)b * M + (size_t)m] = acc[b];",
                             "c->y[(size_t)m * B + (size_t)b] = acc[b];"),
     "bf16_truncates": ("nearbyint(a / q)", "floor(a / q)"),
+    "rmsnorm_sum_not_mean": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn[",
+                             "double inv = 1.0 / sqrt(ss + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
+    "rmsnorm_no_eps": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn[",
+                       "double inv = 1.0 / sqrt(ss / (double)d_model);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
+    "rmsnorm_no_sqrt": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn[",
+                        "double inv = 1.0 / (ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
+    "rmsnorm_gain_first_only": ("* widen_bf16(gain[k])", "* widen_bf16(gain[0])"),
+    "rmsnorm_batch_stride": ("const uint16_t *row = x + (size_t)b * d_model;", "const uint16_t *row = x + (size_t)b;"),
 }
 
 
