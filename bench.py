@@ -211,6 +211,37 @@ def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
     return res
 
 
+def time_rmsnorm(sets, device, batches=(1, 4, 8, 16), steps=200, warmup=20):
+    """Context: the MLP on RMS-normalized input at the 8B layer shape, us per
+    call: the fused entry point (norm inside gate-up where the kernel stages
+    x in LDS), the norm kernel then the plain MLP, and the plain MLP alone."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import inputs
+
+    gain = inputs.randn_bf16_device((D_MODEL,), 0.1, 6200, device).add_(1.0)
+    R = len(sets)
+    res = {}
+    for B in batches:
+        x = inputs.randn_bf16_device((B, D_MODEL), 1.0, 6100 + B, device)
+        xn = torch.empty_like(x)
+        out = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device)
+
+        def fused(i):
+            dfk.dfk_rmsnorm_swiglu_mlp(x, gain, 1e-5, *sets[i % R], out)
+
+        def separate(i):
+            dfk.dfk_rmsnorm(x, gain, 1e-5, xn)
+            dfk.dfk_swiglu_mlp(xn, *sets[i % R], out)
+
+        def plain(i):
+            dfk.dfk_swiglu_mlp(x, *sets[i % R], out)
+
+        res[str(B)] = {k: round(_timed(f, steps, warmup) * 1e3, 2)
+                       for k, f in (("fused_us", fused), ("separate_us", separate), ("no_norm_us", plain))}
+    return res
+
+
 def cpu_baseline(sets, budget_s=12.0, max_calls=400):
     """The fp64 oracle on the host cores: whole-MLP calls at B=1 on weight set 0."""
     import numpy as np
@@ -297,8 +328,9 @@ def main():
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
 
-    stack, shape70b = None, None
+    stack, shape70b, norm = None, None, None
     if not args.no_sweep:
+        norm = time_rmsnorm(sets, device)
         shape70b = time_70b(device)
         stack = time_stack(device)
 
@@ -339,6 +371,7 @@ def main():
         "per_batch": per_batch,
         "per_batch_llama70b_shape": shape70b,
         "stack32_llama8b": stack,
+        "rmsnorm_mlp_llama8b": norm,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets)

@@ -144,6 +144,48 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
                             int d_ff, dfk_layout_t layout, hipStream_t stream);
 
 /*
+ * RMS normalization of the MLP input (GPULlama3.java pull request "[FP16] ...
+ * fusing dequantize with compute", commit list: RMS normalization fused with
+ * the gate and up projections; the page does not define the normalization,
+ * so this is Llama's RMSNorm).  For each batch row b,
+ *     inv_b = 1 / sqrt( (sum_k x[b,k]^2) / d_model + eps ),
+ *     xn[b,k] = RNE_bf16( (x[b,k] * inv_b) * gain[k] ),
+ * all in fp64 and rounded once, fp64 -> bf16, ties to even.
+ *   x     [B, d_model]  bf16 device    gain [d_model] bf16 device
+ *   xn    [B, d_model]  bf16 device output (must not alias x)
+ *   eps   >= 0 and finite, else DFK_ERR_INVALID_ARG (eps = 0 with an all-zero
+ *         row gives NaN, as the formula does)
+ * One launch (one workgroup per batch row), no scratch memory.  B and d_model
+ * follow the limits above.
+ */
+dfk_status_t dfk_rmsnorm(const uint16_t *x, const uint16_t *gain, double eps, uint16_t *xn, int B,
+                         int d_model, hipStream_t stream);
+
+/*
+ * dfk_rmsnorm then dfk_gate_up_silu_mul, with the normalization fused into
+ * gate-up where that kernel stages x in LDS (the vector-ALU variants: each
+ * workgroup normalizes its copy of x there, one launch, no scratch).  The
+ * matrix-core variants run dfk_rmsnorm into a library-owned bf16 buffer
+ * (B * d_model * 2 bytes, per (device, stream)) and then their usual kernel.
+ * Either way h is bit for bit what dfk_rmsnorm followed by
+ * dfk_gate_up_silu_mul with the same plan gives.  The layout picks the
+ * gate-up variant as for dfk_gate_up_silu_mul.
+ */
+dfk_status_t dfk_rmsnorm_gate_up_silu_mul(const uint16_t *x, const uint16_t *gain, double eps,
+                                          const uint16_t *W_gate, const uint16_t *W_up, float *h, int B,
+                                          int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream);
+
+/*
+ * The whole MLP on RMS-normalized input: dfk_rmsnorm_gate_up_silu_mul then
+ * dfk_down_proj on the same stream, h (and, for matrix-core gate-up plans,
+ * the normalized x) in the library-owned workspace of dfk_swiglu_mlp.
+ */
+dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, double eps,
+                                    const uint16_t *W_gate, const uint16_t *W_up, const uint16_t *W_down,
+                                    uint16_t *out, int B, int d_model, int d_ff, dfk_layout_t layout,
+                                    hipStream_t stream);
+
+/*
  * Profiler-driven variant choice ("Deep Kernel Fusion for Transformer
  * Decoding", episode summary: runtime scheduling across row-major and
  * column-major kernel variants; "Deep Kernel Fusion for Transformers",

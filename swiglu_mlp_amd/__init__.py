@@ -51,7 +51,8 @@ class Status(enum.IntEnum):
 EXPORTED = (
     "dfk_gate_up_silu_mul", "dfk_down_proj", "dfk_swiglu_mlp", "dfk_schedule_select",
     "dfk_status_string", "dfk_layout_name", "dfk_version", "dfk_load_tuning_table",
-    "dfk_tuning_table_source", "dfk_release_workspace",
+    "dfk_tuning_table_source", "dfk_release_workspace", "dfk_rmsnorm",
+    "dfk_rmsnorm_gate_up_silu_mul", "dfk_rmsnorm_swiglu_mlp",
 )
 
 
@@ -95,6 +96,13 @@ def lib() -> ctypes.CDLL:
     L.dfk_tuning_table_source.restype = ctypes.c_char_p
     L.dfk_release_workspace.argtypes = []
     L.dfk_release_workspace.restype = i
+    d = ctypes.c_double
+    L.dfk_rmsnorm.argtypes = [u16p, u16p, d, u16p, i, i, vp]
+    L.dfk_rmsnorm.restype = i
+    L.dfk_rmsnorm_gate_up_silu_mul.argtypes = [u16p, u16p, d, u16p, u16p, f32p, i, i, i, i, vp]
+    L.dfk_rmsnorm_gate_up_silu_mul.restype = i
+    L.dfk_rmsnorm_swiglu_mlp.argtypes = [u16p, u16p, d, u16p, u16p, u16p, u16p, i, i, i, i, vp]
+    L.dfk_rmsnorm_swiglu_mlp.restype = i
     _lib = L
     return L
 
@@ -186,6 +194,62 @@ def dfk_swiglu_mlp(x, W_gate, W_up, W_down, out=None, layout: int = Layout.AUTO,
                               out.data_ptr(), B, d_model, d_ff, int(layout),
                               _stream_handle(stream, x.device))
     _check(st, "dfk_swiglu_mlp")
+    return out
+
+
+def dfk_rmsnorm(x, gain, eps: float = 1e-5, out=None, stream=None):
+    """out = bf16_RNE((x * inv) * gain), inv = 1/sqrt(mean(x^2) + eps) per row."""
+    import torch
+    B, d_model = x.shape
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(gain, "gain", torch.bfloat16, (d_model,))
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=x.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_rmsnorm(x.data_ptr(), gain.data_ptr(), float(eps), out.data_ptr(), B, d_model,
+                           _stream_handle(stream, x.device))
+    _check(st, "dfk_rmsnorm")
+    return out
+
+
+def dfk_rmsnorm_gate_up_silu_mul(x, gain, eps: float, W_gate, W_up, h=None, layout: int = Layout.AUTO,
+                                 stream=None):
+    """h = SiLU(xn W_gate^T) * (xn W_up^T), xn the RMS normalization of x."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(gain, "gain", torch.bfloat16, (d_model,))
+    _expect(W_gate, "W_gate", torch.bfloat16, (d_ff, d_model))
+    _expect(W_up, "W_up", torch.bfloat16, (d_ff, d_model))
+    if h is None:
+        h = torch.empty((B, d_ff), dtype=torch.float32, device=x.device)
+    _expect(h, "h", torch.float32, (B, d_ff))
+    st = lib().dfk_rmsnorm_gate_up_silu_mul(x.data_ptr(), gain.data_ptr(), float(eps), W_gate.data_ptr(),
+                                            W_up.data_ptr(), h.data_ptr(), B, d_model, d_ff, int(layout),
+                                            _stream_handle(stream, x.device))
+    _check(st, "dfk_rmsnorm_gate_up_silu_mul")
+    return h
+
+
+def dfk_rmsnorm_swiglu_mlp(x, gain, eps: float, W_gate, W_up, W_down, out=None, layout: int = Layout.AUTO,
+                           stream=None):
+    """The whole MLP on the RMS-normalized input."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(gain, "gain", torch.bfloat16, (d_model,))
+    _expect(W_gate, "W_gate", torch.bfloat16, (d_ff, d_model))
+    _expect(W_up, "W_up", torch.bfloat16, (d_ff, d_model))
+    _expect(W_down, "W_down", torch.bfloat16, (d_model, d_ff))
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=x.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_rmsnorm_swiglu_mlp(x.data_ptr(), gain.data_ptr(), float(eps), W_gate.data_ptr(),
+                                      W_up.data_ptr(), W_down.data_ptr(), out.data_ptr(), B, d_model, d_ff,
+                                      int(layout), _stream_handle(stream, x.device))
+    _check(st, "dfk_rmsnorm_swiglu_mlp")
     return out
 
 

@@ -60,19 +60,34 @@ struct Plan {
     int splits;          // K panels (panel kinds), else 1
     int chunks_per_split;     // 16-byte chunks per panel
     size_t partial_floats;    // scratch the plan needs (panel partial sums), else 0
+    bool fused_norm;     // gate-up: the kernel applies the RMS normalization itself
     const void *fn;      // the kernel
+};
+
+// RMS normalization ahead of gate-up: xn = bf16_RNE((x * inv) * gain),
+// inv = 1 / sqrt(mean_k x^2 + eps) per batch row, all in fp64.
+struct NormArgs {
+    const uint16_t *gain;  // [d_model] bf16
+    double eps;
 };
 
 // Fill a plan for the given shape, engine and traversal.  Returns false when
 // the engine cannot run the shape (e.g. VALU with B above kValuMaxBatch, or x
 // too large to keep in LDS).  `cus` is the device's compute-unit count.
+// norm (gate-up only): fold the RMS normalization in where the kernel stages
+// x in LDS (VALU: p.fused_norm is set); other kernels keep their plan and the
+// caller normalizes x into a buffer first (launch_rmsnorm).
 bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus,
-               Plan *plan);
+               Plan *plan, bool norm = false);
 
 // Enqueue the kernel of a plan on `stream`.
 // `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate,
-                          const uint16_t *w_up, float *h, float *partial, hipStream_t stream);
+                          const uint16_t *w_up, float *h, float *partial, hipStream_t stream,
+                          const NormArgs *norm = nullptr);
+// xn [B][K] = the RMS normalization of x [B][K] (one workgroup per batch row).
+hipError_t launch_rmsnorm(const uint16_t *x, const NormArgs &norm, uint16_t *xn, int B, int K,
+                          hipStream_t stream);
 // `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y,
                        float *partial, hipStream_t stream);

@@ -136,6 +136,8 @@ struct GateUpArgs {
     int B, K, N;  // batch, d_model, d_ff
     int C;        // 16-byte chunks per weight row (K / 8)
     int groups;   // work items: row groups (ROW: per wave, COL: per workgroup)
+    const uint16_t *gain;  // RMS normalization (NORM kernels only): gain [d_model]
+    double eps;            //   and epsilon
 };
 
 struct DownArgs {
@@ -262,6 +264,178 @@ __device__ __forceinline__ void stage_lds(T *dst, const T *src, int n) {
     __syncthreads();
 }
 
+// ---------------------------------------------------- RMS normalization ----
+//
+// xn[b,k] = bf16_RNE((x[b,k] * inv_b) * gain[k]), inv_b = 1 / sqrt(mean_k
+// x[b,k]^2 + eps): Llama-style RMSNorm ahead of the gate and up projections
+// (the GPULlama3.java pull-request page fuses RMS normalization with them).
+// Rounding xn to bf16 decides the projections' inputs, so it is taken from
+// fp64 values, rounded once (no detour through binary32, which would round
+// twice).
+
+__device__ __forceinline__ double widen_bf16_f64(uint32_t bits16) { return (double)__uint_as_float(bits16 << 16); }
+
+// Nearest bf16 of a double, ties to even, rounded once: 8 significant bits,
+// the binary32 exponent range, subnormals down to 2^-133, overflow to
+// infinity, NaN to the quiet NaN 0x7FC0.  With |d| in [2^e, 2^(e+1)) (e
+// clamped to [-126, 128]), C = 1.5 * 2^(e+45) has an fp64 ulp of 2^(e-7), the
+// bf16 spacing at that binade (2^-133 for the subnormals), and |d| + C stays in
+// C's binade: the fp64 addition rounds |d| to that spacing, ties to even, and
+// subtracting C again is exact.  The result is then exact in binary32
+// (2^128 and above become infinity there).
+__device__ __forceinline__ uint32_t bf16_rne_from_f64(double d) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(d);
+    const uint32_t hi = (uint32_t)(u >> 32);
+    uint32_t e = hi & 0x7FF00000u;
+    e = min(max(e, (1023u - 126u) << 20), (1023u + 128u) << 20);
+    const double c = __longlong_as_double((long long)((unsigned long long)(e + (45u << 20) + 0x00080000u) << 32));
+    const double r = (fabs(d) + c) - c;
+    const uint32_t bits = (__float_as_uint((float)r) >> 16) | ((hi >> 16) & 0x8000u);
+    return d != d ? 0x7FC0u : bits;
+}
+
+// Sum of squares of one 16-byte chunk (8 values, in column order) added to ss.
+__device__ __forceinline__ double rms_sumsq_chunk(u32x4_t v, double ss) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const double lo = widen_bf16_f64(w[e] & 0xFFFFu), hi = widen_bf16_f64(w[e] >> 16);
+        ss = fma(lo, lo, ss);
+        ss = fma(hi, hi, ss);
+    }
+    return ss;
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+    // both halves moved with the same pattern; disabled lanes read +0.0
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// The fp64 sum over the 64 lanes in the DPP pattern of wave_sum_to_lane63;
+// the total lands in lane 63.
+__device__ __forceinline__ double wave_sum_f64_to_lane63(double v) {
+    v += dpp_f64<0xb1>(v);
+    v += dpp_f64<0x4e>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    v += dpp_f64<0x142, 0xa>(v);
+    v += dpp_f64<0x143, 0xc>(v);
+    return v;
+}
+
+// The normalization code runs in workgroups of kValuBlock threads (the VALU
+// gate-up kernels and the standalone kernel); the size is a constant so that
+// it never has to be read from the dispatch packet, a memory load whose wait
+// would also wait for the weight loads in flight.
+constexpr int kNormThreads = kValuBlock;
+
+// inv_b = 1 / sqrt(ss_b / K + eps) for b < B from every thread's partial sum
+// ss[b]: the wave sums, then the waves' in wave order through LDS (part:
+// B * kNormThreads / 64 doubles).  Every thread returns the same values.
+template <int MAXB>
+__device__ void rms_inv_from_partials(double (&ss)[MAXB], int B, int K, double eps, double *part,
+                                      double (&inv)[MAXB]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    constexpr int waves = kNormThreads / kWave;
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+        const double t = wave_sum_f64_to_lane63(ss[b]);
+        if (b < B && lane == kWave - 1) part[b * waves + wave] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+        double s = 0.0;
+        if (b < B)
+            for (int w = 0; w < waves; ++w) s += part[b * waves + w];
+        inv[b] = 1.0 / sqrt(s / (double)K + eps);
+    }
+}
+
+// One 16-byte chunk (8 columns) of a row, normalized: (x * inv) * gain in
+// fp64, rounded to bf16.
+__device__ __forceinline__ u32x4_t rms_apply_chunk(u32x4_t v, u32x4_t g, double inv) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = bf16_rne_from_f64((widen_bf16_f64(w[e] & 0xFFFFu) * inv) * widen_bf16_f64(gw[e] & 0xFFFFu));
+        const uint32_t hi = bf16_rne_from_f64((widen_bf16_f64(w[e] >> 16) * inv) * widen_bf16_f64(gw[e] >> 16));
+        o[e] = lo | (hi << 16);
+    }
+    return u32x4_t{o[0], o[1], o[2], o[3]};
+}
+
+// A thread's first kGainRegs gain chunks (c = tid + i * kNormThreads), loaded
+// ahead of x so that they arrive with it (indices clamped into the row).
+constexpr int kGainRegs = 2;
+__device__ __forceinline__ void rms_gain_prefetch(const uint16_t *gain, int C, u32x4_t (&g)[kGainRegs]) {
+    const u32x4_t *gg = reinterpret_cast<const u32x4_t *>(gain);
+#pragma unroll
+    for (int i = 0; i < kGainRegs; ++i) g[i] = gg[min((int)threadIdx.x + i * kNormThreads, C - 1)];
+}
+
+// Normalize x staged in LDS ([B][C] chunks) in place (whole workgroup).  Each
+// thread sums and rewrites its chunks c = tid, tid + kNormThreads, ... of
+// every row, in that order.
+template <int B>
+__device__ void rms_normalize_lds(u32x4_t *xs, const GateUpArgs &a, double *part, const u32x4_t (&greg)[kGainRegs]) {
+    double ss[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) ss[b] = 0.0;
+    for (int c = threadIdx.x; c < a.C; c += kNormThreads)
+#pragma unroll
+        for (int b = 0; b < B; ++b) ss[b] = rms_sumsq_chunk(xs[(size_t)b * a.C + c], ss[b]);
+    double inv[B];
+    rms_inv_from_partials<B>(ss, B, a.K, a.eps, part, inv);
+    auto apply = [&](int c, u32x4_t g) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) xs[(size_t)b * a.C + c] = rms_apply_chunk(xs[(size_t)b * a.C + c], g, inv[b]);
+    };
+#pragma unroll
+    for (int i = 0; i < kGainRegs; ++i) {
+        const int c = threadIdx.x + i * kNormThreads;
+        if (c < a.C) apply(c, greg[i]);
+    }
+    const u32x4_t *gg = reinterpret_cast<const u32x4_t *>(a.gain);
+    for (int c = threadIdx.x + kGainRegs * kNormThreads; c < a.C; c += kNormThreads) apply(c, gg[c]);
+    __syncthreads();
+}
+
+// Standalone: one workgroup per batch row, of the VALU gate-up kernels' size
+// and with their order of summation, so that it gives the x they normalize
+// in LDS bit for bit.
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t *x, const uint16_t *gain, double eps,
+                                                               uint16_t *xn, int K) {
+    __shared__ double part[kNormThreads / kWave];
+    const int C = K / 8;
+    const int tid = threadIdx.x;
+    constexpr int nt = kNormThreads;
+    const u32x4_t *row = reinterpret_cast<const u32x4_t *>(x + (size_t)blockIdx.x * K);
+    const u32x4_t *gg = reinterpret_cast<const u32x4_t *>(gain);
+    u32x4_t *out = reinterpret_cast<u32x4_t *>(xn + (size_t)blockIdx.x * K);
+    u32x4_t greg[kGainRegs], xr[kGainRegs];
+    rms_gain_prefetch(gain, C, greg);
+#pragma unroll
+    for (int i = 0; i < kGainRegs; ++i) xr[i] = row[min(tid + i * nt, C - 1)];
+    double ss[1] = {0.0};
+#pragma unroll
+    for (int i = 0; i < kGainRegs; ++i)
+        if (tid + i * nt < C) ss[0] = rms_sumsq_chunk(xr[i], ss[0]);
+    for (int c = tid + kGainRegs * nt; c < C; c += nt) ss[0] = rms_sumsq_chunk(row[c], ss[0]);
+    double inv[1];
+    rms_inv_from_partials<1>(ss, 1, K, eps, part, inv);
+#pragma unroll
+    for (int i = 0; i < kGainRegs; ++i)
+        if (tid + i * nt < C) out[tid + i * nt] = rms_apply_chunk(xr[i], greg[i], inv[0]);
+    for (int c = tid + kGainRegs * nt; c < C; c += nt) out[c] = rms_apply_chunk(row[c], gg[c], inv[0]);
+}
+
 // ==================================================== VALU row kernels =====
 //
 // ROW: a wave owns R rows (gate-up: R neurons, i.e. R rows of W_gate and the
@@ -276,9 +450,9 @@ __device__ __forceinline__ void stage_lds(T *dst, const T *src, int n) {
 // unconditional (addresses clamped into the row, the lanes past its end
 // masked at use) and the last one or two groups are peeled, so every wait in
 // the loop is for the oldest loads only.
-template <int B, int R, int U>
+template <int B, int R, int U, bool NORM>
 __global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs a) {
-    extern __shared__ u32x4_t xs[];  // [B][C]
+    extern __shared__ u32x4_t xs[];  // [B][C] (NORM: then B * waves doubles)
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
     const int total_waves = gridDim.x * waves;
@@ -357,38 +531,57 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs
             ++k;
         }
     };
+    // the walk from item t on; buffer A holds item t (its loads issued)
+    auto walk = [&](auto &ga, auto &ua, auto &gb, auto &ub, int t, int ka, int ja) {
+        for (; t + 2 < total; t += 2) {
+            int kb = ka, jb = ja;
+            next(kb, jb);
+            load(gb, ub, kb, jb);
+            __builtin_amdgcn_sched_barrier(0);
+            step(ga, ua, ka, ja);
+            int kc = kb, jc = jb;
+            next(kc, jc);
+            load(ga, ua, kc, jc);
+            __builtin_amdgcn_sched_barrier(0);
+            step(gb, ub, kb, jb);
+            ka = kc;
+            ja = jc;
+        }
+        if (t + 1 < total) {
+            int kb = ka, jb = ja;
+            next(kb, jb);
+            load(gb, ub, kb, jb);
+            __builtin_amdgcn_sched_barrier(0);
+            step(ga, ua, ka, ja);
+            step(gb, ub, kb, jb);
+        } else {
+            step(ga, ua, ka, ja);
+        }
+    };
     u32x4_t g0[U][R], u0[U][R], g1[U][R], u1[U][R];
     int k0 = 0, j0 = 0;
     // the first weight loads go out before x is staged (they do not need it;
     // a wave without work loads a clamped row and leaves after the barrier)
     load(g0, u0, k0, j0);
+    u32x4_t greg[kGainRegs];
+    if constexpr (NORM) rms_gain_prefetch(a.gain, a.C, greg);
     __builtin_amdgcn_sched_barrier(0);
     stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
-    if (wave_id >= a.groups) return;
-    int t = 0;
-    for (; t + 2 < total; t += 2) {
+    if constexpr (NORM) {
+        // the second load group goes out before the normalization, so that
+        // HBM keeps streaming under its arithmetic
         int k1 = k0, j1 = j0;
         next(k1, j1);
-        load(g1, u1, k1, j1);
+        const bool more = total > 1;
+        if (more) load(g1, u1, k1, j1);
         __builtin_amdgcn_sched_barrier(0);
+        rms_normalize_lds<B>(xs, a, reinterpret_cast<double *>(xs + (size_t)B * a.C), greg);
+        if (wave_id >= a.groups) return;
         step(g0, u0, k0, j0);
-        int k2 = k1, j2 = j1;
-        next(k2, j2);
-        load(g0, u0, k2, j2);
-        __builtin_amdgcn_sched_barrier(0);
-        step(g1, u1, k1, j1);
-        k0 = k2;
-        j0 = j2;
-    }
-    if (t + 1 < total) {
-        int k1 = k0, j1 = j0;
-        next(k1, j1);
-        load(g1, u1, k1, j1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(g0, u0, k0, j0);
-        step(g1, u1, k1, j1);
+        if (more) walk(g1, u1, g0, u0, 1, k1, j1);
     } else {
-        step(g0, u0, k0, j0);
+        if (wave_id >= a.groups) return;
+        walk(g0, u0, g1, u1, 0, k0, j0);
     }
 }
 
@@ -548,16 +741,20 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
 // LDS before wave 0 runs the epilogue.  More waves per row than ROW: the
 // choice when rows are few or long.  Persistent over row groups.
 
-template <int B, int R, int U>
+template <int B, int R, int U, bool NORM>
 __global__ __launch_bounds__(kValuBlock) void gate_up_valu_col_kernel(GateUpArgs a) {
     constexpr int NV = 2 * R * B;
-    extern __shared__ u32x4_t smem[];  // x [B][C], then red [waves][NV] floats
+    // x [B][C], then red [waves][NV] floats (NORM: then B * waves doubles)
+    extern __shared__ u32x4_t smem[];
     u32x4_t *xs = smem;
     float *red = reinterpret_cast<float *>(smem + (size_t)B * a.C);
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
+    u32x4_t greg[kGainRegs];
+    if constexpr (NORM) rms_gain_prefetch(a.gain, a.C, greg);
     stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
+    if constexpr (NORM) rms_normalize_lds<B>(xs, a, reinterpret_cast<double *>(red + waves * NV), greg);
     const int cw = (a.C + waves - 1) / waves;
     const int c_beg = min(wave * cw, a.C);
     const int c_end = min(c_beg + cw, a.C);
@@ -1964,14 +2161,18 @@ struct KernelInfo {
     int nv;              // COL combine floats per lane
 };
 
-template <int B> KernelInfo gu_valu_row() {
+template <int B, bool NORM> KernelInfo gu_valu_row_t() {
     constexpr int R = DFK_GU_VALU_R(B), U = DFK_GU_VALU_U(B);
-    return {(const void *)gate_up_valu_row_kernel<B, R, U>, R, kValuBlock, 1, 0};
+    return {(const void *)gate_up_valu_row_kernel<B, R, U, NORM>, R, kValuBlock, 1, 0};
 }
-template <int B> KernelInfo gu_valu_col() {
+template <int B, bool NORM> KernelInfo gu_valu_col_t() {
     constexpr int R = DFK_GU_VALU_R(B), U = DFK_GU_VALU_U(B);
-    return {(const void *)gate_up_valu_col_kernel<B, R, U>, R, kValuBlock, kValuBlock / kWave, 2 * R * B};
+    return {(const void *)gate_up_valu_col_kernel<B, R, U, NORM>, R, kValuBlock, kValuBlock / kWave, 2 * R * B};
 }
+template <int B> KernelInfo gu_valu_row() { return gu_valu_row_t<B, false>(); }
+template <int B> KernelInfo gu_valu_col() { return gu_valu_col_t<B, false>(); }
+template <int B> KernelInfo gu_valu_row_norm() { return gu_valu_row_t<B, true>(); }
+template <int B> KernelInfo gu_valu_col_norm() { return gu_valu_col_t<B, true>(); }
 template <int B, bool HLDS> KernelInfo dn_valu_row_t() {
     constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
     return {(const void *)down_valu_row_kernel<B, R, U, HLDS>, R, kValuBlock, 1, 0};
@@ -2067,6 +2268,8 @@ constexpr int kMaxBT = 16;  // B <= 256
 
 static const KernelInfo kGuValuRow[kValuMaxBatch] = DFK_B_TABLE(gu_valu_row);
 static const KernelInfo kGuValuCol[kValuMaxBatch] = DFK_B_TABLE(gu_valu_col);
+static const KernelInfo kGuValuRowNorm[kValuMaxBatch] = DFK_B_TABLE(gu_valu_row_norm);
+static const KernelInfo kGuValuColNorm[kValuMaxBatch] = DFK_B_TABLE(gu_valu_col_norm);
 static const KernelInfo kDnValuRow[kValuMaxBatch] = DFK_B_TABLE(dn_valu_row);
 static const KernelInfo kDnValuRowLds[kValuMaxBatch] = DFK_B_TABLE(dn_valu_row_lds);
 static const KernelInfo kDnValuCol[kValuMaxBatch] = DFK_B_TABLE(dn_valu_col);
@@ -2106,7 +2309,8 @@ static int blocks_per_cu(const void *fn, int block, size_t lds) {
 }
 
 
-bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out) {
+bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out,
+               bool norm) {
     if (B < 1 || d_model < 8 || d_ff < 8 || (d_model % 8) || (d_ff % 8) || cus < 1) return false;
     Plan q{};
     q.op = op;
@@ -2123,10 +2327,14 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
     if (engine == ENGINE_VALU) {
         if (B > kValuMaxBatch) return false;
         if (gu) {
-            // x stays whole in LDS (+ the col combine buffer)
-            ki = row ? kGuValuRow[B - 1] : kGuValuCol[B - 1];
-            q.lds_bytes = (size_t)B * d_model * 2 + (size_t)(ki.block / kWave) * ki.nv * sizeof(float);
+            // x stays whole in LDS (+ the col combine buffer, + the norm's
+            // per-wave sums of squares)
+            if (norm) ki = row ? kGuValuRowNorm[B - 1] : kGuValuColNorm[B - 1];
+            else ki = row ? kGuValuRow[B - 1] : kGuValuCol[B - 1];
+            q.lds_bytes = (size_t)B * d_model * 2 + (size_t)(ki.block / kWave) * ki.nv * sizeof(float) +
+                          (norm ? (size_t)B * (ki.block / kWave) * sizeof(double) : 0);
             if (q.lds_bytes > kLdsLimit) return false;
+            q.fused_norm = norm;
             q.kind = row ? KIND_GU_VALU_ROW : KIND_GU_VALU_COL;
         } else {
             // keep all of h in LDS when it is small, else read it through the caches
@@ -2247,13 +2455,27 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
-                          float *h, float *partial, hipStream_t stream) {
+                          float *h, float *partial, hipStream_t stream, const NormArgs *norm) {
     GateUpArgs a;
     a.x = x; a.wg = w_gate; a.wu = w_up; a.h = h;
     a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.groups = p.groups;
+    a.gain = nullptr; a.eps = 0.0;
+    if (p.fused_norm) {
+        if (!norm || !norm->gain) return hipErrorInvalidValue;
+        a.gain = norm->gain;
+        a.eps = norm->eps;
+    }
     (void)partial;
     void *argv[] = {&a};
     return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+}
+
+hipError_t launch_rmsnorm(const uint16_t *x, const NormArgs &norm, uint16_t *xn, int B, int K, hipStream_t stream) {
+    if (B < 1 || K < 8 || (K % 8) || !norm.gain) return hipErrorInvalidValue;
+    const uint16_t *gain = norm.gain;
+    double eps = norm.eps;
+    void *argv[] = {&x, &gain, &eps, &xn, &K};
+    return hipLaunchKernel((const void *)rmsnorm_kernel, dim3(B), dim3(kNormThreads), argv, 0, stream);
 }
 
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y, float *partial,

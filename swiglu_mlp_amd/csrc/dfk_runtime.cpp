@@ -389,8 +389,10 @@ void apply_force(Variant *v) {
     else if (!std::strcmp(f, "col")) v->trav = dfk::TRAV_COL;
 }
 
-// Turn a layout argument into a runnable plan.
-dfk_status_t resolve(Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int cus, Plan *plan) {
+// Turn a layout argument into a runnable plan.  norm (gate-up): the plan
+// normalizes x itself where its kernel can (plan->fused_norm).
+dfk_status_t resolve(Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int cus, Plan *plan,
+                     bool norm = false) {
     Variant v;
     bool forced_engine = false;
     switch (layout) {
@@ -406,10 +408,10 @@ dfk_status_t resolve(Op op, dfk_layout_t layout, int B, int d_model, int d_ff, i
         case DFK_LAYOUT_COL_MFMA: v = {dfk::ENGINE_MFMA, dfk::TRAV_COL}; forced_engine = true; break;
         default: return DFK_ERR_INVALID_ARG;
     }
-    if (dfk::make_plan(op, v.engine, v.trav, B, d_model, d_ff, cus, plan)) return DFK_OK;
+    if (dfk::make_plan(op, v.engine, v.trav, B, d_model, d_ff, cus, plan, norm)) return DFK_OK;
     if (forced_engine) return DFK_ERR_UNSUPPORTED;
     // the VALU kernel cannot hold this shape: the matrix cores can
-    if (dfk::make_plan(op, dfk::ENGINE_MFMA, v.trav, B, d_model, d_ff, cus, plan)) return DFK_OK;
+    if (dfk::make_plan(op, dfk::ENGINE_MFMA, v.trav, B, d_model, d_ff, cus, plan, norm)) return DFK_OK;
     return DFK_ERR_UNSUPPORTED;
 }
 
@@ -417,11 +419,16 @@ void log_plan(const char *what, const Plan &p) {
     if (log_level() < 2) return;
     std::fprintf(stderr,
                  "[dfk] %s: %s/%s kind=%d B=%d rows=%d K=%d rows/group=%d groups=%d panels=%d grid=%d block=%d "
-                 "lds=%zu scratch=%zu%s\n",
+                 "lds=%zu scratch=%zu%s%s\n",
                  what, p.engine == dfk::ENGINE_VALU ? "valu" : "mfma", p.trav == dfk::TRAV_ROW ? "row" : "col",
                  (int)p.kind, p.B, p.rows, p.K, p.rows_per_group, p.groups, p.splits, p.grid, p.block, p.lds_bytes,
-                 p.partial_floats * sizeof(float), p.h_in_lds ? " h-in-lds" : "");
+                 p.partial_floats * sizeof(float), p.h_in_lds ? " h-in-lds" : "", p.fused_norm ? " fused-norm" : "");
 }
+
+// eps of the RMS normalization: finite and not negative.
+bool valid_eps(double eps) { return eps >= 0.0 && eps <= 1.0e300; }
+
+size_t round256(size_t bytes) { return (bytes + 255) & ~size_t(255); }
 
 // Current device, or an error status.
 dfk_status_t current_device(int *dev) {
@@ -603,6 +610,115 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
         float *h = static_cast<float *>(ws);
         float *partial = partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
         if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_rmsnorm(const uint16_t *x, const uint16_t *gain, double eps, uint16_t *xn, int B, int d_model,
+                         hipStream_t stream) {
+    try {
+        if (!x || !gain || !xn || !valid_eps(eps)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, 8);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(gain) || !aligned16(xn)) return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        const dfk::NormArgs norm{gain, eps};
+        if (dfk::launch_rmsnorm(x, norm, xn, B, d_model, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_rmsnorm_gate_up_silu_mul(const uint16_t *x, const uint16_t *gain, double eps,
+                                          const uint16_t *W_gate, const uint16_t *W_up, float *h, int B,
+                                          int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!x || !gain || !W_gate || !W_up || !h || !valid_layout(layout) || !valid_eps(eps))
+            return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(gain) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h))
+            return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan p;
+        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, device_cus(dev), &p, true)) != DFK_OK)
+            return st;
+        log_plan("rmsnorm_gate_up", p);
+        const dfk::NormArgs norm{gain, eps};
+        // workspace: the normalized x when the kernel cannot normalize it
+        // itself, then the panel partials
+        const size_t xn_bytes = p.fused_norm ? 0 : round256((size_t)B * d_model * 2);
+        const size_t bytes = xn_bytes + p.partial_floats * sizeof(float);
+        char *ws = nullptr;
+        Slot *slot = nullptr;
+        std::unique_lock<std::mutex> lock;
+        if (bytes) {
+            slot = slot_for(dev, stream);
+            lock = std::unique_lock<std::mutex>(slot->mu);
+            void *w = nullptr;
+            if ((st = ensure_workspace(slot, bytes, &w)) != DFK_OK) return st;
+            ws = static_cast<char *>(w);
+        }
+        float *partial = p.partial_floats ? reinterpret_cast<float *>(ws + xn_bytes) : nullptr;
+        if (p.fused_norm) {
+            if (dfk::launch_gate_up(p, x, W_gate, W_up, h, partial, stream, &norm) != hipSuccess) return DFK_ERR_HIP;
+        } else {
+            uint16_t *xn = reinterpret_cast<uint16_t *>(ws);
+            if (dfk::launch_rmsnorm(x, norm, xn, B, d_model, stream) != hipSuccess) return DFK_ERR_HIP;
+            if (dfk::launch_gate_up(p, xn, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        }
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, double eps, const uint16_t *W_gate,
+                                    const uint16_t *W_up, const uint16_t *W_down, uint16_t *out, int B,
+                                    int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!x || !gain || !W_gate || !W_up || !W_down || !out || !valid_layout(layout) || !valid_eps(eps))
+            return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(gain) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+            !aligned16(out))
+            return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        const int cus = device_cus(dev);
+        Plan pg, pd;
+        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, cus, &pg, true)) != DFK_OK) return st;
+        if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
+        log_plan("rmsnorm_gate_up", pg);
+        log_plan("down", pd);
+        const dfk::NormArgs norm{gain, eps};
+        Slot *slot = slot_for(dev, stream);
+        std::lock_guard<std::mutex> lock(slot->mu);
+        // workspace: h, the normalized x (when gate-up cannot normalize it
+        // itself), then the panel partials shared by the two kernels
+        const size_t h_bytes = round256((size_t)B * d_ff * sizeof(float));
+        const size_t xn_bytes = pg.fused_norm ? 0 : round256((size_t)B * d_model * 2);
+        const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
+        void *w = nullptr;
+        if ((st = ensure_workspace(slot, h_bytes + xn_bytes + partial_floats * sizeof(float), &w)) != DFK_OK)
+            return st;
+        char *ws = static_cast<char *>(w);
+        float *h = reinterpret_cast<float *>(ws);
+        float *partial = partial_floats ? reinterpret_cast<float *>(ws + h_bytes + xn_bytes) : nullptr;
+        if (pg.fused_norm) {
+            if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream, &norm) != hipSuccess) return DFK_ERR_HIP;
+        } else {
+            uint16_t *xn = reinterpret_cast<uint16_t *>(ws + h_bytes);
+            if (dfk::launch_rmsnorm(x, norm, xn, B, d_model, stream) != hipSuccess) return DFK_ERR_HIP;
+            if (dfk::launch_gate_up(pg, xn, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        }
         if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {

@@ -16,6 +16,7 @@ layer shapes, no trained weights are used):
     1001..1003, x 1100+B; 8B 32-layer stack weights 3000+4l+{1,2,3}, x0 3000;
     Llama-3-70B layer weights 4001..4003, x 4100+B; shape sweep entry s weights
     5000+100s+{1,2,3}, x 5000+100s+10+B.
+  * RMS-normalization gains: 1 + N(0, 0.1^2) per column (``norm_gain``).
 """
 from __future__ import annotations
 
@@ -150,6 +151,14 @@ def integer_layer(B: int, d_model: int, d_ff: int, seed: int, lo: int = -2, hi: 
         w_up=rand_int_bf16((d_ff, d_model), lo, hi, seed + 2),
         w_down=rand_int_bf16((d_model, d_ff), lo, hi, seed + 3),
     )
+
+
+def norm_gain(d_model: int, seed: int, std: float = 0.1) -> np.ndarray:
+    """RMS-normalization gain [d_model] as bf16 bits: 1 + N(0, std^2) (a trained
+    gain's spread around its initial value of one)."""
+    g = torch.Generator().manual_seed(int(seed))
+    t = torch.randn(d_model, generator=g, dtype=torch.float32).mul_(std).add_(1.0)
+    return to_bf16_bits(t)
 
 
 def integer_h(B: int, d_ff: int, seed: int, bound: int = 256) -> np.ndarray:

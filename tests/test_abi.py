@@ -69,10 +69,23 @@ def mlp(L, x=A, wg=A, wu=A, wd=A, out=A, B=1, dm=256, dff=688, layout=0):
     return L.dfk_swiglu_mlp(x, wg, wu, wd, out, B, dm, dff, layout, None)
 
 
-@pytest.mark.parametrize("fn", [gate_up, down, mlp], ids=["gate_up", "down", "mlp"])
+def norm_gate_up(L, x=A, gain=A, eps=1e-5, wg=A, wu=A, h=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_rmsnorm_gate_up_silu_mul(x, gain, eps, wg, wu, h, B, dm, dff, layout, None)
+
+
+def norm_mlp(L, x=A, gain=A, eps=1e-5, wg=A, wu=A, wd=A, out=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_rmsnorm_swiglu_mlp(x, gain, eps, wg, wu, wd, out, B, dm, dff, layout, None)
+
+
+def rmsnorm(L, x=A, gain=A, eps=1e-5, out=A, B=1, dm=256):
+    return L.dfk_rmsnorm(x, gain, eps, out, B, dm, None)
+
+
+@pytest.mark.parametrize("fn", [gate_up, down, mlp, norm_gate_up, norm_mlp],
+                         ids=["gate_up", "down", "mlp", "norm_gate_up", "norm_mlp"])
 def test_invalid_arguments(L, fn):
     import inspect
-    ptrs = [p for p in inspect.signature(fn).parameters if p in ("x", "wg", "wu", "wd", "h", "out")]
+    ptrs = [p for p in inspect.signature(fn).parameters if p in ("x", "gain", "wg", "wu", "wd", "h", "out")]
     for p in ptrs:
         assert fn(L, **{p: NULL}) == Status.INVALID_ARG, p
         assert fn(L, **{p: MIS}) == Status.MISALIGNED, p
@@ -88,6 +101,22 @@ def test_invalid_arguments(L, fn):
     assert fn(L, layout=-1) == Status.INVALID_ARG
     # validation order: a null pointer is reported before a bad size
     assert fn(L, B=0, **{ptrs[0]: NULL}) == Status.INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", [rmsnorm, norm_gate_up, norm_mlp], ids=["rmsnorm", "norm_gate_up", "norm_mlp"])
+def test_invalid_eps(L, fn):
+    for eps in (-1e-6, float("nan"), float("inf"), -float("inf")):
+        assert fn(L, eps=eps) == Status.INVALID_ARG, eps
+
+
+def test_rmsnorm_invalid_arguments(L):
+    for p in ("x", "gain", "out"):
+        assert rmsnorm(L, **{p: NULL}) == Status.INVALID_ARG, p
+        assert rmsnorm(L, **{p: MIS}) == Status.MISALIGNED, p
+    assert rmsnorm(L, B=0) == Status.INVALID_ARG
+    assert rmsnorm(L, dm=-8) == Status.INVALID_ARG
+    assert rmsnorm(L, B=257) == Status.UNSUPPORTED
+    assert rmsnorm(L, dm=260) == Status.UNSUPPORTED
 
 
 def test_schedule_select_argument_checks(L):
