@@ -206,8 +206,36 @@ def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
         gbps = mlp_bytes(B, dm, dff) / (ms * 1e-3) / 1e9
         res[str(B)] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                        "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        if B == 1:
+            from swiglu_mlp_amd import Layout
+            ms_p = _timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % 2], out, layout=Layout.ROW_PERSISTENT),
+                          steps, warmup)
+            res[str(B)]["persistent_us"] = round(ms_p * 1e3, 2)
     del sets
     torch.cuda.empty_cache()
+    return res
+
+
+def time_persistent(sets, device, batches=(1, 2), steps=300, warmup=30):
+    """Context: the persistent MLP kernel (both row walks in one cooperative
+    launch, DFK_LAYOUT_ROW_PERSISTENT) against the scheduler's two-kernel
+    call, us per call at the 8B shape."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import Layout, inputs
+
+    R = len(sets)
+    res = {}
+    for B in batches:
+        x = inputs.randn_bf16_device((B, D_MODEL), 1.0, 6100 + B, device)
+        out = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device)
+        us = {}
+        for name, layout in (("persistent_us", Layout.ROW_PERSISTENT), ("two_kernel_us", Layout.AUTO),
+                             ("two_kernel_row_valu_us", Layout.ROW_VALU)):
+            us[name] = round(_timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % R], out, layout=layout),
+                                    steps, warmup) * 1e3, 2)
+        us["persistent_GBps"] = round(mlp_bytes(B) / (us["persistent_us"] * 1e-6) / 1e9, 1)
+        res[str(B)] = us
     return res
 
 
@@ -328,8 +356,9 @@ def main():
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
 
-    stack, shape70b, norm = None, None, None
+    stack, shape70b, norm, persistent = None, None, None, None
     if not args.no_sweep:
+        persistent = time_persistent(sets, device)
         norm = time_rmsnorm(sets, device)
         shape70b = time_70b(device)
         stack = time_stack(device)
@@ -372,6 +401,7 @@ def main():
         "per_batch_llama70b_shape": shape70b,
         "stack32_llama8b": stack,
         "rmsnorm_mlp_llama8b": norm,
+        "persistent_mlp_llama8b": persistent,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets)

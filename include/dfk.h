@@ -47,28 +47,6 @@ extern "C" {
 #endif
 
 /*
- * Weight-traversal variant of a kernel.  Every variant computes the same
- * mathematics over the same (row-major) storage; they differ only in how the
- * weight matrix is walked, hence only in fp32 summation order.
- *
- *   ROW  row-major traversal: one wavefront owns each output row's whole dot
- *        product (all of K): the vector kernels put the 64 lanes along K and
- *        reduce across them; the matrix-core kernels give a wavefront a
- *        16-row tile.
- *   COL  column-major traversal: a workgroup owns a group of rows and its
- *        wavefronts split the columns (K) of those rows into slices; the
- *        slices' sums are added in a fixed order through LDS.  More
- *        wavefronts per row than ROW, for shapes with few or long rows.
- * Both are run-to-run deterministic (no float atomics).
- *
- * The engine under a traversal is the vector ALU (bf16 dot2 / fp32 FMA, batch
- * below 16) or the matrix cores (MFMA bf16 -> fp32, batch 16 and up, or where
- * the VALU kernel's LDS staging does not fit).  AUTO asks the scheduler
- * (dfk_schedule_select).  ROW and COL pick the engine by that batch rule; the
- * *_VALU / *_MFMA values force an engine (DFK_ERR_UNSUPPORTED where that
- * engine cannot run the shape).
- */
-/*
  * Weight-traversal variant ("Deep Kernel Fusion for Transformer Decoding",
  * episode summary: row-major and column-major kernel variants).  Weights are
  * always stored row-major ([out, in], as nn.Linear keeps them); the layout
@@ -78,11 +56,24 @@ extern "C" {
  *   AUTO       the scheduler's choice for the shape (dfk_schedule_select)
  *   ROW, COL   that traversal; the engine is VALU below 16 batch rows, else
  *              the matrix cores (and the matrix cores when VALU cannot hold
- *              the shape)
+ *              the shape).  Every variant computes the same mathematics over
+ *              the same storage and differs only in fp32 summation order;
+ *              all are run-to-run deterministic (no float atomics).
  *   *_VALU     that traversal on the vector ALUs (bf16 dot2 / fp32 FMA),
  *              B <= 8; DFK_ERR_UNSUPPORTED beyond what the engine holds
  *   *_MFMA     that traversal on the matrix cores (bf16 MFMA, fp32
  *              accumulation), any B <= 256
+ *   ROW_PERSISTENT  dfk_swiglu_mlp only: both kernels' vector-ALU row walks
+ *              in ONE cooperative launch with a grid-wide barrier between
+ *              them (no launch gap; W_down starts streaming while the last
+ *              gate-up rows finish; "FlashFormer: Whole-Model Kernels for
+ *              Efficient Low-Batch Inference", abstract: launch overhead and
+ *              bandwidth dominate at low batch).  B <= 4 and B * d_ff * 4 <= 128 KiB (h
+ *              is staged in LDS), not on a stream being captured into a
+ *              graph; DFK_ERR_UNSUPPORTED otherwise, and from the other entry
+ *              points.  Launches on one stream share a small barrier state;
+ *              a barrier that cannot complete (its workgroups not all
+ *              resident) gives up after a bounded wait and writes NaN to out.
  */
 typedef enum {
     DFK_LAYOUT_AUTO = 0,
@@ -91,7 +82,8 @@ typedef enum {
     DFK_LAYOUT_ROW_VALU = 3,
     DFK_LAYOUT_COL_VALU = 4,
     DFK_LAYOUT_ROW_MFMA = 5,
-    DFK_LAYOUT_COL_MFMA = 6
+    DFK_LAYOUT_COL_MFMA = 6,
+    DFK_LAYOUT_ROW_PERSISTENT = 7
 } dfk_layout_t;
 
 typedef enum {

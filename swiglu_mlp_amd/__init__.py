@@ -37,6 +37,7 @@ class Layout(enum.IntEnum):
     COL_VALU = 4
     ROW_MFMA = 5
     COL_MFMA = 6
+    ROW_PERSISTENT = 7
 
 
 class Status(enum.IntEnum):

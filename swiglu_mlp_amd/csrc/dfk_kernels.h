@@ -88,6 +88,24 @@ hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_ga
 // xn [B][K] = the RMS normalization of x [B][K] (one workgroup per batch row).
 hipError_t launch_rmsnorm(const uint16_t *x, const NormArgs &norm, uint16_t *xn, int B, int K,
                           hipStream_t stream);
+// The persistent MLP: the VALU gate-up row walk, a grid barrier and the VALU
+// down row walk (h in LDS) in one cooperative launch, every workgroup
+// resident.  Batches up to kMlpMaxBatch, h up to kHLdsLimit bytes.
+constexpr int kMlpMaxBatch = 4;
+struct MlpPlan {
+    int B, d_model, d_ff;
+    int grid, block;
+    size_t lds_bytes;
+    int gu_groups, dn_groups;  // row groups of the two walks
+    const void *fn;
+};
+bool make_mlp_plan(int B, int d_model, int d_ff, int cus, MlpPlan *plan);
+// The barrier's state: kBarrierWords unsigned words, zero before the first
+// launch; each launch leaves its counters at zero again.  One state per
+// stream: launches that may run concurrently must not share it.
+constexpr int kBarrierWords = (16 + 1 + 16) * 32;
+hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
+                      const uint16_t *w_down, float *h, uint16_t *y, unsigned *barrier, hipStream_t stream);
 // `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y,
                        float *partial, hipStream_t stream);

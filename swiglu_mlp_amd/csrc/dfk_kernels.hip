@@ -264,6 +264,28 @@ __device__ __forceinline__ void stage_lds(T *dst, const T *src, int n) {
     __syncthreads();
 }
 
+// stage_lds for data other workgroups of the same launch wrote with
+// device-coherent stores: device-coherent 8-byte loads (they bypass the
+// caches that are not coherent across the chip's dies), kValuBlock threads.
+__device__ __forceinline__ void stage_lds_coherent(f32x4_t *dst, const f32x4_t *src, int n) {
+    constexpr int kBatch = 8;
+    constexpr int step = kValuBlock;
+    unsigned long long *s = reinterpret_cast<unsigned long long *>(const_cast<f32x4_t *>(src));
+    unsigned long long *d = reinterpret_cast<unsigned long long *>(dst);
+    const int n2 = 2 * n;
+    for (int base = threadIdx.x; base < n2; base += kBatch * step) {
+        unsigned long long v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (base + q * step < n2)
+                v[q] = __hip_atomic_load(s + base + q * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (base + q * step < n2) d[base + q * step] = v[q];
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------- RMS normalization ----
 //
 // xn[b,k] = bf16_RNE((x[b,k] * inv_b) * gain[k]), inv_b = 1 / sqrt(mean_k
@@ -450,13 +472,14 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t *x
 // unconditional (addresses clamped into the row, the lanes past its end
 // masked at use) and the last one or two groups are peeled, so every wait in
 // the loop is for the oldest loads only.
-template <int B, int R, int U, bool NORM>
-__global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs a) {
-    extern __shared__ u32x4_t xs[];  // [B][C] (NORM: then B * waves doubles)
+// The body, shared with the persistent MLP kernel: xs is the workgroup's LDS,
+// [B][C] chunks (NORM: then B * 8 doubles); wave_id (wave-uniform) and
+// total_waves place the wave in the persistent walk.
+// COH: h is stored device-coherent, for readers in other workgroups of the
+// same launch.
+template <int B, int R, int U, bool NORM, bool COH = false>
+__device__ __forceinline__ void gate_up_row_body(const GateUpArgs &a, u32x4_t *xs, int wave_id, int total_waves) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int waves = blockDim.x / kWave;
-    const int total_waves = gridDim.x * waves;
-    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
     constexpr int G = kWave * U;                     // chunks per load group
     const int gpr = (a.C + G - 1) / G;               // load groups per row group
     const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
@@ -513,7 +536,14 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs
                 const int n = gi * R + r;
                 if (n < a.N)
 #pragma unroll
-                    for (int b = 0; b < B; ++b) a.h[(size_t)b * a.N + n] = silu_mul(ag[r][b], au[r][b]);
+                    for (int b = 0; b < B; ++b) {
+                        const float v = silu_mul(ag[r][b], au[r][b]);
+                        if constexpr (COH)
+                            __hip_atomic_store(a.h + (size_t)b * a.N + n, v, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            a.h[(size_t)b * a.N + n] = v;
+                    }
             }
         }
 #pragma unroll
@@ -585,15 +615,27 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs
     }
 }
 
+template <int B, int R, int U, bool NORM>
+__global__ __launch_bounds__(kValuBlock) void gate_up_valu_row_kernel(GateUpArgs a) {
+    extern __shared__ u32x4_t xs[];
+    constexpr int waves = kValuBlock / kWave;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    gate_up_row_body<B, R, U, NORM>(a, xs, wave_id, gridDim.x * waves);
+}
+
 // (same flattened, double-buffered walk as the gate-up row kernel; without h
 // in LDS a load group also carries its h values, issued before its weights)
-template <int B, int R, int U, bool HLDS>
-__global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
-    extern __shared__ f32x4_t hs[];  // HLDS: [B][2C]
+//
+// The body, shared with the persistent MLP kernel: hs is the workgroup's LDS
+// (HLDS: [B][2C]).  before_stage() runs after the first weight loads are
+// issued and before h is read (the persistent kernel's grid barrier); with
+// poison set every output is NaN (a barrier that timed out).
+// COH (with HLDS): h, written in this launch, is staged with device-coherent
+// loads.
+template <int B, int R, int U, bool HLDS, bool COH, class Hook>
+__device__ __forceinline__ void down_row_body(const DownArgs &a, f32x4_t *hs, int wave_id, int total_waves,
+                                              Hook before_stage) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int waves = blockDim.x / kWave;
-    const int total_waves = gridDim.x * waves;
-    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
     const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
     constexpr int G = kWave * U;
     constexpr int HU = HLDS ? 1 : U;  // h registers per group (none used with h in LDS)
@@ -601,6 +643,7 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
     const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
     const int total = rows * gpr;
     const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool poison = false;
     float acc[R][B];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -679,7 +722,8 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
                 const int m = gi * R + r;
                 if (m < a.M)
 #pragma unroll
-                    for (int b = 0; b < B; ++b) a.y[(size_t)b * a.M + m] = to_bf16_rne(acc[r][b]);
+                    for (int b = 0; b < B; ++b)
+                        a.y[(size_t)b * a.M + m] = to_bf16_rne(poison ? __builtin_nanf("") : acc[r][b]);
             }
         }
 #pragma unroll
@@ -701,10 +745,13 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
     f32x4_t h0[HU][B][2], h1[HU][B][2];
     int k0 = 0, j0 = 0;
     // the first loads go out before h is staged (a wave without work loads a
-    // clamped row and leaves after the barrier)
+    // clamped row and leaves after the barrier); h must not be read before
+    // before_stage() (h registers come with the weights only without HLDS)
     load(w0, h0, k0, j0);
     __builtin_amdgcn_sched_barrier(0);
-    if (HLDS) stage_lds(hs, hg, B * 2 * a.C);
+    poison = before_stage();
+    if constexpr (HLDS && COH) stage_lds_coherent(hs, hg, B * 2 * a.C);
+    else if constexpr (HLDS) stage_lds(hs, hg, B * 2 * a.C);
     if (wave_id >= a.groups) return;
     int t = 0;
     for (; t + 2 < total; t += 2) {
@@ -731,6 +778,114 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
     } else {
         step(w0, h0, k0, j0);
     }
+}
+
+template <int B, int R, int U, bool HLDS>
+__global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
+    extern __shared__ f32x4_t hs[];
+    constexpr int waves = kValuBlock / kWave;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    down_row_body<B, R, U, HLDS, false>(a, hs, wave_id, gridDim.x * waves, [] { return false; });
+}
+
+// ============================================ persistent MLP (row, VALU) =====
+//
+// Both kernels of the MLP in one cooperative launch (every workgroup
+// resident): the gate-up row walk, then a grid-wide barrier, then the down row
+// walk, so that no launch gap separates them and W_down starts streaming
+// while the slowest gate-up waves finish.  Each wave issues its first W_down
+// load group before the barrier (the weights do not depend on h); h is staged
+// into LDS (where x was) after it.  Barrier state: two words, zero before the
+// first launch and left zero-count after each (the last workgroup to arrive
+// resets the count and advances the generation the others wait on).
+
+// Barrier state (kBarrierWords words, zero before the first launch): 16 group
+// counters, a top counter and 16 copies of the generation, each in its own
+// 128-byte line.  Workgroup w arrives on group counter w % 16; the last of a
+// group to arrive bumps the top counter; the last group resets the counters
+// and advances every copy of the generation; workgroup w waits on copy w % 16.
+// Spreading the arrivals keeps the same-address atomics, which the memory
+// system serializes, to a few dozen per address.
+struct GridBarrier {
+    unsigned *words;
+};
+constexpr int kBarrierGroups = 16;
+constexpr int kBarrierLine = 32;  // words per 128-byte line
+__device__ __forceinline__ unsigned *bar_group(const GridBarrier &g, int i) { return g.words + i * kBarrierLine; }
+__device__ __forceinline__ unsigned *bar_top(const GridBarrier &g) { return g.words + kBarrierGroups * kBarrierLine; }
+__device__ __forceinline__ unsigned *bar_gen(const GridBarrier &g, int i) {
+    return g.words + (kBarrierGroups + 1 + i) * kBarrierLine;
+}
+
+// Upper bound on the spin of a waiting workgroup (each turn sleeps ~128
+// cycles plus a memory round trip): far beyond any launch's skew, it only
+// keeps a launch whose workgroups are not all resident from hanging.
+constexpr unsigned kBarrierSpins = 1u << 20;
+
+// The protocol uses no cache-maintenance fences: a device-scope release or
+// acquire writes back or invalidates a whole L2 per die, far too slow here.
+// Instead h travels device-coherent: written with coherent stores that each
+// wave waits to complete before its workgroup arrives, and read (after the
+// generation moves) with coherent loads.
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): this wave's stores are
+// complete.
+__device__ __forceinline__ void wait_stores_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The launch's generation as workgroup w sees it, read at the kernel's start:
+// it moves only when every workgroup of this launch has arrived.
+__device__ __forceinline__ unsigned grid_generation(const GridBarrier &g) {
+    return __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(bar_gen(g, blockIdx.x % kBarrierGroups), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Arrive and wait (whole workgroup, after every wave's coherent h stores
+// completed).  Returns true (every thread) when the wait gave up.
+__device__ bool grid_sync(const GridBarrier &g, unsigned gen) {
+    __shared__ int timed_out;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nb = gridDim.x, grp = blockIdx.x % kBarrierGroups;
+        const int groups = min(nb, kBarrierGroups);
+        const unsigned in_group = (unsigned)((nb - grp + kBarrierGroups - 1) / kBarrierGroups);
+        const unsigned a = __hip_atomic_fetch_add(bar_group(g, grp), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (a == in_group - 1) {
+            __hip_atomic_store(bar_group(g, grp), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned b = __hip_atomic_fetch_add(bar_top(g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (b == (unsigned)groups - 1) {
+                __hip_atomic_store(bar_top(g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wait_stores_done();
+                for (int i = 0; i < kBarrierGroups; ++i)
+                    __hip_atomic_fetch_add(bar_gen(g, i), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        int bad = 0;
+        unsigned spins = 0;
+        while (__hip_atomic_load(bar_gen(g, grp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kBarrierSpins) {
+                bad = 1;
+                break;
+            }
+        }
+        timed_out = bad;
+    }
+    __syncthreads();
+    return timed_out != 0;
+}
+
+template <int B, int RG, int UG, int RD, int UD>
+__global__ __launch_bounds__(kValuBlock) void mlp_valu_row_persistent_kernel(GateUpArgs ga, DownArgs da,
+                                                                              GridBarrier bar) {
+    extern __shared__ u32x4_t smem[];  // x [B][d_model / 8], later h [B][2 d_ff / 8]
+    constexpr int waves = kValuBlock / kWave;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    const int total_waves = gridDim.x * waves;
+    const unsigned gen = grid_generation(bar);
+    gate_up_row_body<B, RG, UG, false, true>(ga, smem, wave_id, total_waves);
+    wait_stores_done();  // this wave's coherent h stores are complete before its workgroup arrives
+    down_row_body<B, RD, UD, true, true>(da, reinterpret_cast<f32x4_t *>(smem), wave_id, total_waves,
+                                         [&] { return grid_sync(bar, gen); });
 }
 
 // ==================================================== VALU col kernels =====
@@ -2290,6 +2445,25 @@ static const KernelInfo kGuStaged8[kStMaxBT] = DFK_B_TABLE(gu_staged8);
 static const KernelInfo kDnStaged4[kStMaxBT] = DFK_B_TABLE(dn_staged4);
 static const KernelInfo kDnStaged8[kStMaxBT] = DFK_B_TABLE(dn_staged8);
 
+// The persistent MLP kernel per batch: its gate-up and down row counts per
+// work item.
+#ifndef DFK_MLP_DN_R
+#define DFK_MLP_DN_R(B) DFK_DN_VALU_R(B)
+#endif
+#ifndef DFK_MLP_DN_U
+#define DFK_MLP_DN_U(B) DFK_DN_VALU_U(B)
+#endif
+struct MlpKernel {
+    const void *fn;
+    int rg, rd;
+};
+template <int B> MlpKernel mlp_persistent() {
+    constexpr int RG = DFK_GU_VALU_R(B), UG = DFK_GU_VALU_U(B), RD = DFK_MLP_DN_R(B), UD = DFK_MLP_DN_U(B);
+    return {(const void *)mlp_valu_row_persistent_kernel<B, RG, UG, RD, UD>, RG, RD};
+}
+static const MlpKernel kMlpPersistent[kMlpMaxBatch] = {mlp_persistent<1>(), mlp_persistent<2>(),
+                                                       mlp_persistent<3>(), mlp_persistent<4>()};
+
 // Blocks of a kernel that fit on one CU (cached per kernel, block and LDS).
 static int blocks_per_cu(const void *fn, int block, size_t lds) {
     static std::mutex mu;
@@ -2452,6 +2626,42 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
     q.fn = ki.fn;
     *out = q;
     return true;
+}
+
+bool make_mlp_plan(int B, int d_model, int d_ff, int cus, MlpPlan *out) {
+    if (B < 1 || B > kMlpMaxBatch || d_model < 8 || d_ff < 8 || (d_model % 8) || (d_ff % 8) || cus < 1) return false;
+    const size_t x_bytes = (size_t)B * d_model * 2, h_bytes = (size_t)B * d_ff * 4;
+    if (h_bytes > kHLdsLimit || x_bytes > kLdsLimit) return false;
+    const MlpKernel &mk = kMlpPersistent[B - 1];
+    MlpPlan q{};
+    q.B = B;
+    q.d_model = d_model;
+    q.d_ff = d_ff;
+    q.fn = mk.fn;
+    q.block = kValuBlock;
+    q.lds_bytes = std::max(x_bytes, h_bytes);
+    q.gu_groups = (int)ceil_div(d_ff, mk.rg);
+    q.dn_groups = (int)ceil_div(d_model, mk.rd);
+    // every workgroup resident (a cooperative launch), no more than the work
+    const long slots = (long)cus * blocks_per_cu(q.fn, q.block, q.lds_bytes);
+    const long need = ceil_div(std::max(q.gu_groups, q.dn_groups), kValuBlock / kWave);
+    q.grid = (int)std::max(1L, std::min(slots, need));
+    *out = q;
+    return true;
+}
+
+hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
+                      const uint16_t *w_down, float *h, uint16_t *y, unsigned *barrier, hipStream_t stream) {
+    if (!barrier) return hipErrorInvalidValue;
+    GateUpArgs ga{};
+    ga.x = x; ga.wg = w_gate; ga.wu = w_up; ga.h = h;
+    ga.B = p.B; ga.K = p.d_model; ga.N = p.d_ff; ga.C = p.d_model / 8; ga.groups = p.gu_groups;
+    DownArgs da{};
+    da.h = h; da.wd = w_down; da.y = y;
+    da.B = p.B; da.K = p.d_ff; da.M = p.d_model; da.C = p.d_ff / 8; da.groups = p.dn_groups;
+    GridBarrier bar{barrier};
+    void *argv[] = {&ga, &da, &bar};
+    return hipLaunchCooperativeKernel(p.fn, dim3(p.grid), dim3(p.block), argv, (unsigned)p.lds_bytes, stream);
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,

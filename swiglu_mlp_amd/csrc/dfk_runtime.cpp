@@ -53,7 +53,7 @@ dfk_status_t check_dims(int B, int d_model, int d_ff) {
     return DFK_OK;
 }
 
-bool valid_layout(dfk_layout_t l) { return l >= DFK_LAYOUT_AUTO && l <= DFK_LAYOUT_COL_MFMA; }
+bool valid_layout(dfk_layout_t l) { return l >= DFK_LAYOUT_AUTO && l <= DFK_LAYOUT_ROW_PERSISTENT; }
 
 // ------------------------------------------------------------ devices -----
 
@@ -82,6 +82,7 @@ struct Slot {
     std::mutex mu;
     void *data = nullptr;
     size_t bytes = 0;
+    unsigned *barrier = nullptr;  // the persistent kernel's grid-barrier state
 };
 
 std::mutex g_ws_mu;
@@ -112,6 +113,34 @@ dfk_status_t ensure_workspace(Slot *slot, size_t bytes, void **out) {
     }
     *out = slot->data;
     return DFK_OK;
+}
+
+// Caller holds slot->mu.  The barrier words are cleared once, on the stream,
+// before the first persistent launch; every launch leaves them reusable.
+dfk_status_t ensure_barrier(Slot *slot, hipStream_t stream, unsigned **out) {
+    if (!slot->barrier) {
+        void *p = nullptr;
+        if (hipMalloc(&p, dfk::kBarrierWords * sizeof(unsigned)) != hipSuccess) {
+            (void)hipGetLastError();
+            return DFK_ERR_OOM;
+        }
+        if (hipMemsetAsync(p, 0, dfk::kBarrierWords * sizeof(unsigned), stream) != hipSuccess) {
+            (void)hipFree(p);
+            return DFK_ERR_HIP;
+        }
+        slot->barrier = static_cast<unsigned *>(p);
+    }
+    *out = slot->barrier;
+    return DFK_OK;
+}
+
+bool stream_capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;  // unknown: treat as capturing (no cooperative launch)
+    }
+    return st != hipStreamCaptureStatusNone;
 }
 
 // ------------------------------------------------------------ tiny JSON ---
@@ -406,6 +435,7 @@ dfk_status_t resolve(Op op, dfk_layout_t layout, int B, int d_model, int d_ff, i
         case DFK_LAYOUT_COL_VALU: v = {dfk::ENGINE_VALU, dfk::TRAV_COL}; forced_engine = true; break;
         case DFK_LAYOUT_ROW_MFMA: v = {dfk::ENGINE_MFMA, dfk::TRAV_ROW}; forced_engine = true; break;
         case DFK_LAYOUT_COL_MFMA: v = {dfk::ENGINE_MFMA, dfk::TRAV_COL}; forced_engine = true; break;
+        case DFK_LAYOUT_ROW_PERSISTENT: return DFK_ERR_UNSUPPORTED;  // whole-MLP calls only
         default: return DFK_ERR_INVALID_ARG;
     }
     if (dfk::make_plan(op, v.engine, v.trav, B, d_model, d_ff, cus, plan, norm)) return DFK_OK;
@@ -466,6 +496,7 @@ const char *dfk_layout_name(dfk_layout_t l) {
         case DFK_LAYOUT_COL_VALU: return "col_valu";
         case DFK_LAYOUT_ROW_MFMA: return "row_mfma";
         case DFK_LAYOUT_COL_MFMA: return "col_mfma";
+        case DFK_LAYOUT_ROW_PERSISTENT: return "row_persistent";
     }
     return "invalid";
 }
@@ -595,6 +626,27 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
         int dev;
         if ((st = current_device(&dev)) != DFK_OK) return st;
         const int cus = device_cus(dev);
+        if (layout == DFK_LAYOUT_ROW_PERSISTENT) {
+            dfk::MlpPlan mp;
+            if (!dfk::make_mlp_plan(B, d_model, d_ff, cus, &mp)) return DFK_ERR_UNSUPPORTED;
+            // a cooperative launch is not captured into graphs here
+            if (stream_capturing(stream)) return DFK_ERR_UNSUPPORTED;
+            if (log_level() >= 2)
+                std::fprintf(stderr, "[dfk] mlp persistent: B=%d grid=%d lds=%zu groups=%d/%d\n", B, mp.grid,
+                             mp.lds_bytes, mp.gu_groups, mp.dn_groups);
+            Slot *slot = slot_for(dev, stream);
+            std::lock_guard<std::mutex> lock(slot->mu);
+            void *ws = nullptr;
+            unsigned *barrier = nullptr;
+            if ((st = ensure_workspace(slot, (size_t)B * d_ff * sizeof(float), &ws)) != DFK_OK) return st;
+            if ((st = ensure_barrier(slot, stream, &barrier)) != DFK_OK) return st;
+            if (dfk::launch_mlp(mp, x, W_gate, W_up, W_down, static_cast<float *>(ws), out, barrier, stream) !=
+                hipSuccess) {
+                (void)hipGetLastError();
+                return DFK_ERR_HIP;
+            }
+            return DFK_OK;
+        }
         Plan pg, pd;
         if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, cus, &pg)) != DFK_OK) return st;
         if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
@@ -741,8 +793,10 @@ dfk_status_t dfk_release_workspace(void) {
             {
                 std::lock_guard<std::mutex> l2(it->second->mu);
                 if (it->second->data && hipFree(it->second->data) != hipSuccess) st = DFK_ERR_HIP;
+                if (it->second->barrier && hipFree(it->second->barrier) != hipSuccess) st = DFK_ERR_HIP;
                 it->second->data = nullptr;
                 it->second->bytes = 0;
+                it->second->barrier = nullptr;
             }
             it = g_ws.erase(it);
         }

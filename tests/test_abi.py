@@ -49,7 +49,7 @@ def test_strings(L):
         assert text.startswith("DFK_")
     assert dfk.status_string(99) == "DFK_ERR_UNKNOWN"
     names = [dfk.layout_name(l) for l in Layout]
-    assert names == ["auto", "row", "col", "row_valu", "col_valu", "row_mfma", "col_mfma"]
+    assert names == ["auto", "row", "col", "row_valu", "col_valu", "row_mfma", "col_mfma", "row_persistent"]
     assert dfk.layout_name(42) == "invalid"
     assert "gfx950" in dfk.version()
 
@@ -97,7 +97,7 @@ def test_invalid_arguments(L, fn):
     assert fn(L, dm=260) == Status.UNSUPPORTED
     assert fn(L, dff=690) == Status.UNSUPPORTED
     assert fn(L, dm=65536, dff=32768) == Status.UNSUPPORTED  # d_model*d_ff >= 2^31
-    assert fn(L, layout=7) == Status.INVALID_ARG
+    assert fn(L, layout=8) == Status.INVALID_ARG
     assert fn(L, layout=-1) == Status.INVALID_ARG
     # validation order: a null pointer is reported before a bad size
     assert fn(L, B=0, **{ptrs[0]: NULL}) == Status.INVALID_ARG
