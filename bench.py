@@ -239,6 +239,31 @@ def time_persistent(sets, device, batches=(1, 2), steps=300, warmup=30):
     return res
 
 
+def time_packed(sets, device, batches=(1, 4, 8), steps=200, warmup=20):
+    """Context: the MLP with W_gate and W_up packed in one tensor (blocked and
+    row-interleaved) against separate tensors, us per call at the 8B shape
+    (scheduler's variants)."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import Packing, inputs
+
+    R = len(sets)
+    packed = {p: [dfk.pack_gate_up(s[0], s[1], p) for s in sets] for p in Packing}
+    res = {}
+    for B in batches:
+        x = inputs.randn_bf16_device((B, D_MODEL), 1.0, 6100 + B, device)
+        out = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device)
+        r = {"separate_us": round(_timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % R], out), steps, warmup) * 1e3, 2)}
+        for p in Packing:
+            r[p.name.lower() + "_us"] = round(_timed(
+                lambda i: dfk.dfk_swiglu_mlp_packed(x, packed[p][i % R], sets[i % R][2], p, out), steps,
+                warmup) * 1e3, 2)
+        res[str(B)] = r
+    del packed
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_rmsnorm(sets, device, batches=(1, 4, 8, 16), steps=200, warmup=20):
     """Context: the MLP on RMS-normalized input at the 8B layer shape, us per
     call: the fused entry point (norm inside gate-up where the kernel stages
@@ -356,8 +381,9 @@ def main():
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
 
-    stack, shape70b, norm, persistent = None, None, None, None
+    stack, shape70b, norm, persistent, packed = None, None, None, None, None
     if not args.no_sweep:
+        packed = time_packed(sets, device)
         persistent = time_persistent(sets, device)
         norm = time_rmsnorm(sets, device)
         shape70b = time_70b(device)
@@ -402,6 +428,7 @@ def main():
         "stack32_llama8b": stack,
         "rmsnorm_mlp_llama8b": norm,
         "persistent_mlp_llama8b": persistent,
+        "packed_gate_up_llama8b": packed,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets)

@@ -136,6 +136,37 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
                             int d_ff, dfk_layout_t layout, hipStream_t stream);
 
 /*
+ * How W_gate and W_up share one packed weight tensor W_gu [2 * d_ff, d_model]
+ * ("Optimizing QKV Projection with Operator Fusion", "Implementing Fusion:
+ * Packed Projections": projections packed into one weight read through one
+ * base pointer, the same principle carried over to SwiGLU's gate and up).
+ *   BLOCKED      rows [0, d_ff) are W_gate, rows [d_ff, 2 d_ff) are W_up
+ *   INTERLEAVED  row 2n is W_gate's row n, row 2n + 1 is W_up's row n, so a
+ *                neuron's gate and up weights are one contiguous 4 * d_model
+ *                byte stream
+ */
+typedef enum { DFK_PACK_BLOCKED = 0, DFK_PACK_INTERLEAVED = 1 } dfk_packing_t;
+
+/*
+ * dfk_gate_up_silu_mul with W_gate and W_up packed in W_gu (device, bf16,
+ * [2 * d_ff, d_model], layout per `packing`).  Same kernels, same results bit
+ * for bit as passing the two halves separately; only the weights' addresses
+ * differ.  A bad `packing` value is DFK_ERR_INVALID_ARG.
+ */
+dfk_status_t dfk_gate_up_silu_mul_packed(const uint16_t *x, const uint16_t *W_gu, float *h, int B,
+                                         int d_model, int d_ff, dfk_packing_t packing,
+                                         dfk_layout_t layout, hipStream_t stream);
+
+/*
+ * dfk_swiglu_mlp with W_gate and W_up packed in W_gu (as above); W_down is
+ * separate.  DFK_LAYOUT_ROW_PERSISTENT takes the blocked packing only
+ * (DFK_ERR_UNSUPPORTED for the interleaved one).
+ */
+dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, const uint16_t *W_down,
+                                   uint16_t *out, int B, int d_model, int d_ff,
+                                   dfk_packing_t packing, dfk_layout_t layout, hipStream_t stream);
+
+/*
  * RMS normalization of the MLP input (GPULlama3.java pull request "[FP16] ...
  * fusing dequantize with compute", commit list: RMS normalization fused with
  * the gate and up projections; the page does not define the normalization,

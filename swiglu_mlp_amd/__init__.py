@@ -40,6 +40,11 @@ class Layout(enum.IntEnum):
     ROW_PERSISTENT = 7
 
 
+class Packing(enum.IntEnum):
+    BLOCKED = 0
+    INTERLEAVED = 1
+
+
 class Status(enum.IntEnum):
     OK = 0
     INVALID_ARG = 1
@@ -53,7 +58,8 @@ EXPORTED = (
     "dfk_gate_up_silu_mul", "dfk_down_proj", "dfk_swiglu_mlp", "dfk_schedule_select",
     "dfk_status_string", "dfk_layout_name", "dfk_version", "dfk_load_tuning_table",
     "dfk_tuning_table_source", "dfk_release_workspace", "dfk_rmsnorm",
-    "dfk_rmsnorm_gate_up_silu_mul", "dfk_rmsnorm_swiglu_mlp",
+    "dfk_rmsnorm_gate_up_silu_mul", "dfk_rmsnorm_swiglu_mlp", "dfk_gate_up_silu_mul_packed",
+    "dfk_swiglu_mlp_packed",
 )
 
 
@@ -104,6 +110,10 @@ def lib() -> ctypes.CDLL:
     L.dfk_rmsnorm_gate_up_silu_mul.restype = i
     L.dfk_rmsnorm_swiglu_mlp.argtypes = [u16p, u16p, d, u16p, u16p, u16p, u16p, i, i, i, i, vp]
     L.dfk_rmsnorm_swiglu_mlp.restype = i
+    L.dfk_gate_up_silu_mul_packed.argtypes = [u16p, u16p, f32p, i, i, i, i, i, vp]
+    L.dfk_gate_up_silu_mul_packed.restype = i
+    L.dfk_swiglu_mlp_packed.argtypes = [u16p, u16p, u16p, u16p, i, i, i, i, i, vp]
+    L.dfk_swiglu_mlp_packed.restype = i
     _lib = L
     return L
 
@@ -196,6 +206,49 @@ def dfk_swiglu_mlp(x, W_gate, W_up, W_down, out=None, layout: int = Layout.AUTO,
                               _stream_handle(stream, x.device))
     _check(st, "dfk_swiglu_mlp")
     return out
+
+
+def dfk_gate_up_silu_mul_packed(x, W_gu, packing: int, h=None, layout: int = Layout.AUTO, stream=None):
+    """dfk_gate_up_silu_mul with W_gate and W_up packed in W_gu [2 d_ff, d_model]."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gu.shape[0] // 2
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(W_gu, "W_gu", torch.bfloat16, (2 * d_ff, d_model))
+    if h is None:
+        h = torch.empty((B, d_ff), dtype=torch.float32, device=x.device)
+    _expect(h, "h", torch.float32, (B, d_ff))
+    st = lib().dfk_gate_up_silu_mul_packed(x.data_ptr(), W_gu.data_ptr(), h.data_ptr(), B, d_model, d_ff,
+                                           int(packing), int(layout), _stream_handle(stream, x.device))
+    _check(st, "dfk_gate_up_silu_mul_packed")
+    return h
+
+
+def dfk_swiglu_mlp_packed(x, W_gu, W_down, packing: int, out=None, layout: int = Layout.AUTO, stream=None):
+    """dfk_swiglu_mlp with W_gate and W_up packed in W_gu [2 d_ff, d_model]."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gu.shape[0] // 2
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(W_gu, "W_gu", torch.bfloat16, (2 * d_ff, d_model))
+    _expect(W_down, "W_down", torch.bfloat16, (d_model, d_ff))
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=x.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_swiglu_mlp_packed(x.data_ptr(), W_gu.data_ptr(), W_down.data_ptr(), out.data_ptr(), B,
+                                     d_model, d_ff, int(packing), int(layout), _stream_handle(stream, x.device))
+    _check(st, "dfk_swiglu_mlp_packed")
+    return out
+
+
+def pack_gate_up(W_gate, W_up, packing: int):
+    """Pack two [d_ff, d_model] tensors into one [2 d_ff, d_model] (a copy)."""
+    import torch
+    if int(packing) == Packing.BLOCKED:
+        return torch.cat([W_gate, W_up], dim=0).contiguous()
+    if int(packing) == Packing.INTERLEAVED:
+        return torch.stack([W_gate, W_up], dim=1).reshape(-1, W_gate.shape[1]).contiguous()
+    raise ValueError(f"unknown packing {packing}")
 
 
 def dfk_rmsnorm(x, gain, eps: float = 1e-5, out=None, stream=None):

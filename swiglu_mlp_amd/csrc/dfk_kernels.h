@@ -82,9 +82,11 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
 
 // Enqueue the kernel of a plan on `stream`.
 // `partial` must hold p.partial_floats floats when that is non-zero.
+// `ldw`: elements from one row of W_gate (and of W_up) to the next, >= the
+// plan's K (0: K, dense); 2K for row-interleaved gate/up storage.
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate,
                           const uint16_t *w_up, float *h, float *partial, hipStream_t stream,
-                          const NormArgs *norm = nullptr);
+                          const NormArgs *norm = nullptr, int ldw = 0);
 // xn [B][K] = the RMS normalization of x [B][K] (one workgroup per batch row).
 hipError_t launch_rmsnorm(const uint16_t *x, const NormArgs &norm, uint16_t *xn, int B, int K,
                           hipStream_t stream);

@@ -136,6 +136,7 @@ struct GateUpArgs {
     int B, K, N;  // batch, d_model, d_ff
     int C;        // 16-byte chunks per weight row (K / 8)
     int groups;   // work items: row groups (ROW: per wave, COL: per workgroup)
+    int ldw;      // elements from one row of W_gate (and of W_up) to the next: K, or 2K row-interleaved
     const uint16_t *gain;  // RMS normalization (NORM kernels only): gain [d_model]
     double eps;            //   and epsilon
 };
@@ -495,8 +496,8 @@ __device__ __forceinline__ void gate_up_row_body(const GateUpArgs &a, u32x4_t *x
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = min(gi * R + r, a.N - 1);
-            const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
-            const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+            const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.ldw);
+            const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.ldw);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = min(j * G + kWave * u + lane, a.C - 1);
@@ -920,8 +921,8 @@ __global__ __launch_bounds__(kValuBlock) void gate_up_valu_col_kernel(GateUpArgs
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = min(gi * R + r, a.N - 1);
-            rg[r] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
-            ru[r] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+            rg[r] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.ldw);
+            ru[r] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.ldw);
         }
         float ag[R][B], au[R][B];
 #pragma unroll
@@ -1035,8 +1036,8 @@ __device__ __forceinline__ void gu_mfma_accumulate(const GateUpArgs &a, int row0
 #pragma unroll
     for (int t = 0; t < TR; ++t) {
         const int n = min(row0 + t * 16 + lr, a.N - 1);
-        pg[t] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.K);
-        pu[t] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.K);
+        pg[t] = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)n * a.ldw);
+        pu[t] = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)n * a.ldw);
     }
     const u32x4_t *px[BT];
     bool bvalid[BT];
@@ -1290,8 +1291,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
         if (active && kb_beg < kb_end) {
             u32x4_t vg0[L::kInsts], vu0[L::kInsts], vg1[L::kInsts], vu1[L::kInsts];
             auto load_w = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
-                L::load(vg, a.wg, a.K, a.C, row0, a.N, kb, lane);
-                L::load(vu, a.wu, a.K, a.C, row0, a.N, kb, lane);
+                L::load(vg, a.wg, a.ldw, a.C, row0, a.N, kb, lane);
+                L::load(vu, a.wu, a.ldw, a.C, row0, a.N, kb, lane);
             };
             auto step = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
                 L::store(ltg, vg, kb, a.C, lane);
@@ -1707,8 +1708,8 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
     for (int g = blockIdx.x; g < wg_items; g += gridDim.x) {
         const int tile = g * WAVES + wave;
         const int row = min(tile * 16 + lr, a.N - 1);
-        const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)row * a.K);
-        const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)row * a.K);
+        const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.wg + (size_t)row * a.ldw);
+        const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.wu + (size_t)row * a.ldw);
         f32x4_t accg[BT], accu[BT];
 #pragma unroll
         for (int bt = 0; bt < BT; ++bt) accg[bt] = accu[bt] = f32x4_t{0, 0, 0, 0};
@@ -2655,7 +2656,7 @@ hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gat
     if (!barrier) return hipErrorInvalidValue;
     GateUpArgs ga{};
     ga.x = x; ga.wg = w_gate; ga.wu = w_up; ga.h = h;
-    ga.B = p.B; ga.K = p.d_model; ga.N = p.d_ff; ga.C = p.d_model / 8; ga.groups = p.gu_groups;
+    ga.B = p.B; ga.K = p.d_model; ga.N = p.d_ff; ga.C = p.d_model / 8; ga.groups = p.gu_groups; ga.ldw = p.d_model;
     DownArgs da{};
     da.h = h; da.wd = w_down; da.y = y;
     da.B = p.B; da.K = p.d_ff; da.M = p.d_model; da.C = p.d_ff / 8; da.groups = p.dn_groups;
@@ -2665,10 +2666,12 @@ hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gat
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
-                          float *h, float *partial, hipStream_t stream, const NormArgs *norm) {
+                          float *h, float *partial, hipStream_t stream, const NormArgs *norm, int ldw) {
     GateUpArgs a;
     a.x = x; a.wg = w_gate; a.wu = w_up; a.h = h;
     a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.groups = p.groups;
+    a.ldw = ldw > 0 ? ldw : p.K;
+    if (a.ldw < p.K) return hipErrorInvalidValue;
     a.gain = nullptr; a.eps = 0.0;
     if (p.fused_norm) {
         if (!norm || !norm->gain) return hipErrorInvalidValue;

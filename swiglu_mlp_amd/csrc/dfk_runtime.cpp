@@ -469,6 +469,91 @@ dfk_status_t current_device(int *dev) {
     return DFK_OK;
 }
 
+// dfk_gate_up_silu_mul with W_gate / W_up rows `ldw` elements apart.
+dfk_status_t gate_up_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up, int ldw, float *h,
+                          int B, int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream) {
+    {
+        if (!x || !W_gate || !W_up || !h || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h)) return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan p;
+        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
+        log_plan("gate_up", p);
+        float *partial = nullptr;
+        Slot *slot = nullptr;
+        std::unique_lock<std::mutex> lock;
+        if (p.partial_floats) {
+            slot = slot_for(dev, stream);
+            lock = std::unique_lock<std::mutex>(slot->mu);
+            void *ws = nullptr;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            partial = static_cast<float *>(ws);
+        }
+        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, partial, stream, nullptr, ldw) != hipSuccess)
+            return DFK_ERR_HIP;
+        return DFK_OK;
+    }
+}
+
+// dfk_swiglu_mlp with W_gate / W_up rows `ldw` elements apart.
+dfk_status_t mlp_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up, int ldw,
+                      const uint16_t *W_down, uint16_t *out, int B, int d_model, int d_ff, dfk_layout_t layout,
+                      hipStream_t stream) {
+    {
+        if (!x || !W_gate || !W_up || !W_down || !out || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) || !aligned16(out))
+            return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        const int cus = device_cus(dev);
+        if (layout == DFK_LAYOUT_ROW_PERSISTENT) {
+            if (ldw != d_model) return DFK_ERR_UNSUPPORTED;  // dense gate / up only
+            dfk::MlpPlan mp;
+            if (!dfk::make_mlp_plan(B, d_model, d_ff, cus, &mp)) return DFK_ERR_UNSUPPORTED;
+            // a cooperative launch is not captured into graphs here
+            if (stream_capturing(stream)) return DFK_ERR_UNSUPPORTED;
+            if (log_level() >= 2)
+                std::fprintf(stderr, "[dfk] mlp persistent: B=%d grid=%d lds=%zu groups=%d/%d\n", B, mp.grid,
+                             mp.lds_bytes, mp.gu_groups, mp.dn_groups);
+            Slot *slot = slot_for(dev, stream);
+            std::lock_guard<std::mutex> lock(slot->mu);
+            void *ws = nullptr;
+            unsigned *barrier = nullptr;
+            if ((st = ensure_workspace(slot, (size_t)B * d_ff * sizeof(float), &ws)) != DFK_OK) return st;
+            if ((st = ensure_barrier(slot, stream, &barrier)) != DFK_OK) return st;
+            if (dfk::launch_mlp(mp, x, W_gate, W_up, W_down, static_cast<float *>(ws), out, barrier, stream) !=
+                hipSuccess) {
+                (void)hipGetLastError();
+                return DFK_ERR_HIP;
+            }
+            return DFK_OK;
+        }
+        Plan pg, pd;
+        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, cus, &pg)) != DFK_OK) return st;
+        if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
+        log_plan("gate_up", pg);
+        log_plan("down", pd);
+        Slot *slot = slot_for(dev, stream);
+        std::lock_guard<std::mutex> lock(slot->mu);
+        void *ws = nullptr;
+        const size_t h_bytes = ((size_t)B * d_ff * sizeof(float) + 255) & ~size_t(255);
+        // the two kernels run in stream order, so their panel partials share one region
+        const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
+        if ((st = ensure_workspace(slot, h_bytes + partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+        float *h = static_cast<float *>(ws);
+        float *partial = partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
+        if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream, nullptr, ldw) != hipSuccess)
+            return DFK_ERR_HIP;
+        if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    }
+}
+
 }  // namespace
 
 // ================================================================ C ABI ====
@@ -559,27 +644,7 @@ const char *dfk_tuning_table_source(void) {
 dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up, float *h,
                                   int B, int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream) {
     try {
-        if (!x || !W_gate || !W_up || !h || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
-        dfk_status_t st = check_dims(B, d_model, d_ff);
-        if (st != DFK_OK) return st;
-        if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h)) return DFK_ERR_MISALIGNED;
-        int dev;
-        if ((st = current_device(&dev)) != DFK_OK) return st;
-        Plan p;
-        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, device_cus(dev), &p)) != DFK_OK) return st;
-        log_plan("gate_up", p);
-        float *partial = nullptr;
-        Slot *slot = nullptr;
-        std::unique_lock<std::mutex> lock;
-        if (p.partial_floats) {
-            slot = slot_for(dev, stream);
-            lock = std::unique_lock<std::mutex>(slot->mu);
-            void *ws = nullptr;
-            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
-            partial = static_cast<float *>(ws);
-        }
-        if (dfk::launch_gate_up(p, x, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
-        return DFK_OK;
+        return gate_up_impl(x, W_gate, W_up, d_model, h, B, d_model, d_ff, layout, stream);
     } catch (...) {
         return DFK_ERR_HIP;
     }
@@ -618,52 +683,56 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
                             const uint16_t *W_down, uint16_t *out, int B, int d_model, int d_ff,
                             dfk_layout_t layout, hipStream_t stream) {
     try {
-        if (!x || !W_gate || !W_up || !W_down || !out || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
-        dfk_status_t st = check_dims(B, d_model, d_ff);
-        if (st != DFK_OK) return st;
-        if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) || !aligned16(out))
-            return DFK_ERR_MISALIGNED;
-        int dev;
-        if ((st = current_device(&dev)) != DFK_OK) return st;
-        const int cus = device_cus(dev);
-        if (layout == DFK_LAYOUT_ROW_PERSISTENT) {
-            dfk::MlpPlan mp;
-            if (!dfk::make_mlp_plan(B, d_model, d_ff, cus, &mp)) return DFK_ERR_UNSUPPORTED;
-            // a cooperative launch is not captured into graphs here
-            if (stream_capturing(stream)) return DFK_ERR_UNSUPPORTED;
-            if (log_level() >= 2)
-                std::fprintf(stderr, "[dfk] mlp persistent: B=%d grid=%d lds=%zu groups=%d/%d\n", B, mp.grid,
-                             mp.lds_bytes, mp.gu_groups, mp.dn_groups);
-            Slot *slot = slot_for(dev, stream);
-            std::lock_guard<std::mutex> lock(slot->mu);
-            void *ws = nullptr;
-            unsigned *barrier = nullptr;
-            if ((st = ensure_workspace(slot, (size_t)B * d_ff * sizeof(float), &ws)) != DFK_OK) return st;
-            if ((st = ensure_barrier(slot, stream, &barrier)) != DFK_OK) return st;
-            if (dfk::launch_mlp(mp, x, W_gate, W_up, W_down, static_cast<float *>(ws), out, barrier, stream) !=
-                hipSuccess) {
-                (void)hipGetLastError();
-                return DFK_ERR_HIP;
-            }
+        return mlp_impl(x, W_gate, W_up, d_model, W_down, out, B, d_model, d_ff, layout, stream);
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+// W_gate, W_up and their row stride inside a packed [2 d_ff, d_model] tensor.
+static dfk_status_t unpack(const uint16_t *W_gu, int d_model, int d_ff, dfk_packing_t packing,
+                           const uint16_t **wg, const uint16_t **wu, int *ldw) {
+    if (!W_gu) return DFK_ERR_INVALID_ARG;
+    switch (packing) {
+        case DFK_PACK_BLOCKED:
+            *wg = W_gu;
+            *wu = W_gu + (size_t)d_ff * d_model;
+            *ldw = d_model;
             return DFK_OK;
-        }
-        Plan pg, pd;
-        if ((st = resolve(dfk::OP_GATE_UP, layout, B, d_model, d_ff, cus, &pg)) != DFK_OK) return st;
-        if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
-        log_plan("gate_up", pg);
-        log_plan("down", pd);
-        Slot *slot = slot_for(dev, stream);
-        std::lock_guard<std::mutex> lock(slot->mu);
-        void *ws = nullptr;
-        const size_t h_bytes = ((size_t)B * d_ff * sizeof(float) + 255) & ~size_t(255);
-        // the two kernels run in stream order, so their panel partials share one region
-        const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
-        if ((st = ensure_workspace(slot, h_bytes + partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
-        float *h = static_cast<float *>(ws);
-        float *partial = partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
-        if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
-        if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
-        return DFK_OK;
+        case DFK_PACK_INTERLEAVED:
+            *wg = W_gu;
+            *wu = W_gu + d_model;
+            *ldw = 2 * d_model;
+            return DFK_OK;
+    }
+    return DFK_ERR_INVALID_ARG;
+}
+
+dfk_status_t dfk_gate_up_silu_mul_packed(const uint16_t *x, const uint16_t *W_gu, float *h, int B, int d_model,
+                                         int d_ff, dfk_packing_t packing, dfk_layout_t layout,
+                                         hipStream_t stream) {
+    try {
+        const uint16_t *wg = nullptr, *wu = nullptr;
+        int ldw = 0;
+        dfk_status_t st = unpack(W_gu, d_model, d_ff, packing, &wg, &wu, &ldw);
+        if (st != DFK_OK) return st;
+        if (d_model > (1 << 29)) return DFK_ERR_UNSUPPORTED;
+        return gate_up_impl(x, wg, wu, ldw, h, B, d_model, d_ff, layout, stream);
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, const uint16_t *W_down, uint16_t *out,
+                                   int B, int d_model, int d_ff, dfk_packing_t packing, dfk_layout_t layout,
+                                   hipStream_t stream) {
+    try {
+        const uint16_t *wg = nullptr, *wu = nullptr;
+        int ldw = 0;
+        dfk_status_t st = unpack(W_gu, d_model, d_ff, packing, &wg, &wu, &ldw);
+        if (st != DFK_OK) return st;
+        if (d_model > (1 << 29)) return DFK_ERR_UNSUPPORTED;
+        return mlp_impl(x, wg, wu, ldw, W_down, out, B, d_model, d_ff, layout, stream);
     } catch (...) {
         return DFK_ERR_HIP;
     }

@@ -77,15 +77,24 @@ def norm_mlp(L, x=A, gain=A, eps=1e-5, wg=A, wu=A, wd=A, out=A, B=1, dm=256, dff
     return L.dfk_rmsnorm_swiglu_mlp(x, gain, eps, wg, wu, wd, out, B, dm, dff, layout, None)
 
 
+def gu_packed(L, x=A, wgu=A, h=A, B=1, dm=256, dff=688, packing=0, layout=0):
+    return L.dfk_gate_up_silu_mul_packed(x, wgu, h, B, dm, dff, packing, layout, None)
+
+
+def mlp_packed(L, x=A, wgu=A, wd=A, out=A, B=1, dm=256, dff=688, packing=1, layout=0):
+    return L.dfk_swiglu_mlp_packed(x, wgu, wd, out, B, dm, dff, packing, layout, None)
+
+
 def rmsnorm(L, x=A, gain=A, eps=1e-5, out=A, B=1, dm=256):
     return L.dfk_rmsnorm(x, gain, eps, out, B, dm, None)
 
 
-@pytest.mark.parametrize("fn", [gate_up, down, mlp, norm_gate_up, norm_mlp],
-                         ids=["gate_up", "down", "mlp", "norm_gate_up", "norm_mlp"])
+@pytest.mark.parametrize("fn", [gate_up, down, mlp, norm_gate_up, norm_mlp, gu_packed, mlp_packed],
+                         ids=["gate_up", "down", "mlp", "norm_gate_up", "norm_mlp", "gu_packed", "mlp_packed"])
 def test_invalid_arguments(L, fn):
     import inspect
-    ptrs = [p for p in inspect.signature(fn).parameters if p in ("x", "gain", "wg", "wu", "wd", "h", "out")]
+    ptrs = [p for p in inspect.signature(fn).parameters
+            if p in ("x", "gain", "wg", "wu", "wgu", "wd", "h", "out")]
     for p in ptrs:
         assert fn(L, **{p: NULL}) == Status.INVALID_ARG, p
         assert fn(L, **{p: MIS}) == Status.MISALIGNED, p
@@ -107,6 +116,12 @@ def test_invalid_arguments(L, fn):
 def test_invalid_eps(L, fn):
     for eps in (-1e-6, float("nan"), float("inf"), -float("inf")):
         assert fn(L, eps=eps) == Status.INVALID_ARG, eps
+
+
+@pytest.mark.parametrize("fn", [gu_packed, mlp_packed], ids=["gu_packed", "mlp_packed"])
+def test_invalid_packing(L, fn):
+    for packing in (-1, 2, 7):
+        assert fn(L, packing=packing) == Status.INVALID_ARG, packing
 
 
 def test_rmsnorm_invalid_arguments(L):
