@@ -48,6 +48,20 @@ def _p64(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(_f64p)
 
 
+def _codes(a, name: str) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8 or a.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint8 array of FP8 codes")
+    return a
+
+
+def _scales(a, n: int) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
+    if a.shape != (n,):
+        raise ValueError(f"expected {n} row scales, got {a.shape}")
+    return a
+
+
 def _bits(a, name: str) -> np.ndarray:
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16:
@@ -84,6 +98,18 @@ class Oracle:
         lib.oracle_rms_rescale.restype = ctypes.c_int
         lib.oracle_rms_rescale.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                            _u16p]
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        _u8p, _f32p = ctypes.c_void_p, ctypes.c_void_p
+        lib.oracle_gate_up_fp8.restype = ctypes.c_int
+        lib.oracle_gate_up_fp8.argtypes = [_u16p, _u8p, _f32p, _u8p, _f32p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, _f64p, ctypes.c_int]
+        lib.oracle_down_fp8.restype = ctypes.c_int
+        lib.oracle_down_fp8.argtypes = [_f64p, _u8p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p,
+                                        ctypes.c_int]
+        lib.oracle_mlp_fp8.restype = ctypes.c_int
+        lib.oracle_mlp_fp8.argtypes = [_u16p, _u8p, _f32p, _u8p, _f32p, _u8p, _f32p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int]
         lib.oracle_rmsnorm.restype = ctypes.c_int
         lib.oracle_rmsnorm.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _u16p]
 
@@ -146,6 +172,58 @@ class Oracle:
                                   _p64(y), _p64(h), nthreads)
         if rc != 0:
             raise RuntimeError(f"oracle_mlp failed ({rc})")
+        return y, h
+
+    # -- weight-only FP8 weights ---------------------------------------------
+    def e4m3_to_double(self, code: int) -> float:
+        return self._lib.oracle_e4m3_to_double(int(code))
+
+    def gate_up_fp8(self, x, q_gate, s_gate, q_up, s_up, nthreads: int = 0) -> np.ndarray:
+        """h fp64 [B, d_ff] over W = s[row] * e4m3(q)."""
+        x = _bits(x, "x")
+        B, d_model = x.shape
+        qg, qu = _codes(q_gate, "q_gate"), _codes(q_up, "q_up")
+        sg, su = _scales(s_gate, qg.shape[0]), _scales(s_up, qg.shape[0])
+        d_ff = qg.shape[0]
+        if qg.shape != (d_ff, d_model) or qu.shape != (d_ff, d_model):
+            raise ValueError("weight shapes do not match x")
+        h = np.empty((B, d_ff))
+        rc = self._lib.oracle_gate_up_fp8(_p16(x), qg.ctypes.data, sg.ctypes.data, qu.ctypes.data,
+                                          su.ctypes.data, B, d_model, d_ff, _p64(h), nthreads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gate_up_fp8 failed ({rc})")
+        return h
+
+    def down_fp8(self, h, q_down, s_down, nthreads: int = 0) -> np.ndarray:
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        B, d_ff = h.shape
+        qd = _codes(q_down, "q_down")
+        d_model = qd.shape[0]
+        if qd.shape != (d_model, d_ff):
+            raise ValueError("q_down shape does not match h")
+        sd = _scales(s_down, d_model)
+        y = np.empty((B, d_model))
+        rc = self._lib.oracle_down_fp8(_p64(h), qd.ctypes.data, sd.ctypes.data, B, d_model, d_ff, _p64(y),
+                                       nthreads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_down_fp8 failed ({rc})")
+        return y
+
+    def mlp_fp8(self, x, q_gate, s_gate, q_up, s_up, q_down, s_down, nthreads: int = 0):
+        """(y, h) fp64 over the dequantized FP8 weights."""
+        x = _bits(x, "x")
+        B, d_model = x.shape
+        qg, qu, qd = _codes(q_gate, "q_gate"), _codes(q_up, "q_up"), _codes(q_down, "q_down")
+        d_ff = qg.shape[0]
+        if qg.shape != (d_ff, d_model) or qu.shape != (d_ff, d_model) or qd.shape != (d_model, d_ff):
+            raise ValueError("weight shapes do not match x")
+        sg, su, sd = _scales(s_gate, d_ff), _scales(s_up, d_ff), _scales(s_down, d_model)
+        y = np.empty((B, d_model)); h = np.empty((B, d_ff))
+        rc = self._lib.oracle_mlp_fp8(_p16(x), qg.ctypes.data, sg.ctypes.data, qu.ctypes.data, su.ctypes.data,
+                                      qd.ctypes.data, sd.ctypes.data, B, d_model, d_ff, _p64(y), _p64(h),
+                                      nthreads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_mlp_fp8 failed ({rc})")
         return y, h
 
     def rmsnorm(self, x, gain, eps: float = 1e-5) -> np.ndarray:

@@ -10,7 +10,8 @@
  *
  * What it computes (each function names the passage it follows):
  *   g = x . W_gate^T,  u = x . W_up^T,  h = SiLU(g) * u,  y = h . W_down^T,
- * and the RMS normalization that may precede the gate and up projections
+ * the same over weight-only FP8 weights (dequantized exactly to fp64), and
+ * the RMS normalization that may precede the gate and up projections
  * with x [B, d_model], W_gate and W_up [d_ff, d_model], W_down [d_model, d_ff],
  * all given as bf16 bit patterns and widened exactly to fp64.  Every dot product
  * is summed in fp64 in ascending index order; nothing is rounded until the
@@ -261,6 +262,131 @@ int oracle_mlp(const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
     }
     int rc = oracle_gate_up(x, w_gate, w_up, B, d_model, d_ff, NULL, NULL, h, nthreads);
     if (rc == 0) rc = oracle_down(h, w_down, B, d_model, d_ff, y, nthreads);
+    if (!h_out) free(h);
+    return rc;
+}
+
+/* ---------- weight-only FP8 weights, dequantized in the product -------- */
+
+/*
+ * The GPULlama3.java pull request "[FP16] ... fusing dequantize with compute"
+ * (PR summary) dequantizes quantized weights inside the matrix-vector
+ * product instead of writing dequantized weights out first.  The page fixes
+ * no format.  Reading taken: OCP FP8 E4M3 codes (1 sign bit, 4 exponent bits
+ * with bias 7, 3 fraction bits; exponent field 0 holds the subnormals
+ * m/8 * 2^-6; no infinities; S.1111.111 is NaN; largest finite 448) with one
+ * fp32 scale per weight row (output channel):
+ *     W[r, c] = s[r] * e4m3(q[r, c]).
+ * The quantized MLP is then exactly the MLP above over these weights.
+ */
+double oracle_e4m3_to_double(uint8_t q) {
+    const int sign = q >> 7, e = (q >> 3) & 0xF, m = q & 7;
+    if (e == 0xF && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9)         /* (m / 8) * 2^-6 */
+                        : ldexp((double)(8 + m), e - 10); /* (1 + m / 8) * 2^(e - 7) */
+    return sign ? -v : v;
+}
+
+typedef struct {
+    const double *xd;          /* [B, d_model] widened x */
+    const uint8_t *qg, *qu;    /* [d_ff, d_model] E4M3 codes */
+    const float *sg, *su;      /* [d_ff] row scales */
+    int B, d_model, d_ff;
+    double *h;                 /* [B, d_ff] */
+} gu8_ctx;
+
+/* As gu_span, over the dequantized rows s[n] * e4m3(q[n, k]) (each product of
+ * a 4-bit code value and a 24-bit scale is exact in fp64). */
+static void gu8_span(void *p, long lo, long hi) {
+    gu8_ctx *c = (gu8_ctx *)p;
+    const int B = c->B, K = c->d_model, N = c->d_ff;
+    double *ag = (double *)calloc((size_t)B, sizeof(double));
+    double *au = (double *)calloc((size_t)B, sizeof(double));
+    for (long n = lo; n < hi; ++n) {
+        const uint8_t *rg = c->qg + (size_t)n * K;
+        const uint8_t *ru = c->qu + (size_t)n * K;
+        const double sg = (double)c->sg[n], su = (double)c->su[n];
+        for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            double wg = sg * oracle_e4m3_to_double(rg[k]);
+            double wu = su * oracle_e4m3_to_double(ru[k]);
+            for (int b = 0; b < B; ++b) {
+                double xv = c->xd[(size_t)b * K + k];
+                ag[b] += xv * wg;
+                au[b] += xv * wu;
+            }
+        }
+        for (int b = 0; b < B; ++b) c->h[(size_t)b * N + (size_t)n] = oracle_silu(ag[b]) * au[b];
+    }
+    free(ag);
+    free(au);
+}
+
+/* The fused gate-up step over FP8 weights; h fp64 [B, d_ff]. */
+int oracle_gate_up_fp8(const uint16_t *x, const uint8_t *q_gate, const float *s_gate, const uint8_t *q_up,
+                       const float *s_up, int B, int d_model, int d_ff, double *h, int nthreads) {
+    if (B < 0 || d_model < 0 || d_ff < 0) return -1;
+    if (B == 0 || d_ff == 0) return 0;
+    if (!x || !q_gate || !s_gate || !q_up || !s_up || !h) return -1;
+    double *xd = (double *)malloc(sizeof(double) * (size_t)B * (size_t)(d_model ? d_model : 1));
+    if (!xd) return -1;
+    for (size_t i = 0; i < (size_t)B * (size_t)d_model; ++i) xd[i] = widen_bf16(x[i]);
+    gu8_ctx c = {xd, q_gate, q_up, s_gate, s_up, B, d_model, d_ff, h};
+    parallel_for(d_ff, nthreads, gu8_span, &c);
+    free(xd);
+    return 0;
+}
+
+typedef struct {
+    const double *h;           /* [B, d_ff] */
+    const uint8_t *qd;         /* [d_model, d_ff] E4M3 codes */
+    const float *sd;           /* [d_model] row scales */
+    int B, d_model, d_ff;
+    double *y;                 /* [B, d_model] */
+} dn8_ctx;
+
+static void dn8_span(void *p, long lo, long hi) {
+    dn8_ctx *c = (dn8_ctx *)p;
+    const int B = c->B, M = c->d_model, N = c->d_ff;
+    double *acc = (double *)calloc((size_t)B, sizeof(double));
+    for (long m = lo; m < hi; ++m) {
+        const uint8_t *rd = c->qd + (size_t)m * N;
+        const double s = (double)c->sd[m];
+        for (int b = 0; b < B; ++b) acc[b] = 0.0;
+        for (int n = 0; n < N; ++n) {
+            double w = s * oracle_e4m3_to_double(rd[n]);
+            for (int b = 0; b < B; ++b) acc[b] += c->h[(size_t)b * N + n] * w;
+        }
+        for (int b = 0; b < B; ++b) c->y[(size_t)b * M + (size_t)m] = acc[b];
+    }
+    free(acc);
+}
+
+/* The down projection over FP8 weights; y fp64 [B, d_model]. */
+int oracle_down_fp8(const double *h, const uint8_t *q_down, const float *s_down, int B, int d_model, int d_ff,
+                    double *y, int nthreads) {
+    if (B < 0 || d_model < 0 || d_ff < 0) return -1;
+    if (B == 0 || d_model == 0) return 0;
+    if (!h || !q_down || !s_down || !y) return -1;
+    dn8_ctx c = {h, q_down, s_down, B, d_model, d_ff, y};
+    parallel_for(d_model, nthreads, dn8_span, &c);
+    return 0;
+}
+
+/* The whole MLP over FP8 weights, h unrounded between the steps. */
+int oracle_mlp_fp8(const uint16_t *x, const uint8_t *q_gate, const float *s_gate, const uint8_t *q_up,
+                   const float *s_up, const uint8_t *q_down, const float *s_down, int B, int d_model, int d_ff,
+                   double *y, double *h_out, int nthreads) {
+    if (B < 0 || d_model < 0 || d_ff < 0) return -1;
+    if (B == 0 || d_model == 0) return 0;
+    if (!y) return -1;
+    double *h = h_out;
+    if (!h) {
+        h = (double *)malloc(sizeof(double) * (size_t)B * (size_t)(d_ff ? d_ff : 1));
+        if (!h) return -1;
+    }
+    int rc = oracle_gate_up_fp8(x, q_gate, s_gate, q_up, s_up, B, d_model, d_ff, h, nthreads);
+    if (rc == 0) rc = oracle_down_fp8(h, q_down, s_down, B, d_model, d_ff, y, nthreads);
     if (!h_out) free(h);
     return rc;
 }

@@ -17,6 +17,8 @@ layer shapes, no trained weights are used):
     Llama-3-70B layer weights 4001..4003, x 4100+B; shape sweep entry s weights
     5000+100s+{1,2,3}, x 5000+100s+10+B.
   * RMS-normalization gains: 1 + N(0, 0.1^2) per column (``norm_gain``).
+  * FP8 weights (``fp8_weights``): N(0, std^2) rows scaled by max|row| / 448
+    into OCP E4M3 codes, x ~ N(0, 1); seeds seed+{1,2,3} for gate, up, down.
 """
 from __future__ import annotations
 
@@ -159,6 +161,29 @@ def norm_gain(d_model: int, seed: int, std: float = 0.1) -> np.ndarray:
     g = torch.Generator().manual_seed(int(seed))
     t = torch.randn(d_model, generator=g, dtype=torch.float32).mul_(std).add_(1.0)
     return to_bf16_bits(t)
+
+
+def fp8_weights(rows: int, cols: int, std: float, seed: int):
+    """Weight-only FP8 weights: (codes, scales).  Draws W ~ N(0, std^2) as
+    fp32, takes one scale per row, s = max|W[row]| / 448 (1 for an all-zero
+    row), and stores W / s as OCP FP8 E4M3 codes (torch's float8_e4m3fn
+    conversion, round to nearest even): codes uint8 [rows, cols], scales
+    float32 [rows].  The weight the codes stand for is s[row] * e4m3(code)."""
+    g = torch.Generator().manual_seed(int(seed))
+    w = torch.randn(rows, cols, generator=g, dtype=torch.float32).mul_(std)
+    amax = w.abs().amax(dim=1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (w / s[:, None]).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy().copy(), s.numpy().copy()
+
+
+def fp8_layer(B: int, d_model: int, d_ff: int, seed: int, std: float = 0.02) -> Dict[str, np.ndarray]:
+    """x (bf16 bits) and FP8 gate/up/down weights with their row scales."""
+    qg, sg = fp8_weights(d_ff, d_model, std, seed + 1)
+    qu, su = fp8_weights(d_ff, d_model, std, seed + 2)
+    qd, sd = fp8_weights(d_model, d_ff, std, seed + 3)
+    return {"x": randn_bf16((B, d_model), 1.0, seed), "q_gate": qg, "s_gate": sg, "q_up": qu, "s_up": su,
+            "q_down": qd, "s_down": sd}
 
 
 def integer_h(B: int, d_ff: int, seed: int, bound: int = 256) -> np.ndarray:

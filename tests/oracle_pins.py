@@ -326,10 +326,111 @@ def check_rmsnorm_invariants(orc):
     assert np.allclose((widen(orc.rmsnorm(x, ones, eps=0.0)) ** 2).mean(axis=1), 1.0, rtol=1e-2)
 
 
+# ------------------------------------------------------- FP8 weights ----
+
+def check_e4m3_decode(orc):
+    """Every E4M3 code against torch's float8_e4m3fn (an independent decoder)
+    and the format's fixed points: 448 the largest finite value, 2^-6 the
+    smallest normal, 2^-9 the smallest subnormal, S.1111.111 NaN, signed zero."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([orc.e4m3_to_double(int(c)) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert orc.e4m3_to_double(0x7E) == 448.0 and orc.e4m3_to_double(0xFE) == -448.0
+    assert orc.e4m3_to_double(0x08) == 2.0 ** -6 and orc.e4m3_to_double(0x01) == 2.0 ** -9
+    assert orc.e4m3_to_double(0x38) == 1.0 and orc.e4m3_to_double(0x3F) == 1.875
+    assert np.isnan(orc.e4m3_to_double(0x7F)) and np.isnan(orc.e4m3_to_double(0xFF))
+    assert math.copysign(1.0, orc.e4m3_to_double(0x80)) == -1.0
+
+
+def _fp8_exact_bf16_layer(B, K, N, seed):
+    """FP8 codes with power-of-two row scales 2^-(row % 5): every weight
+    s * e4m3(q) then has at most 4 significant bits, so it is also exactly a
+    bf16 value."""
+    rng = np.random.default_rng(seed)
+
+    def codes(r, c):
+        q = rng.integers(0, 256, size=(r, c), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        return q
+
+    def scales(r):
+        return np.array([2.0 ** -(i % 5) for i in range(r)], dtype=np.float32)
+
+    def as_bf16(q, s):
+        vals = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).to(torch.float64) * torch.from_numpy(
+            s.astype(np.float64))[:, None]
+        return inputs.to_bf16_bits(vals.to(torch.float32))
+
+    x = inputs.randn_bf16((B, K), 1.0, seed)
+    qg, qu, qd = codes(N, K), codes(N, K), codes(K, N)
+    sg, su, sd = scales(N), scales(N)[::-1].copy(), scales(K)
+    return x, (qg, sg, qu, su, qd, sd), (as_bf16(qg, sg), as_bf16(qu, su), as_bf16(qd, sd))
+
+
+def check_fp8_reduces_to_bf16(orc):
+    """Quantized weights whose dequantized values are exactly bf16: the FP8
+    MLP must equal the (pinned) bf16 MLP over those values bit for bit in
+    fp64, on h and y."""
+    for i, (B, K, N) in enumerate([(1, 16, 24), (3, 40, 8), (2, 8, 56)]):
+        x, (qg, sg, qu, su, qd, sd), (wg, wu, wd) = _fp8_exact_bf16_layer(B, K, N, seed=300 + i)
+        y8, h8 = orc.mlp_fp8(x, qg, sg, qu, su, qd, sd)
+        y, h = orc.mlp(x, wg, wu, wd)
+        assert np.array_equal(h8, h), ("h", B, K, N)
+        assert np.array_equal(y8, y), ("y", B, K, N)
+        assert np.array_equal(orc.gate_up_fp8(x, qg, sg, qu, su), h)
+        assert np.array_equal(orc.down_fp8(h, qd, sd), y)
+
+
+def check_fp8_bruteforce(orc):
+    """General fp32 row scales against exact rationals + 40-digit SiLU:
+    normwise error <= 1e-14 on h and y."""
+    for i, (B, K, N) in enumerate([(1, 8, 5), (2, 5, 7), (3, 16, 4)]):
+        L = inputs.fp8_layer(B, K, N, seed=400 + i, std=0.5)
+
+        def deq(q, s):
+            return torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy() * \
+                s.astype(np.float64)[:, None]
+
+        wg, wu, wd = deq(L["q_gate"], L["s_gate"]), deq(L["q_up"], L["s_up"]), deq(L["q_down"], L["s_down"])
+        xs = widen(L["x"])
+        fx = [[Fraction(float(v)) for v in row] for row in xs]
+        g = [[sum((fx[b][k] * Fraction(float(wg[n, k])) for k in range(K)), Fraction(0)) for n in range(N)]
+             for b in range(B)]
+        u = [[sum((fx[b][k] * Fraction(float(wu[n, k])) for k in range(K)), Fraction(0)) for n in range(N)]
+             for b in range(B)]
+        eh = [[mp_silu(mpmath.mpf(g[b][n].numerator) / g[b][n].denominator)
+               * (mpmath.mpf(u[b][n].numerator) / u[b][n].denominator) for n in range(N)] for b in range(B)]
+        ey = [[mpmath.fsum(eh[b][n] * mpmath.mpf(float(wd[m, n])) for n in range(N)) for m in range(K)]
+              for b in range(B)]
+        y, h = orc.mlp_fp8(L["x"], L["q_gate"], L["s_gate"], L["q_up"], L["s_up"], L["q_down"], L["s_down"])
+        fl = lambda m: np.array([[float(v) for v in row] for row in m])
+        assert normwise(h, fl(eh)) <= 1e-14, ("h", B, K, N)
+        assert normwise(y, fl(ey)) <= 1e-14, ("y", B, K, N)
+
+
+def check_fp8_scale_linearity(orc):
+    """Doubling every up scale doubles h and y; doubling every down scale
+    doubles y (powers of two: exact in fp64)."""
+    L = inputs.fp8_layer(2, 24, 40, seed=450, std=0.3)
+    a = [L[k] for k in ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down")]
+    y, h = orc.mlp_fp8(L["x"], *a)
+    a_up = list(a); a_up[3] = a[3] * 2
+    y2, h2 = orc.mlp_fp8(L["x"], *a_up)
+    assert np.array_equal(h2, 2 * h) and np.array_equal(y2, 2 * y)
+    a_dn = list(a); a_dn[5] = a[5] * 2
+    y3, h3 = orc.mlp_fp8(L["x"], *a_dn)
+    assert np.array_equal(h3, h) and np.array_equal(y3, 2 * y)
+
+
 ALL_CHECKS = [
     check_silu_tanh_form, check_silu_lambert_minimum, check_silu_identities,
     check_silu_limits, check_bf16_rne, check_worked_example, check_bruteforce_tiny,
     check_extended_precision, check_zero_invariants, check_linearity_in_wdown,
     check_batch_and_permutation, check_threads_deterministic, check_rms_rescale,
-    check_rmsnorm_bruteforce, check_rmsnorm_invariants,
+    check_rmsnorm_bruteforce, check_rmsnorm_invariants, check_e4m3_decode, check_fp8_reduces_to_bf16,
+    check_fp8_bruteforce, check_fp8_scale_linearity,
 ]

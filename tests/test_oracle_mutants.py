@@ -14,18 +14,21 @@ from tests import oracle_pins
 
 MUTANTS = {
     "exp_sign": ("exp(-z)", "exp(z)"),
-    "silu_on_up": ("oracle_silu(ag[b]) * au[b]", "oracle_silu(au[b]) * ag[b]"),
-    "no_silu": ("oracle_silu(ag[b]) * au[b]", "ag[b] * au[b]"),
+    "silu_on_up": ("if (c->h) c->h[o] = oracle_silu(ag[b]) * au[b]", "if (c->h) c->h[o] = oracle_silu(au[b]) * ag[b]"),
+    "no_silu": ("if (c->h) c->h[o] = oracle_silu(ag[b]) * au[b]", "if (c->h) c->h[o] = ag[b] * au[b]"),
     "sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "down_transposed": ("double w = widen_bf16(rd[n]);",
                         "double w = widen_bf16(c->wd[(size_t)n * M + m]);"),
-    "gate_up_drops_last_k": ("for (int k = 0; k < K; ++k) {", "for (int k = 0; k < K - 1; ++k) {"),
-    "down_drops_last_n": ("for (int n = 0; n < N; ++n) {", "for (int n = 0; n < N - 1; ++n) {"),
-    "x_batch_stride": ("c->xd[(size_t)b * K + k]", "c->xd[(size_t)b + k]"),
+    "gate_up_drops_last_k": ("for (int k = 0; k < K; ++k) {\n            double wg = widen_bf16(rg[k]);",
+                             "for (int k = 0; k < K - 1; ++k) {\n            double wg = widen_bf16(rg[k]);"),
+    "down_drops_last_n": ("for (int n = 0; n < N; ++n) {\n            double w = widen_bf16(rd[n]);",
+                          "for (int n = 0; n < N - 1; ++n) {\n            double w = widen_bf16(rd[n]);"),
+    "x_batch_stride": ("double wu = widen_bf16(ru[k]);\n            for (int b = 0; b < B; ++b) {\n                double xv = c->xd[(size_t)b * K + k];",
+                       "double wu = widen_bf16(ru[k]);\n            for (int b = 0; b < B; ++b) {\n                double xv = c->xd[(size_t)b + k];"),
     "h_rounded_fp32": ("c->h[o] = oracle_silu(ag[b]) * au[b];",
                        "c->h[o] = (float)(oracle_silu(ag[b]) * au[b]);"),
-    "y_stored_transposed": ("c->y[(size_t)b * M + (size_t)m] = acc[b];",
-                            "c->y[(size_t)m * B + (size_t)b] = acc[b];"),
+    "y_stored_transposed": ("acc[b] += c->h[(size_t)b * N + n] * w;\n        }\n        for (int b = 0; b < B; ++b) c->y[(size_t)b * M + (size_t)m] = acc[b];\n    }\n    free(acc);\n}\n\n/*\n * The separate down",
+                            "acc[b] += c->h[(size_t)b * N + n] * w;\n        }\n        for (int b = 0; b < B; ++b) c->y[(size_t)m * B + (size_t)b] = acc[b];\n    }\n    free(acc);\n}\n\n/*\n * The separate down"),
     "bf16_truncates": ("nearbyint(a / q)", "floor(a / q)"),
     "rmsnorm_sum_not_mean": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn[",
                              "double inv = 1.0 / sqrt(ss + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
@@ -35,6 +38,13 @@ MUTANTS = {
                         "double inv = 1.0 / (ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
     "rmsnorm_gain_first_only": ("* widen_bf16(gain[k])", "* widen_bf16(gain[0])"),
     "rmsnorm_batch_stride": ("const uint16_t *row = x + (size_t)b * d_model;", "const uint16_t *row = x + (size_t)b;"),
+    "fp8_bias_8": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    "fp8_no_subnormals": ("(e == 0) ? ldexp((double)m, -9)", "(e == 0) ? 0.0"),
+    "fp8_gate_scale_ignored": ("const double sg = (double)c->sg[n], su", "const double sg = 1.0, su"),
+    "fp8_down_scale_by_column": ("double w = s * oracle_e4m3_to_double(rd[n]);",
+                                 "double w = (double)c->sd[n % M] * oracle_e4m3_to_double(rd[n]);"),
+    "fp8_up_codes_from_gate": ("double wu = su * oracle_e4m3_to_double(ru[k]);",
+                               "double wu = su * oracle_e4m3_to_double(rg[k]);"),
 }
 
 
