@@ -264,6 +264,46 @@ def time_packed(sets, device, batches=(1, 4, 8), steps=200, warmup=20):
     return res
 
 
+def fp8_mlp_bytes(B, d_model=D_MODEL, d_ff=D_FF):
+    """Algorithmic bytes of one FP8-weight MLP call: the E4M3 codes and row
+    scales of the three matrices, x, h written and read (fp32), y."""
+    return 3 * d_model * d_ff + 4 * (2 * d_ff + d_model) + 2 * B * d_model + 2 * 4 * B * d_ff + 2 * B * d_model
+
+
+def time_fp8(device, batches=(1, 2, 3, 4), steps=300, warmup=30, rotate=8):
+    """Context: the MLP over weight-only FP8 weights (E4M3 codes + per-row
+    fp32 scales) at the 8B shape, `rotate` weight sets (2.8 GB) so every call
+    streams from HBM: us per call and HBM roofline fraction of the codes."""
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import inputs
+
+    def codes(rows, cols, seed):
+        w = inputs.randn_bf16_device((rows, cols), 0.02, seed, device).float()
+        s = (w.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+        return (w / s[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), s.contiguous()
+
+    sets = []
+    for r in range(rotate):
+        base = 6500 + 10 * r
+        qg, sg = codes(D_FF, D_MODEL, base + 1)
+        qu, su = codes(D_FF, D_MODEL, base + 2)
+        qd, sd = codes(D_MODEL, D_FF, base + 3)
+        sets.append((qg, sg, qu, su, qd, sd))
+    torch.cuda.synchronize()
+    res = {}
+    for B in batches:
+        x = inputs.randn_bf16_device((B, D_MODEL), 1.0, 6100 + B, device)
+        out = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device)
+        ms = _timed(lambda i: dfk.dfk_swiglu_mlp_fp8(x, *sets[i % rotate], out), steps, warmup)
+        gbps = fp8_mlp_bytes(B) / (ms * 1e-3) / 1e9
+        res[str(B)] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_rmsnorm(sets, device, batches=(1, 4, 8, 16), steps=200, warmup=20):
     """Context: the MLP on RMS-normalized input at the 8B layer shape, us per
     call: the fused entry point (norm inside gate-up where the kernel stages
@@ -381,8 +421,9 @@ def main():
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
 
-    stack, shape70b, norm, persistent, packed = None, None, None, None, None
+    stack, shape70b, norm, persistent, packed, fp8 = None, None, None, None, None, None
     if not args.no_sweep:
+        fp8 = time_fp8(device)
         packed = time_packed(sets, device)
         persistent = time_persistent(sets, device)
         norm = time_rmsnorm(sets, device)
@@ -429,6 +470,7 @@ def main():
         "rmsnorm_mlp_llama8b": norm,
         "persistent_mlp_llama8b": persistent,
         "packed_gate_up_llama8b": packed,
+        "fp8_weights_mlp_llama8b": fp8,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets)

@@ -167,6 +167,42 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
                                    dfk_packing_t packing, dfk_layout_t layout, hipStream_t stream);
 
 /*
+ * Weight-only FP8 weights, dequantized inside the kernels (GPULlama3.java
+ * pull request "[FP16] ... fusing dequantize with compute", PR summary:
+ * quantized weights are dequantized inside the matrix-vector product and
+ * never written back dequantized).  The page fixes no format; here a weight
+ * matrix W [rows, cols] is stored as
+ *     Wq  [rows, cols]  uint8  OCP FP8 E4M3 codes (bias 7, 3 fraction bits,
+ *                              subnormals, no infinities, S.1111.111 = NaN)
+ *     s   [rows]        fp32   one scale per row (output channel)
+ * standing for W[r, c] = s[r] * e4m3(Wq[r, c]).  The codes stream from HBM at
+ * half the bytes of bf16 and are widened in registers; each row's fp32 sum is
+ * multiplied by its scale once.  The computed h and out are those of the bf16
+ * entry points over the dequantized weights (to fp32 summation order).
+ * Limits beyond the shared ones: 1 <= B <= 4, d_model and d_ff multiples of
+ * 16, B * d_model * 2 <= 160 KiB; DFK_ERR_UNSUPPORTED otherwise.  Layouts:
+ * AUTO, ROW and ROW_VALU (all the vector-ALU row walk); the others are
+ * DFK_ERR_UNSUPPORTED.  Code and tensor pointers must be 16-byte aligned,
+ * scale pointers 4-byte aligned.
+ */
+dfk_status_t dfk_gate_up_silu_mul_fp8(const uint16_t *x, const uint8_t *Wq_gate, const float *s_gate,
+                                      const uint8_t *Wq_up, const float *s_up, float *h, int B,
+                                      int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream);
+
+/* The down projection over FP8 W_down ([d_model, d_ff] codes, [d_model]
+ * scales); as dfk_down_proj otherwise. */
+dfk_status_t dfk_down_proj_fp8(const float *h, const uint8_t *Wq_down, const float *s_down,
+                               uint16_t *out, int B, int d_model, int d_ff, dfk_layout_t layout,
+                               hipStream_t stream);
+
+/* The whole MLP over FP8 weights: the two kernels above on one stream, h in
+ * the library-owned workspace of dfk_swiglu_mlp. */
+dfk_status_t dfk_swiglu_mlp_fp8(const uint16_t *x, const uint8_t *Wq_gate, const float *s_gate,
+                                const uint8_t *Wq_up, const float *s_up, const uint8_t *Wq_down,
+                                const float *s_down, uint16_t *out, int B, int d_model, int d_ff,
+                                dfk_layout_t layout, hipStream_t stream);
+
+/*
  * RMS normalization of the MLP input (GPULlama3.java pull request "[FP16] ...
  * fusing dequantize with compute", commit list: RMS normalization fused with
  * the gate and up projections; the page does not define the normalization,

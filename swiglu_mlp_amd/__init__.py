@@ -59,7 +59,7 @@ EXPORTED = (
     "dfk_status_string", "dfk_layout_name", "dfk_version", "dfk_load_tuning_table",
     "dfk_tuning_table_source", "dfk_release_workspace", "dfk_rmsnorm",
     "dfk_rmsnorm_gate_up_silu_mul", "dfk_rmsnorm_swiglu_mlp", "dfk_gate_up_silu_mul_packed",
-    "dfk_swiglu_mlp_packed",
+    "dfk_swiglu_mlp_packed", "dfk_gate_up_silu_mul_fp8", "dfk_down_proj_fp8", "dfk_swiglu_mlp_fp8",
 )
 
 
@@ -114,6 +114,12 @@ def lib() -> ctypes.CDLL:
     L.dfk_gate_up_silu_mul_packed.restype = i
     L.dfk_swiglu_mlp_packed.argtypes = [u16p, u16p, u16p, u16p, i, i, i, i, i, vp]
     L.dfk_swiglu_mlp_packed.restype = i
+    L.dfk_gate_up_silu_mul_fp8.argtypes = [u16p, vp, vp, vp, vp, f32p, i, i, i, i, vp]
+    L.dfk_gate_up_silu_mul_fp8.restype = i
+    L.dfk_down_proj_fp8.argtypes = [f32p, vp, vp, u16p, i, i, i, i, vp]
+    L.dfk_down_proj_fp8.restype = i
+    L.dfk_swiglu_mlp_fp8.argtypes = [u16p, vp, vp, vp, vp, vp, vp, u16p, i, i, i, i, vp]
+    L.dfk_swiglu_mlp_fp8.restype = i
     _lib = L
     return L
 
@@ -238,6 +244,80 @@ def dfk_swiglu_mlp_packed(x, W_gu, W_down, packing: int, out=None, layout: int =
     st = lib().dfk_swiglu_mlp_packed(x.data_ptr(), W_gu.data_ptr(), W_down.data_ptr(), out.data_ptr(), B,
                                      d_model, d_ff, int(packing), int(layout), _stream_handle(stream, x.device))
     _check(st, "dfk_swiglu_mlp_packed")
+    return out
+
+
+def _expect_fp8(q, s, name: str, rows: int, cols: int) -> None:
+    import torch
+    _expect_codes(q, name, (rows, cols))
+    _expect(s, name.replace("q", "s", 1), torch.float32, (rows,))
+
+
+def _expect_codes(q, name: str, shape) -> None:
+    import torch
+    if not isinstance(q, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {q.dtype}")
+    if q.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {q.device}")
+    if tuple(q.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(q.shape)}")
+    if not q.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def dfk_gate_up_silu_mul_fp8(x, q_gate, s_gate, q_up, s_up, h=None, layout: int = Layout.AUTO, stream=None):
+    """h = SiLU(x W_gate^T) * (x W_up^T) with W = s[row] * e4m3(q), one fused kernel."""
+    import torch
+    B, d_model = x.shape
+    d_ff = q_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect_fp8(q_gate, s_gate, "q_gate", d_ff, d_model)
+    _expect_fp8(q_up, s_up, "q_up", d_ff, d_model)
+    if h is None:
+        h = torch.empty((B, d_ff), dtype=torch.float32, device=x.device)
+    _expect(h, "h", torch.float32, (B, d_ff))
+    st = lib().dfk_gate_up_silu_mul_fp8(x.data_ptr(), q_gate.data_ptr(), s_gate.data_ptr(), q_up.data_ptr(),
+                                        s_up.data_ptr(), h.data_ptr(), B, d_model, d_ff, int(layout),
+                                        _stream_handle(stream, x.device))
+    _check(st, "dfk_gate_up_silu_mul_fp8")
+    return h
+
+
+def dfk_down_proj_fp8(h, q_down, s_down, out=None, layout: int = Layout.AUTO, stream=None):
+    """out = bf16_RNE(h W_down^T) with W_down = s[row] * e4m3(q)."""
+    import torch
+    B, d_ff = h.shape
+    d_model = q_down.shape[0]
+    _expect(h, "h", torch.float32, (B, d_ff))
+    _expect_fp8(q_down, s_down, "q_down", d_model, d_ff)
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=h.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_down_proj_fp8(h.data_ptr(), q_down.data_ptr(), s_down.data_ptr(), out.data_ptr(), B, d_model,
+                                 d_ff, int(layout), _stream_handle(stream, h.device))
+    _check(st, "dfk_down_proj_fp8")
+    return out
+
+
+def dfk_swiglu_mlp_fp8(x, q_gate, s_gate, q_up, s_up, q_down, s_down, out=None, layout: int = Layout.AUTO,
+                       stream=None):
+    """The whole MLP over FP8 weights (two kernels)."""
+    import torch
+    B, d_model = x.shape
+    d_ff = q_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect_fp8(q_gate, s_gate, "q_gate", d_ff, d_model)
+    _expect_fp8(q_up, s_up, "q_up", d_ff, d_model)
+    _expect_fp8(q_down, s_down, "q_down", d_model, d_ff)
+    if out is None:
+        out = torch.empty((B, d_model), dtype=torch.bfloat16, device=x.device)
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_swiglu_mlp_fp8(x.data_ptr(), q_gate.data_ptr(), s_gate.data_ptr(), q_up.data_ptr(),
+                                  s_up.data_ptr(), q_down.data_ptr(), s_down.data_ptr(), out.data_ptr(), B,
+                                  d_model, d_ff, int(layout), _stream_handle(stream, x.device))
+    _check(st, "dfk_swiglu_mlp_fp8")
     return out
 
 

@@ -39,7 +39,9 @@ enum Kind {
     KIND_DN_MFMA_LT = 11,
     KIND_GU_MFMA_STAGED = 12,  // gate-up, B operand staged in LDS per workgroup (B > 16)
     KIND_DN_MFMA_STAGED = 13,  // down, the same, K split across workgroups + a reduce kernel
-    KIND_DN_MFMA_COOP = 15     // down ROW (B <= 16), workgroup-cooperative LDS weight tile
+    KIND_DN_MFMA_COOP = 15,    // down ROW (B <= 16), workgroup-cooperative LDS weight tile
+    KIND_GU_FP8_ROW = 16,      // gate-up over FP8 E4M3 weights + row scales, VALU row walk
+    KIND_DN_FP8_ROW = 17       // down, the same
 };
 
 // A fully resolved launch: which kernel and how the weight matrix is cut.
@@ -90,6 +92,18 @@ hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_ga
 // xn [B][K] = the RMS normalization of x [B][K] (one workgroup per batch row).
 hipError_t launch_rmsnorm(const uint16_t *x, const NormArgs &norm, uint16_t *xn, int B, int K,
                           hipStream_t stream);
+// Weight-only FP8 (E4M3 codes, one fp32 scale per weight row): VALU row
+// kernels, B <= kF8MaxBatch (beyond it the down kernel's fp32 h operand no
+// longer fits in registers), d_model and d_ff multiples of 16.
+constexpr int kF8MaxBatch = 4;
+bool make_fp8_plan(Op op, int B, int d_model, int d_ff, int cus, Plan *plan);
+hipError_t launch_gate_up_fp8(const Plan &p, const uint16_t *x, const uint8_t *q_gate, const float *s_gate,
+                              const uint8_t *q_up, const float *s_up, float *h, hipStream_t stream);
+// `partial` must hold p.partial_floats floats when that is non-zero (K cut
+// into panels whose h fits in LDS, added by a second kernel).
+hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down, const float *s_down, uint16_t *y,
+                           float *partial, hipStream_t stream);
+
 // The persistent MLP: the VALU gate-up row walk, a grid barrier and the VALU
 // down row walk (h in LDS) in one cooperative launch, every workgroup
 // resident.  Batches up to kMlpMaxBatch, h up to kHLdsLimit bytes.

@@ -789,6 +789,355 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_row_kernel(DownArgs a) {
     down_row_body<B, R, U, HLDS, false>(a, hs, wave_id, gridDim.x * waves, [] { return false; });
 }
 
+// ============================================= FP8 weights (row, VALU) =====
+//
+// Weight-only FP8 (the GPULlama3.java pull request fuses dequantization into
+// the matrix-vector product): weights are OCP FP8 E4M3 codes with one fp32
+// scale per row, W[r, c] = s[r] * e4m3(q[r, c]).  The codes stream from HBM
+// (half the bytes of bf16) and are widened in registers; the row scale
+// multiplies the row's fp32 sum once.  Same flattened, double-buffered row
+// walk as the bf16 row kernels, one 16-byte load now carrying 16 weights.
+// Each load group also loads its rows' scales (all lanes the same address),
+// so the epilogue never waits on a load issued after the weights.
+
+struct GateUpF8Args {
+    const uint16_t *x;
+    const uint8_t *qg, *qu;  // [N][K] E4M3 codes
+    const float *sg, *su;    // [N] row scales
+    float *h;
+    int B, K, N;  // batch, d_model, d_ff
+    int C;        // 16-byte x chunks per row (K / 8)
+    int C16;      // 16-byte weight chunks per row (K / 16)
+    int groups;
+};
+
+struct DownF8Args {
+    const float *h;
+    const uint8_t *qd;  // [M][K] E4M3 codes
+    const float *sd;    // [M] row scales
+    uint16_t *y;
+    int B, K, M;  // batch, d_ff, d_model
+    int C16;      // 16-byte weight chunks per row (K / 16)
+    int groups;
+};
+
+// Two E4M3 codes (the low or high half of a word) as a bf16 pair; exact, every
+// E4M3 value being a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// 16 codes (k .. k+15) as two chunks of 8 bf16 (k .. k+7, k+8 .. k+15).
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t q, u32x4_t &lo, u32x4_t &hi) {
+    lo = u32x4_t{e4m3x2_to_bf16x2<false>(q.x), e4m3x2_to_bf16x2<true>(q.x), e4m3x2_to_bf16x2<false>(q.y),
+                 e4m3x2_to_bf16x2<true>(q.y)};
+    hi = u32x4_t{e4m3x2_to_bf16x2<false>(q.z), e4m3x2_to_bf16x2<true>(q.z), e4m3x2_to_bf16x2<false>(q.w),
+                 e4m3x2_to_bf16x2<true>(q.w)};
+}
+
+template <int B, int R, int U>
+__global__ __launch_bounds__(kValuBlock) void gate_up_fp8_row_kernel(GateUpF8Args a) {
+    extern __shared__ u32x4_t xs[];  // [B][C]
+    constexpr int waves = kValuBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    const int total_waves = gridDim.x * waves;
+    constexpr int G = kWave * U;  // weight chunks per load group
+    const int gpr = (a.C16 + G - 1) / G;
+    const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
+    const int total = rows * gpr;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    float ag[R][B], au[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
+    struct Buf {
+        u32x4_t g[U][R], u[U][R];
+        float sg[R], su[R];
+    };
+    auto load = [&](Buf &f, int k, int j) {
+        const int gi = wave_id + k * total_waves;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = min(gi * R + r, a.N - 1);
+            const u32x4_t *pg = reinterpret_cast<const u32x4_t *>(a.qg + (size_t)n * a.K);
+            const u32x4_t *pu = reinterpret_cast<const u32x4_t *>(a.qu + (size_t)n * a.K);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = min(j * G + kWave * u + lane, a.C16 - 1);
+                f.g[u][r] = load_stream(pg + c);
+                f.u[u][r] = load_stream(pu + c);
+            }
+            f.sg[r] = a.sg[n];
+            f.su[r] = a.su[n];
+        }
+    };
+    auto compute = [&](const Buf &f, int j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = j * G + kWave * u + lane;
+            const bool ok = c < a.C16;
+            const int cc = min(c, a.C16 - 1);  // unconditional reads, masked after
+            u32x4_t x0[B], x1[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                x0[b] = xs[b * a.C + 2 * cc];
+                x1[b] = xs[b * a.C + 2 * cc + 1];
+                if (!ok) x0[b] = x1[b] = zero;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                u32x4_t lo, hi;
+                e4m3x16_to_bf16(f.g[u][r], lo, hi);
+#pragma unroll
+                for (int b = 0; b < B; ++b) ag[r][b] = dot8_bf16(hi, x1[b], dot8_bf16(lo, x0[b], ag[r][b]));
+                e4m3x16_to_bf16(f.u[u][r], lo, hi);
+#pragma unroll
+                for (int b = 0; b < B; ++b) au[r][b] = dot8_bf16(hi, x1[b], dot8_bf16(lo, x0[b], au[r][b]));
+            }
+        }
+    };
+    auto finish = [&](const Buf &f, int k) {
+        const int gi = wave_id + k * total_waves;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                ag[r][b] = wave_sum_to_lane63(ag[r][b]);
+                au[r][b] = wave_sum_to_lane63(au[r][b]);
+            }
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int n = gi * R + r;
+                if (n < a.N)
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
+                        a.h[(size_t)b * a.N + n] = silu_mul(f.sg[r] * ag[r][b], f.su[r] * au[r][b]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) ag[r][b] = au[r][b] = 0.0f;
+    };
+    auto step = [&](const Buf &f, int k, int j) {
+        compute(f, j);
+        if (j == gpr - 1) finish(f, k);
+    };
+    auto next = [&](int &k, int &j) {
+        if (++j == gpr) {
+            j = 0;
+            ++k;
+        }
+    };
+    Buf f0, f1;
+    int k0 = 0, j0 = 0;
+    load(f0, k0, j0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_lds(xs, reinterpret_cast<const u32x4_t *>(a.x), B * a.C);
+    if (wave_id >= a.groups) return;
+    int t = 0;
+    for (; t + 2 < total; t += 2) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(f1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(f0, k0, j0);
+        int k2 = k1, j2 = j1;
+        next(k2, j2);
+        load(f0, k2, j2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(f1, k1, j1);
+        k0 = k2;
+        j0 = j2;
+    }
+    if (t + 1 < total) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(f1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(f0, k0, j0);
+        step(f1, k1, j1);
+    } else {
+        step(f0, k0, j0);
+    }
+}
+
+// Two E4M3 codes (the low or high half of a word) as two floats, exact.
+template <bool HI>
+__device__ __forceinline__ void e4m3x2_to_f32(uint32_t w, float &a, float &b) {
+    const auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    a = v[0];
+    b = v[1];
+}
+
+// K is cut into gridDim.y panels of CS weight chunks, each small enough that
+// its slice of h ([B][16 CS] fp32) sits in LDS; one panel writes y directly,
+// several write scaled fp32 partial sums that panel_reduce_kernel adds.
+template <int B, int R, int U>
+__global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, float *partial, int CS) {
+    extern __shared__ f32x4_t hs[];  // [B][4 CS]: this panel's h
+    constexpr int waves = kValuBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    const int total_waves = gridDim.x * waves;
+    const int panel = blockIdx.y, panels = gridDim.y;
+    const int c_lo = panel * CS;
+    const int cn = min(CS, a.C16 - c_lo);  // weight chunks in this panel
+    const int HC = a.K / 4;                // f32x4 chunks of a whole h row
+    const int HP = 4 * CS;                 // LDS pitch of a panel's h row
+    constexpr int G = kWave * U;
+    const int gpr = (cn + G - 1) / G;
+    const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
+    const int total = rows * gpr;
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    struct Buf {
+        u32x4_t w[U][R];
+        float s[R];
+    };
+    auto load = [&](Buf &f, int k, int j) {
+        const int gi = wave_id + k * total_waves;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = min(gi * R + r, a.M - 1);
+            const u32x4_t *pw = reinterpret_cast<const u32x4_t *>(a.qd + (size_t)m * a.K) + c_lo;
+#pragma unroll
+            for (int u = 0; u < U; ++u) f.w[u][r] = load_stream(pw + min(j * G + kWave * u + lane, cn - 1));
+            f.s[r] = a.sd[m];
+        }
+    };
+    auto compute = [&](const Buf &f, int j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = j * G + kWave * u + lane;
+            const bool ok = c < cn;
+            const int cc = min(c, cn - 1);
+            // 16 weights k = 16c .. 16c+15, in four quarters of four
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4_t hv[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    hv[b] = hs[(size_t)b * HP + 4 * cc + q];  // unconditional read, masked after
+                    if (!ok) hv[b] = fzero;
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t word = q == 0 ? f.w[u][r].x : q == 1 ? f.w[u][r].y : q == 2 ? f.w[u][r].z
+                                                                                                  : f.w[u][r].w;
+                    float w0, w1, w2, w3;
+                    e4m3x2_to_f32<false>(word, w0, w1);
+                    e4m3x2_to_f32<true>(word, w2, w3);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        float t = acc[r][b];
+                        t = fmaf(w0, hv[b].x, t);
+                        t = fmaf(w1, hv[b].y, t);
+                        t = fmaf(w2, hv[b].z, t);
+                        t = fmaf(w3, hv[b].w, t);
+                        acc[r][b] = t;
+                    }
+                }
+            }
+        }
+    };
+    auto finish = [&](const Buf &f, int k) {
+        const int gi = wave_id + k * total_waves;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = wave_sum_to_lane63(acc[r][b]);
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int m = gi * R + r;
+                if (m < a.M)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float v = f.s[r] * acc[r][b];
+                        if (panels == 1) a.y[(size_t)b * a.M + m] = to_bf16_rne(v);
+                        else partial[((size_t)panel * B + b) * a.M + m] = v;
+                    }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    };
+    auto step = [&](const Buf &f, int k, int j) {
+        compute(f, j);
+        if (j == gpr - 1) finish(f, k);
+    };
+    auto next = [&](int &k, int &j) {
+        if (++j == gpr) {
+            j = 0;
+            ++k;
+        }
+    };
+    Buf f0, f1;
+    int k0 = 0, j0 = 0;
+    load(f0, k0, j0);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    if (panels == 1) {
+        stage_lds(hs, hg, B * HC);  // all of h, contiguous
+    } else {
+        // this panel's slice of each of the B rows of h (4 cn chunks)
+        const int rc = 4 * cn;
+        constexpr int kBatch = 8;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const f32x4_t *src = hg + (size_t)b * HC + 4 * c_lo;
+            f32x4_t *dst = hs + (size_t)b * HP;
+            for (int base = threadIdx.x; base < rc; base += kBatch * kValuBlock) {
+                f32x4_t v[kBatch];
+#pragma unroll
+                for (int s = 0; s < kBatch; ++s)
+                    if (base + s * kValuBlock < rc) v[s] = src[base + s * kValuBlock];
+#pragma unroll
+                for (int s = 0; s < kBatch; ++s)
+                    if (base + s * kValuBlock < rc) dst[base + s * kValuBlock] = v[s];
+            }
+        }
+        __syncthreads();
+    }
+    if (wave_id >= a.groups) return;
+    int t = 0;
+    for (; t + 2 < total; t += 2) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(f1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(f0, k0, j0);
+        int k2 = k1, j2 = j1;
+        next(k2, j2);
+        load(f0, k2, j2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(f1, k1, j1);
+        k0 = k2;
+        j0 = j2;
+    }
+    if (t + 1 < total) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(f1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(f0, k0, j0);
+        step(f1, k1, j1);
+    } else {
+        step(f0, k0, j0);
+    }
+}
+
 // ============================================ persistent MLP (row, VALU) =====
 //
 // Both kernels of the MLP in one cooperative launch (every workgroup
@@ -2446,6 +2795,32 @@ static const KernelInfo kGuStaged8[kStMaxBT] = DFK_B_TABLE(gu_staged8);
 static const KernelInfo kDnStaged4[kStMaxBT] = DFK_B_TABLE(dn_staged4);
 static const KernelInfo kDnStaged8[kStMaxBT] = DFK_B_TABLE(dn_staged8);
 
+// FP8 row kernels: rows per work item (R) and 16-byte weight loads per lane
+// and row in one load group (U).
+#ifndef DFK_F8_GU_R
+#define DFK_F8_GU_R(B) 1
+#endif
+#ifndef DFK_F8_GU_U
+#define DFK_F8_GU_U(B) ((B) <= 2 ? 4 : 2)
+#endif
+#ifndef DFK_F8_DN_R
+#define DFK_F8_DN_R(B) ((B) <= 2 ? 2 : 4)
+#endif
+#ifndef DFK_F8_DN_U
+#define DFK_F8_DN_U(B) 2
+#endif
+template <int B> KernelInfo gu_f8_row() {
+    constexpr int R = DFK_F8_GU_R(B), U = DFK_F8_GU_U(B);
+    return {(const void *)gate_up_fp8_row_kernel<B, R, U>, R, kValuBlock, 1, 0};
+}
+template <int B> KernelInfo dn_f8_row() {
+    constexpr int R = DFK_F8_DN_R(B), U = DFK_F8_DN_U(B);
+    return {(const void *)down_fp8_row_kernel<B, R, U>, R, kValuBlock, 1, 0};
+}
+#define DFK_B4_TABLE(F) {F<1>(), F<2>(), F<3>(), F<4>()}
+static const KernelInfo kGuF8Row[kF8MaxBatch] = DFK_B4_TABLE(gu_f8_row);
+static const KernelInfo kDnF8Row[kF8MaxBatch] = DFK_B4_TABLE(dn_f8_row);
+
 // The persistent MLP kernel per batch: its gate-up and down row counts per
 // work item.
 #ifndef DFK_MLP_DN_R
@@ -2663,6 +3038,81 @@ hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gat
     GridBarrier bar{barrier};
     void *argv[] = {&ga, &da, &bar};
     return hipLaunchCooperativeKernel(p.fn, dim3(p.grid), dim3(p.block), argv, (unsigned)p.lds_bytes, stream);
+}
+
+bool make_fp8_plan(Op op, int B, int d_model, int d_ff, int cus, Plan *out) {
+    if (B < 1 || B > kF8MaxBatch || d_model < 16 || d_ff < 16 || (d_model % 16) || (d_ff % 16) || cus < 1)
+        return false;
+    const bool gu = (op == OP_GATE_UP);
+    Plan q{};
+    q.op = op;
+    q.engine = ENGINE_VALU;
+    q.trav = TRAV_ROW;
+    q.B = B;
+    q.rows = gu ? d_ff : d_model;
+    q.K = gu ? d_model : d_ff;
+    q.splits = 1;
+    q.chunks_per_split = q.K / 16;
+    KernelInfo ki{};
+    if (gu) {
+        ki = kGuF8Row[B - 1];
+        q.lds_bytes = (size_t)B * d_model * 2;  // x
+        if (q.lds_bytes > kLdsLimit) return false;
+        q.kind = KIND_GU_FP8_ROW;
+    } else {
+        // h in LDS, K cut into the fewest panels whose h slice fits
+        const long c16 = q.K / 16;
+        const long max_cs = std::max(1L, (long)(kHLdsLimit / ((size_t)B * 64)));
+        const long S = ceil_div(c16, max_cs);
+        const long cs = ceil_div(c16, S);
+        q.splits = (int)ceil_div(c16, cs);
+        q.chunks_per_split = (int)cs;
+        q.partial_floats = q.splits > 1 ? (size_t)q.splits * B * q.rows : 0;
+        q.h_in_lds = true;
+        ki = kDnF8Row[B - 1];
+        q.lds_bytes = (size_t)B * cs * 64;
+        q.kind = KIND_DN_FP8_ROW;
+    }
+    q.block = ki.block;
+    q.rows_per_group = ki.rows_per_group;
+    q.groups = (int)ceil_div(q.rows, ki.rows_per_group);
+    // persistent, balanced: every wave of a panel gets the same number of row
+    // groups (the panels share the resident waves)
+    const long waves = std::max(1L, (long)cus * blocks_per_cu(ki.fn, q.block, q.lds_bytes) * (q.block / kWave) /
+                                        q.splits);
+    const long per_wave = ceil_div((long)q.groups, waves);
+    q.grid = (int)std::max(1L, ceil_div(ceil_div((long)q.groups, per_wave), q.block / kWave));
+    q.fn = ki.fn;
+    *out = q;
+    return true;
+}
+
+hipError_t launch_gate_up_fp8(const Plan &p, const uint16_t *x, const uint8_t *q_gate, const float *s_gate,
+                              const uint8_t *q_up, const float *s_up, float *h, hipStream_t stream) {
+    if (p.kind != KIND_GU_FP8_ROW) return hipErrorInvalidValue;
+    GateUpF8Args a{};
+    a.x = x; a.qg = q_gate; a.qu = q_up; a.sg = s_gate; a.su = s_up; a.h = h;
+    a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.C16 = p.K / 16; a.groups = p.groups;
+    void *argv[] = {&a};
+    return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+}
+
+hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down, const float *s_down, uint16_t *y,
+                           float *partial, hipStream_t stream) {
+    if (p.kind != KIND_DN_FP8_ROW) return hipErrorInvalidValue;
+    if (p.splits > 1 && !partial) return hipErrorInvalidValue;
+    DownF8Args a{};
+    a.h = h; a.qd = q_down; a.sd = s_down; a.y = y;
+    a.B = p.B; a.K = p.K; a.M = p.rows; a.C16 = p.K / 16; a.groups = p.groups;
+    int cs = p.chunks_per_split;
+    void *argv[] = {&a, &partial, &cs};
+    hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid, p.splits), dim3(p.block), argv, p.lds_bytes, stream);
+    if (e != hipSuccess || p.splits == 1) return e;
+    int S = p.splits, n = p.B * p.rows;
+    const float *cpartial = partial;
+    void *rargv[] = {&cpartial, &y, &S, &n};
+    return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256), rargv,
+                           0, stream);
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,

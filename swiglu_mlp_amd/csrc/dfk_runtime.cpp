@@ -44,6 +44,7 @@ int log_level() {
 // ------------------------------------------------------------ validation --
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 dfk_status_t check_dims(int B, int d_model, int d_ff) {
     if (B < 1 || d_model < 1 || d_ff < 1) return DFK_ERR_INVALID_ARG;
@@ -841,6 +842,96 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
             if (dfk::launch_gate_up(pg, xn, W_gate, W_up, h, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         }
         if (dfk::launch_down(pd, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+// FP8 plans: the VALU row kernels (AUTO, ROW and ROW_VALU all mean them).
+static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int dev, Plan *p) {
+    if (layout != DFK_LAYOUT_AUTO && layout != DFK_LAYOUT_ROW && layout != DFK_LAYOUT_ROW_VALU)
+        return DFK_ERR_UNSUPPORTED;
+    if (!dfk::make_fp8_plan(op, B, d_model, d_ff, device_cus(dev), p)) return DFK_ERR_UNSUPPORTED;
+    log_plan(op == dfk::OP_GATE_UP ? "gate_up_fp8" : "down_fp8", *p);
+    return DFK_OK;
+}
+
+dfk_status_t dfk_gate_up_silu_mul_fp8(const uint16_t *x, const uint8_t *Wq_gate, const float *s_gate,
+                                      const uint8_t *Wq_up, const float *s_up, float *h, int B, int d_model,
+                                      int d_ff, dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!x || !Wq_gate || !s_gate || !Wq_up || !s_up || !h || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(Wq_gate) || !aligned16(Wq_up) || !aligned16(h) || !aligned4(s_gate) ||
+            !aligned4(s_up))
+            return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan p;
+        if ((st = fp8_plan(dfk::OP_GATE_UP, layout, B, d_model, d_ff, dev, &p)) != DFK_OK) return st;
+        if (dfk::launch_gate_up_fp8(p, x, Wq_gate, s_gate, Wq_up, s_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_down_proj_fp8(const float *h, const uint8_t *Wq_down, const float *s_down, uint16_t *out, int B,
+                               int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!h || !Wq_down || !s_down || !out || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(h) || !aligned16(Wq_down) || !aligned16(out) || !aligned4(s_down)) return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan p;
+        if ((st = fp8_plan(dfk::OP_DOWN, layout, B, d_model, d_ff, dev, &p)) != DFK_OK) return st;
+        float *partial = nullptr;
+        Slot *slot = nullptr;
+        std::unique_lock<std::mutex> lock;
+        if (p.partial_floats) {
+            slot = slot_for(dev, stream);
+            lock = std::unique_lock<std::mutex>(slot->mu);
+            void *ws = nullptr;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            partial = static_cast<float *>(ws);
+        }
+        if (dfk::launch_down_fp8(p, h, Wq_down, s_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_swiglu_mlp_fp8(const uint16_t *x, const uint8_t *Wq_gate, const float *s_gate,
+                                const uint8_t *Wq_up, const float *s_up, const uint8_t *Wq_down,
+                                const float *s_down, uint16_t *out, int B, int d_model, int d_ff,
+                                dfk_layout_t layout, hipStream_t stream) {
+    try {
+        if (!x || !Wq_gate || !s_gate || !Wq_up || !s_up || !Wq_down || !s_down || !out || !valid_layout(layout))
+            return DFK_ERR_INVALID_ARG;
+        dfk_status_t st = check_dims(B, d_model, d_ff);
+        if (st != DFK_OK) return st;
+        if (!aligned16(x) || !aligned16(Wq_gate) || !aligned16(Wq_up) || !aligned16(Wq_down) || !aligned16(out) ||
+            !aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))
+            return DFK_ERR_MISALIGNED;
+        int dev;
+        if ((st = current_device(&dev)) != DFK_OK) return st;
+        Plan pg, pd;
+        if ((st = fp8_plan(dfk::OP_GATE_UP, layout, B, d_model, d_ff, dev, &pg)) != DFK_OK) return st;
+        if ((st = fp8_plan(dfk::OP_DOWN, layout, B, d_model, d_ff, dev, &pd)) != DFK_OK) return st;
+        Slot *slot = slot_for(dev, stream);
+        std::lock_guard<std::mutex> lock(slot->mu);
+        void *ws = nullptr;
+        const size_t h_bytes = round256((size_t)B * d_ff * sizeof(float));
+        if ((st = ensure_workspace(slot, h_bytes + pd.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+        float *h = static_cast<float *>(ws);
+        float *partial = pd.partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
+        if (dfk::launch_gate_up_fp8(pg, x, Wq_gate, s_gate, Wq_up, s_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
+        if (dfk::launch_down_fp8(pd, h, Wq_down, s_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
         return DFK_OK;
     } catch (...) {
         return DFK_ERR_HIP;

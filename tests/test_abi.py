@@ -31,7 +31,7 @@ def L():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dfk_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dfk_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_exported_set():
@@ -83,6 +83,36 @@ def gu_packed(L, x=A, wgu=A, h=A, B=1, dm=256, dff=688, packing=0, layout=0):
 
 def mlp_packed(L, x=A, wgu=A, wd=A, out=A, B=1, dm=256, dff=688, packing=1, layout=0):
     return L.dfk_swiglu_mlp_packed(x, wgu, wd, out, B, dm, dff, packing, layout, None)
+
+
+def gu_fp8(L, x=A, qg=A, sg=A, qu=A, su=A, h=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_gate_up_silu_mul_fp8(x, qg, sg, qu, su, h, B, dm, dff, layout, None)
+
+
+def down_fp8(L, h=A, qd=A, sd=A, out=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_down_proj_fp8(h, qd, sd, out, B, dm, dff, layout, None)
+
+
+def mlp_fp8(L, x=A, qg=A, sg=A, qu=A, su=A, qd=A, sd=A, out=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_swiglu_mlp_fp8(x, qg, sg, qu, su, qd, sd, out, B, dm, dff, layout, None)
+
+
+FP8_FNS = [gu_fp8, down_fp8, mlp_fp8]
+
+
+@pytest.mark.parametrize("fn", FP8_FNS, ids=["gu_fp8", "down_fp8", "mlp_fp8"])
+def test_fp8_invalid_arguments(L, fn):
+    import inspect
+    params = inspect.signature(fn).parameters
+    for p in [p for p in params if p in ("x", "qg", "qu", "qd", "h", "out")]:
+        assert fn(L, **{p: NULL}) == Status.INVALID_ARG, p
+        assert fn(L, **{p: MIS}) == Status.MISALIGNED, p
+    for p in [p for p in params if p in ("sg", "su", "sd")]:
+        assert fn(L, **{p: NULL}) == Status.INVALID_ARG, p
+        assert fn(L, **{p: A + 2}) == Status.MISALIGNED, p
+    assert fn(L, B=0) == Status.INVALID_ARG
+    assert fn(L, B=257) == Status.UNSUPPORTED
+    assert fn(L, layout=8) == Status.INVALID_ARG
 
 
 def rmsnorm(L, x=A, gain=A, eps=1e-5, out=A, B=1, dm=256):
