@@ -41,7 +41,8 @@ enum Kind {
     KIND_DN_MFMA_STAGED = 13,  // down, the same, K split across workgroups + a reduce kernel
     KIND_DN_MFMA_COOP = 15,    // down ROW (B <= 16), workgroup-cooperative LDS weight tile
     KIND_GU_FP8_ROW = 16,      // gate-up over FP8 E4M3 weights + row scales, VALU row walk
-    KIND_DN_FP8_ROW = 17       // down, the same
+    KIND_DN_FP8_ROW = 17,      // down, the same
+    KIND_DN_VALU_PANEL = 18    // down VALU row walk over K panels whose h fits in LDS + a reduce kernel
 };
 
 // A fully resolved launch: which kernel and how the weight matrix is cut.

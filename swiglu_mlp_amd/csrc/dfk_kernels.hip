@@ -1138,6 +1138,163 @@ __global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, 
     }
 }
 
+// ================================================ down, VALU row K panels ====
+//
+// The down row walk for batches whose fp32 h does not fit in LDS whole: K is
+// cut into gridDim.y panels of CS 16-byte weight chunks whose h slice
+// ([B][8 CS] fp32) does; each panel's waves walk their rows over the panel
+// only and write fp32 partial sums that panel_reduce_kernel adds (fixed
+// order).  h is read from LDS, never through the caches.
+template <int B, int R, int U>
+__global__ __launch_bounds__(kValuBlock) void down_valu_panel_kernel(DownArgs a, float *partial, int CS) {
+    extern __shared__ f32x4_t hs[];  // [B][2 CS]: this panel's h
+    constexpr int waves = kValuBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
+    const int total_waves = gridDim.x * waves;
+    const int panel = blockIdx.y;
+    const int c_lo = panel * CS;
+    const int cn = min(CS, a.C - c_lo);  // weight chunks in this panel
+    const int HC = 2 * a.C;              // f32x4 chunks of a whole h row
+    const int HP = 2 * CS;               // LDS pitch of a panel's h row
+    constexpr int G = kWave * U;
+    const int gpr = (cn + G - 1) / G;
+    const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
+    const int total = rows * gpr;
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    auto load = [&](u32x4_t (&wv)[U][R], int k, int j) {
+        const int gi = wave_id + k * total_waves;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = min(gi * R + r, a.M - 1);
+            const u32x4_t *pw = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K) + c_lo;
+#pragma unroll
+            for (int u = 0; u < U; ++u) wv[u][r] = load_stream(pw + min(j * G + kWave * u + lane, cn - 1));
+        }
+    };
+    auto compute = [&](const u32x4_t (&wv)[U][R], int j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = j * G + kWave * u + lane;
+            const bool ok = c < cn;
+            const int cc = min(c, cn - 1);
+            f32x4_t h2[B][2];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                h2[b][0] = hs[(size_t)b * HP + 2 * cc];  // unconditional reads, masked after
+                h2[b][1] = hs[(size_t)b * HP + 2 * cc + 1];
+                if (!ok) h2[b][0] = h2[b][1] = fzero;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const u32x4_t w = wv[u][r];
+                const float w0 = bf16_lo(w.x), w1 = bf16_hi(w.x), w2 = bf16_lo(w.y), w3 = bf16_hi(w.y),
+                            w4 = bf16_lo(w.z), w5 = bf16_hi(w.z), w6 = bf16_lo(w.w), w7 = bf16_hi(w.w);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const f32x4_t h0 = h2[b][0], h1 = h2[b][1];
+                    float t = acc[r][b];
+                    t = fmaf(w0, h0.x, t);
+                    t = fmaf(w1, h0.y, t);
+                    t = fmaf(w2, h0.z, t);
+                    t = fmaf(w3, h0.w, t);
+                    t = fmaf(w4, h1.x, t);
+                    t = fmaf(w5, h1.y, t);
+                    t = fmaf(w6, h1.z, t);
+                    t = fmaf(w7, h1.w, t);
+                    acc[r][b] = t;
+                }
+            }
+        }
+    };
+    auto finish = [&](int k) {
+        const int gi = wave_id + k * total_waves;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = wave_sum_to_lane63(acc[r][b]);
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int m = gi * R + r;
+                if (m < a.M)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) partial[((size_t)panel * B + b) * a.M + m] = acc[r][b];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    };
+    auto step = [&](const u32x4_t (&wv)[U][R], int k, int j) {
+        compute(wv, j);
+        if (j == gpr - 1) finish(k);
+    };
+    auto next = [&](int &k, int &j) {
+        if (++j == gpr) {
+            j = 0;
+            ++k;
+        }
+    };
+    u32x4_t w0[U][R], w1[U][R];
+    int k0 = 0, j0 = 0;
+    load(w0, k0, j0);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        // this panel's slice of each of the B rows of h (2 cn chunks)
+        const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+        const int rc = 2 * cn;
+        constexpr int kBatch = 8;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const f32x4_t *src = hg + (size_t)b * HC + 2 * c_lo;
+            f32x4_t *dst = hs + (size_t)b * HP;
+            for (int base = threadIdx.x; base < rc; base += kBatch * kValuBlock) {
+                f32x4_t v[kBatch];
+#pragma unroll
+                for (int s = 0; s < kBatch; ++s)
+                    if (base + s * kValuBlock < rc) v[s] = src[base + s * kValuBlock];
+#pragma unroll
+                for (int s = 0; s < kBatch; ++s)
+                    if (base + s * kValuBlock < rc) dst[base + s * kValuBlock] = v[s];
+            }
+        }
+        __syncthreads();
+    }
+    if (wave_id >= a.groups) return;
+    int t = 0;
+    for (; t + 2 < total; t += 2) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(w1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(w0, k0, j0);
+        int k2 = k1, j2 = j1;
+        next(k2, j2);
+        load(w0, k2, j2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(w1, k1, j1);
+        k0 = k2;
+        j0 = j2;
+    }
+    if (t + 1 < total) {
+        int k1 = k0, j1 = j0;
+        next(k1, j1);
+        load(w1, k1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(w0, k0, j0);
+        step(w1, k1, j1);
+    } else {
+        step(w0, k0, j0);
+    }
+}
+
 // ============================================ persistent MLP (row, VALU) =====
 //
 // Both kernels of the MLP in one cooperative launch (every workgroup
@@ -2537,7 +2694,7 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #define DFK_GU_VALU_R(B) 1
 #endif
 #ifndef DFK_GU_VALU_U
-#define DFK_GU_VALU_U(B) 4
+#define DFK_GU_VALU_U(B) ((B) == 4 ? 3 : 4)
 #endif
 #ifndef DFK_DN_VALU_R
 #define DFK_DN_VALU_R(B) ((B) <= 2 ? 2 : 4)
@@ -2686,6 +2843,13 @@ template <int B, bool HLDS> KernelInfo dn_valu_col_t() {
     constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
     return {(const void *)down_valu_col_kernel<B, R, U, HLDS>, R, kValuBlock, kValuBlock / kWave, R * B};
 }
+#ifndef DFK_DN_PANEL_VALU_U
+#define DFK_DN_PANEL_VALU_U(B) 2
+#endif
+template <int B> KernelInfo dn_valu_panel() {
+    constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_PANEL_VALU_U(B);
+    return {(const void *)down_valu_panel_kernel<B, R, U>, R, kValuBlock, 1, 0};
+}
 template <int B> KernelInfo dn_valu_row() { return dn_valu_row_t<B, false>(); }
 template <int B> KernelInfo dn_valu_row_lds() { return dn_valu_row_t<B, true>(); }
 template <int B> KernelInfo dn_valu_col() { return dn_valu_col_t<B, false>(); }
@@ -2779,6 +2943,7 @@ static const KernelInfo kDnValuRow[kValuMaxBatch] = DFK_B_TABLE(dn_valu_row);
 static const KernelInfo kDnValuRowLds[kValuMaxBatch] = DFK_B_TABLE(dn_valu_row_lds);
 static const KernelInfo kDnValuCol[kValuMaxBatch] = DFK_B_TABLE(dn_valu_col);
 static const KernelInfo kDnValuColLds[kValuMaxBatch] = DFK_B_TABLE(dn_valu_col_lds);
+static const KernelInfo kDnValuPanel[kValuMaxBatch] = DFK_B_TABLE(dn_valu_panel);
 static const KernelInfo kGuMfmaRow[kMaxBT] = DFK_BT_TABLE(gu_mfma_row);
 static const KernelInfo kDnMfmaRow[kMaxBT] = DFK_BT_TABLE(dn_mfma_row);
 static const KernelInfo kGuMfmaCol[kMaxBT] = DFK_BT_TABLE(gu_mfma_col);
@@ -2886,6 +3051,30 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             if (q.lds_bytes > kLdsLimit) return false;
             q.fused_norm = norm;
             q.kind = row ? KIND_GU_VALU_ROW : KIND_GU_VALU_COL;
+        } else if (row && (size_t)B * q.K * 4 > DFK_HLDS_LIMIT) {
+            // h does not fit in LDS whole: cut K into the fewest panels whose h
+            // slice does (32 bytes per weight chunk and batch row), partial
+            // sums added by the reduce kernel
+            const long C = q.K / 8;
+            const long max_cs = std::max(1L, (long)(DFK_HLDS_LIMIT / ((size_t)B * 32)));
+            const long cs = ceil_div(C, ceil_div(C, max_cs));
+            const KernelInfo pk = kDnValuPanel[B - 1];
+            q.kind = KIND_DN_VALU_PANEL;
+            q.splits = (int)ceil_div(C, cs);
+            q.chunks_per_split = (int)cs;
+            q.partial_floats = (size_t)q.splits * B * q.rows;
+            q.h_in_lds = true;
+            q.lds_bytes = (size_t)B * cs * 32;
+            q.block = pk.block;
+            q.rows_per_group = pk.rows_per_group;
+            q.groups = (int)ceil_div(q.rows, pk.rows_per_group);
+            const long waves = std::max(1L, (long)cus * blocks_per_cu(pk.fn, q.block, q.lds_bytes) *
+                                                (q.block / kWave) / q.splits);
+            const long per_wave = ceil_div((long)q.groups, waves);
+            q.grid = (int)std::max(1L, ceil_div(ceil_div((long)q.groups, per_wave), q.block / kWave));
+            q.fn = pk.fn;
+            *out = q;
+            return true;
         } else {
             // keep all of h in LDS when it is small, else read it through the caches
             const size_t whole = (size_t)B * q.K * 4;
@@ -3146,6 +3335,18 @@ hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, ui
     DownArgs a;
     a.h = h; a.wd = w_down; a.y = y;
     a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.groups = p.groups;
+    if (p.kind == KIND_DN_VALU_PANEL) {
+        if (!partial) return hipErrorInvalidValue;
+        int cs = p.chunks_per_split;
+        void *argv[] = {&a, &partial, &cs};
+        hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid, p.splits), dim3(p.block), argv, p.lds_bytes, stream);
+        if (e != hipSuccess) return e;
+        int S = p.splits, n = p.B * p.rows;
+        const float *cpartial = partial;
+        void *rargv[] = {&cpartial, &y, &S, &n};
+        return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256),
+                               rargv, 0, stream);
+    }
     if (p.kind != KIND_DN_MFMA_PANEL && p.kind != KIND_DN_MFMA_STAGED) {
         void *argv[] = {&a};
         return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);

@@ -82,6 +82,9 @@ SMALL_SHAPES = [
     # (shifted last stages), a two-way K split with a short last split, and a
     # ragged last row tile
     (2, 4104, 264), (4, 264, 4104), (5, 600, 1096), (16, 1032, 2056),
+    # h past the LDS limit: the vector-ALU down walk over K panels (2, 2 and
+    # 5 panels, ragged last panel)
+    (3, 136, 11008), (8, 64, 4112), (5, 264, 28680),
 ]
 
 
