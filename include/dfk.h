@@ -179,7 +179,7 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * half the bytes of bf16 and are widened in registers; each row's fp32 sum is
  * multiplied by its scale once.  The computed h and out are those of the bf16
  * entry points over the dequantized weights (to fp32 summation order).
- * Limits beyond the shared ones: 1 <= B <= 4, d_model and d_ff multiples of
+ * Limits beyond the shared ones: 1 <= B <= 8, d_model and d_ff multiples of
  * 16, B * d_model * 2 <= 160 KiB; DFK_ERR_UNSUPPORTED otherwise.  Layouts:
  * AUTO, ROW and ROW_VALU (all the vector-ALU row walk); the others are
  * DFK_ERR_UNSUPPORTED.  Code and tensor pointers must be 16-byte aligned,

@@ -2972,7 +2972,7 @@ static const KernelInfo kDnStaged8[kStMaxBT] = DFK_B_TABLE(dn_staged8);
 #define DFK_F8_DN_R(B) ((B) <= 2 ? 2 : 4)
 #endif
 #ifndef DFK_F8_DN_U
-#define DFK_F8_DN_U(B) 2
+#define DFK_F8_DN_U(B) ((B) <= 4 ? 2 : 1)
 #endif
 template <int B> KernelInfo gu_f8_row() {
     constexpr int R = DFK_F8_GU_R(B), U = DFK_F8_GU_U(B);
@@ -2982,9 +2982,8 @@ template <int B> KernelInfo dn_f8_row() {
     constexpr int R = DFK_F8_DN_R(B), U = DFK_F8_DN_U(B);
     return {(const void *)down_fp8_row_kernel<B, R, U>, R, kValuBlock, 1, 0};
 }
-#define DFK_B4_TABLE(F) {F<1>(), F<2>(), F<3>(), F<4>()}
-static const KernelInfo kGuF8Row[kF8MaxBatch] = DFK_B4_TABLE(gu_f8_row);
-static const KernelInfo kDnF8Row[kF8MaxBatch] = DFK_B4_TABLE(dn_f8_row);
+static const KernelInfo kGuF8Row[kF8MaxBatch] = DFK_B_TABLE(gu_f8_row);
+static const KernelInfo kDnF8Row[kF8MaxBatch] = DFK_B_TABLE(dn_f8_row);
 
 // The persistent MLP kernel per batch: its gate-up and down row counts per
 // work item.
