@@ -270,7 +270,7 @@ def fp8_mlp_bytes(B, d_model=D_MODEL, d_ff=D_FF):
     return 3 * d_model * d_ff + 4 * (2 * d_ff + d_model) + 2 * B * d_model + 2 * 4 * B * d_ff + 2 * B * d_model
 
 
-def time_fp8(device, batches=(1, 2, 3, 4, 8), steps=300, warmup=30, rotate=8):
+def time_fp8(device, batches=(1, 2, 4, 8, 16, 64), steps=300, warmup=30, rotate=8):
     """Context: the MLP over weight-only FP8 weights (E4M3 codes + per-row
     fp32 scales) at the 8B shape, `rotate` weight sets (2.8 GB) so every call
     streams from HBM: us per call and HBM roofline fraction of the codes."""

@@ -179,11 +179,17 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * half the bytes of bf16 and are widened in registers; each row's fp32 sum is
  * multiplied by its scale once.  The computed h and out are those of the bf16
  * entry points over the dequantized weights (to fp32 summation order).
- * Limits beyond the shared ones: 1 <= B <= 8, d_model and d_ff multiples of
- * 16, B * d_model * 2 <= 160 KiB; DFK_ERR_UNSUPPORTED otherwise.  Layouts:
- * AUTO, ROW and ROW_VALU (all the vector-ALU row walk); the others are
- * DFK_ERR_UNSUPPORTED.  Code and tensor pointers must be 16-byte aligned,
- * scale pointers 4-byte aligned.
+ * Engines: the vector-ALU row walk (B <= 8; x kept in LDS, so
+ * B * d_model * 2 <= 160 KiB) and the LDS-transposed matrix-core kernels
+ * (B <= 128), which widen the codes to bf16 on their way into LDS.  Layouts:
+ * AUTO = the measured best at the Llama-3-8B layer shape (gate-up: vector
+ * ALU to B = 3, matrix-core column traversal to B = 16, row traversal above;
+ * down: vector ALU to B = 4, matrix-core column traversal above); ROW =
+ * vector ALU up to B = 8, else matrix cores; COL = matrix
+ * cores; ROW_VALU, ROW_MFMA, COL_MFMA force the engine; COL_VALU and
+ * ROW_PERSISTENT are DFK_ERR_UNSUPPORTED.  d_model and d_ff must be
+ * multiples of 16.  Code and tensor pointers must be 16-byte aligned, scale
+ * pointers 4-byte aligned.
  */
 dfk_status_t dfk_gate_up_silu_mul_fp8(const uint16_t *x, const uint8_t *Wq_gate, const float *s_gate,
                                       const uint8_t *Wq_up, const float *s_up, float *h, int B,

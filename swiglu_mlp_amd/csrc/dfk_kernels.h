@@ -93,10 +93,11 @@ hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_ga
 // xn [B][K] = the RMS normalization of x [B][K] (one workgroup per batch row).
 hipError_t launch_rmsnorm(const uint16_t *x, const NormArgs &norm, uint16_t *xn, int B, int K,
                           hipStream_t stream);
-// Weight-only FP8 (E4M3 codes, one fp32 scale per weight row): VALU row
-// kernels, B <= kF8MaxBatch, d_model and d_ff multiples of 16.
+// Weight-only FP8 (E4M3 codes, one fp32 scale per weight row), d_model and
+// d_ff multiples of 16: VALU row kernels (ROW only, B <= kF8MaxBatch) or the
+// LDS-transposed matrix-core kernels (ROW or COL, B <= 128).
 constexpr int kF8MaxBatch = 8;
-bool make_fp8_plan(Op op, int B, int d_model, int d_ff, int cus, Plan *plan);
+bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *plan);
 hipError_t launch_gate_up_fp8(const Plan &p, const uint16_t *x, const uint8_t *q_gate, const float *s_gate,
                               const uint8_t *q_up, const float *s_up, float *h, hipStream_t stream);
 // `partial` must hold p.partial_floats floats when that is non-zero (K cut

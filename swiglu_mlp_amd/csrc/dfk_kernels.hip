@@ -137,6 +137,8 @@ struct GateUpArgs {
     int C;        // 16-byte chunks per weight row (K / 8)
     int groups;   // work items: row groups (ROW: per wave, COL: per workgroup)
     int ldw;      // elements from one row of W_gate (and of W_up) to the next: K, or 2K row-interleaved
+    const uint8_t *qg, *qu;  // FP8-weight matrix-core kernels: E4M3 codes [N][K]
+    const float *sg, *su;    //   and row scales [N]
     const uint16_t *gain;  // RMS normalization (NORM kernels only): gain [d_model]
     double eps;            //   and epsilon
 };
@@ -147,6 +149,8 @@ struct DownArgs {
     uint16_t *y;
     int B, K, M;  // batch, d_ff, d_model
     int C, groups;
+    const uint8_t *qd;  // FP8-weight matrix-core kernels: E4M3 codes [M][K]
+    const float *sd;    //   and row scales [M]
 };
 
 // ================================================== VALU building blocks ==
@@ -1719,6 +1723,47 @@ template <int KBC> struct Lt {
     }
 };
 
+// The same LDS tile filled from FP8 E4M3 codes: one 16-byte load carries 16
+// codes (two bf16 chunks), so a row of a block takes KBC / 2 lanes and an
+// instruction covers 64 / (KBC / 2) rows; the codes are widened to bf16
+// (exactly) on the way into LDS.  C counts bf16 chunks (K / 8) as for Lt.
+template <int KBC> struct Lt8 {
+    static constexpr int kC8 = KBC / 2;
+    static constexpr int kRowsPerInst = 64 / kC8;
+    static constexpr int kInsts = 16 / kRowsPerInst;
+    static constexpr int kPitch = KBC + 1;
+    static constexpr int kTile = 16 * kPitch;
+    static constexpr int kSteps = KBC / 4;
+
+    static __device__ __forceinline__ void load(u32x4_t (&v)[kInsts], const uint8_t *q, int K, int C, int row0,
+                                                int rows, int kb, int lane) {
+        const int c = min(kb * kC8 + lane % kC8, C / 2 - 1);
+#pragma unroll
+        for (int i = 0; i < kInsts; ++i) {
+            const int row = min(row0 + i * kRowsPerInst + lane / kC8, rows - 1);
+            v[i] = load_stream(reinterpret_cast<const u32x4_t *>(q + (size_t)row * K) + c);
+        }
+    }
+    static __device__ __forceinline__ void store(u32x4_t *lt, const u32x4_t (&v)[kInsts], int kb, int C, int lane) {
+        const bool ok = kb * kC8 + lane % kC8 < C / 2;
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kInsts; ++i) {
+            u32x4_t lo, hi;
+            e4m3x16_to_bf16(v[i], lo, hi);
+            u32x4_t *dst = lt + (i * kRowsPerInst + lane / kC8) * kPitch + 2 * (lane % kC8);
+            dst[0] = ok ? lo : zero;
+            dst[1] = ok ? hi : zero;
+        }
+    }
+    static __device__ __forceinline__ bf16x8_t frag(const u32x4_t *lt, int j, int lr, int lq) {
+        return as_bf16x8(lt[lr * kPitch + 4 * j + lq]);
+    }
+};
+
+template <bool C, class A, class B> struct Pick { using T = A; };
+template <class A, class B> struct Pick<false, A, B> { using T = B; };
+
 // The B operand (x, or h as bf16 hi + lo) is read as MFMA B fragments straight
 // from global memory (it is small and L2-resident).  Loads return in issue
 // order, so a fragment load issued after the next weight block would make the
@@ -1727,9 +1772,10 @@ template <int KBC> struct Lt {
 // otherwise one step ahead.  Fragment reads are never predicated: rows past B
 // read row B - 1 (their output columns are dropped) and chunks past the row
 // end read the last chunk, masked to zero in the tail block only.
-template <int BT, int KSPLIT, int WAVES>
+// F8: the weights are FP8 codes (a.qg, a.qu) with row scales (a.sg, a.su).
+template <int BT, int KSPLIT, int WAVES, bool F8 = false>
 __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpArgs a) {
-    using L = Lt<32>;
+    using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
     constexpr int KBC = 32;
     constexpr bool kPre = BT <= 2;
     constexpr int XS = kPre ? L::kSteps : 2;
@@ -1760,6 +1806,15 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
         f32x4_t accg[BT], accu[BT];
 #pragma unroll
         for (int bt = 0; bt < BT; ++bt) accg[bt] = accu[bt] = f32x4_t{0, 0, 0, 0};
+        float scg[4], scu[4];  // F8: the scales of this lane's output rows, loaded ahead of the weights
+        if constexpr (F8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = min(row0 + 4 * lq + e, a.N - 1);
+                scg[e] = a.sg[n];
+                scu[e] = a.su[n];
+            }
+        }
 
         u32x4_t xf[XS][BT];
         auto load_x = [&](int kb, int j, u32x4_t (&xb)[BT]) {
@@ -1797,8 +1852,13 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
         if (active && kb_beg < kb_end) {
             u32x4_t vg0[L::kInsts], vu0[L::kInsts], vg1[L::kInsts], vu1[L::kInsts];
             auto load_w = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
-                L::load(vg, a.wg, a.ldw, a.C, row0, a.N, kb, lane);
-                L::load(vu, a.wu, a.ldw, a.C, row0, a.N, kb, lane);
+                if constexpr (F8) {
+                    L::load(vg, a.qg, a.K, a.C, row0, a.N, kb, lane);
+                    L::load(vu, a.qu, a.K, a.C, row0, a.N, kb, lane);
+                } else {
+                    L::load(vg, a.wg, a.ldw, a.C, row0, a.N, kb, lane);
+                    L::load(vu, a.wu, a.ldw, a.C, row0, a.N, kb, lane);
+                }
             };
             auto step = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
                 L::store(ltg, vg, kb, a.C, lane);
@@ -1863,7 +1923,10 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
                 if (b < a.B && n < a.N) {
                     f32x4_t o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (F8) o[e] = silu_mul(scg[e] * accg[bt][e], scu[e] * accu[bt][e]);
+                        else o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    }
                     *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
                 }
             }
@@ -1871,9 +1934,10 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
     }
 }
 
-template <int BT, int KSPLIT, int WAVES, int KBC>
+// F8: W_down is FP8 codes (a.qd) with row scales (a.sd).
+template <int BT, int KSPLIT, int WAVES, int KBC, bool F8 = false>
 __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a) {
-    using L = Lt<KBC>;
+    using L = typename Pick<F8, Lt8<KBC>, Lt<KBC>>::T;
     constexpr bool kPre = BT <= 1;
     constexpr int HS = kPre ? L::kSteps : 2;
     constexpr int TPW = WAVES / KSPLIT;
@@ -1902,6 +1966,11 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a)
         f32x4_t acc[BT];
 #pragma unroll
         for (int bt = 0; bt < BT; ++bt) acc[bt] = f32x4_t{0, 0, 0, 0};
+        float scd[4];  // F8: the scales of this lane's output rows, loaded ahead of the weights
+        if constexpr (F8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) scd[e] = a.sd[min(row0 + 4 * lq + e, a.M - 1)];
+        }
 
         f32x4_t hf[HS][BT][2];
         auto load_h = [&](int kb, int j, f32x4_t (&hb)[BT][2]) {
@@ -1948,19 +2017,23 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a)
             };
             // software pipeline, one weight block ahead, no conditional loads
             // in the steady loop
+            auto load_w = [&](u32x4_t (&v)[L::kInsts], int kb) {
+                if constexpr (F8) L::load(v, a.qd, a.K, a.C, row0, a.M, kb, lane);
+                else L::load(v, a.wd, a.K, a.C, row0, a.M, kb, lane);
+            };
             if constexpr (kPre) load_block(kb_beg);
-            L::load(v0, a.wd, a.K, a.C, row0, a.M, kb_beg, lane);
+            load_w(v0, kb_beg);
             int kb = kb_beg;
             for (; kb + 2 < kb_end; kb += 2) {
-                L::load(v1, a.wd, a.K, a.C, row0, a.M, kb + 1, lane);
+                load_w(v1, kb + 1);
                 step(v0, kb);
                 if constexpr (kPre) load_block(kb + 1);
-                L::load(v0, a.wd, a.K, a.C, row0, a.M, kb + 2, lane);
+                load_w(v0, kb + 2);
                 step(v1, kb + 1);
                 if constexpr (kPre) load_block(kb + 2);
             }
             if (kb + 1 < kb_end) {
-                L::load(v1, a.wd, a.K, a.C, row0, a.M, kb + 1, lane);
+                load_w(v1, kb + 1);
                 step(v0, kb);
                 if constexpr (kPre) load_block(kb + 1);
                 step(v1, kb + 1);
@@ -1995,8 +2068,13 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a)
             for (int bt = 0; bt < BT; ++bt) {
                 const int b = bt * 16 + lr;
                 if (b < a.B && m < a.M) {
-                    const unsigned lo = to_bf16_rne(acc[bt][0]) | ((unsigned)to_bf16_rne(acc[bt][1]) << 16);
-                    const unsigned hi = to_bf16_rne(acc[bt][2]) | ((unsigned)to_bf16_rne(acc[bt][3]) << 16);
+                    f32x4_t v = acc[bt];
+                    if constexpr (F8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] *= scd[e];
+                    }
+                    const unsigned lo = to_bf16_rne(v[0]) | ((unsigned)to_bf16_rne(v[1]) << 16);
+                    const unsigned hi = to_bf16_rne(v[2]) | ((unsigned)to_bf16_rne(v[3]) << 16);
                     *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
                 }
             }
@@ -2953,6 +3031,28 @@ static const KernelInfo kGuLtRow[kLtMaxBT] = DFK_B_TABLE(gu_lt_row);
 static const KernelInfo kGuLtCol[kLtMaxBT] = DFK_B_TABLE(gu_lt_col);
 static const KernelInfo kDnLtRow[kLtMaxBT] = DFK_B_TABLE(dn_lt_row);
 static const KernelInfo kDnLtCol[kLtMaxBT] = DFK_B_TABLE(dn_lt_col);
+
+// The LDS-transposed kernels over FP8 weights (codes widened on the way into LDS).
+template <int BT> KernelInfo gu_lt_row_f8() {
+    constexpr int W = DFK_LT_GU_ROW_WAVES(BT);
+    return {(const void *)gate_up_mfma_lt_kernel<BT, 1, W, true>, 16, W * kWave, 1, 2 * BT * 4};
+}
+template <int BT> KernelInfo gu_lt_col_f8() {
+    constexpr int W = DFK_LT_GU_WAVES(BT), KS = DFK_LT_GU_KSPLIT(BT);
+    return {(const void *)gate_up_mfma_lt_kernel<BT, KS, W, true>, 16, W * kWave, KS, 2 * BT * 4};
+}
+template <int BT> KernelInfo dn_lt_row_f8() {
+    constexpr int W = DFK_LT_DN_WAVES(BT);
+    return {(const void *)down_mfma_lt_kernel<BT, 1, W, DFK_LT_DN_KBC, true>, 16, W * kWave, 1, BT * 4};
+}
+template <int BT> KernelInfo dn_lt_col_f8() {
+    constexpr int W = DFK_LT_DN_WAVES(BT), KS = DFK_LT_DN_KSPLIT(BT);
+    return {(const void *)down_mfma_lt_kernel<BT, KS, W, DFK_LT_DN_KBC, true>, 16, W * kWave, KS, BT * 4};
+}
+static const KernelInfo kGuLtRowF8[kLtMaxBT] = DFK_B_TABLE(gu_lt_row_f8);
+static const KernelInfo kGuLtColF8[kLtMaxBT] = DFK_B_TABLE(gu_lt_col_f8);
+static const KernelInfo kDnLtRowF8[kLtMaxBT] = DFK_B_TABLE(dn_lt_row_f8);
+static const KernelInfo kDnLtColF8[kLtMaxBT] = DFK_B_TABLE(dn_lt_col_f8);
 constexpr int kStMaxBT = 8;
 // (waves_per_item holds the staged kernels' LDS buffer count)
 static const KernelInfo kGuStaged4[kStMaxBT] = DFK_B_TABLE(gu_staged4);
@@ -3228,10 +3328,40 @@ hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gat
     return hipLaunchCooperativeKernel(p.fn, dim3(p.grid), dim3(p.block), argv, (unsigned)p.lds_bytes, stream);
 }
 
-bool make_fp8_plan(Op op, int B, int d_model, int d_ff, int cus, Plan *out) {
-    if (B < 1 || B > kF8MaxBatch || d_model < 16 || d_ff < 16 || (d_model % 16) || (d_ff % 16) || cus < 1)
-        return false;
+bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out) {
+    if (B < 1 || d_model < 16 || d_ff < 16 || (d_model % 16) || (d_ff % 16) || cus < 1) return false;
     const bool gu = (op == OP_GATE_UP);
+    if (engine == ENGINE_MFMA) {
+        // the LDS-transposed matrix-core kernels, FP8 codes widened into LDS
+        const int BT = (int)ceil_div(B, 16);
+        if (BT > kLtMaxBT) return false;
+        const bool row = (trav == TRAV_ROW);
+        const KernelInfo ki = row ? (gu ? kGuLtRowF8 : kDnLtRowF8)[BT - 1] : (gu ? kGuLtColF8 : kDnLtColF8)[BT - 1];
+        Plan q{};
+        q.op = op;
+        q.engine = ENGINE_MFMA;
+        q.trav = trav;
+        q.B = B;
+        q.rows = gu ? d_ff : d_model;
+        q.K = gu ? d_model : d_ff;
+        q.splits = 1;
+        q.chunks_per_split = q.K / 8;
+        const int waves = ki.block / kWave;
+        q.lds_bytes = (size_t)waves * (gu ? 2 * Lt8<32>::kTile : Lt8<DFK_LT_DN_KBC>::kTile) * 16 +
+                      (ki.waves_per_item > 1 ? (size_t)waves * ki.nv * kWave * sizeof(float) : 0);
+        if (q.lds_bytes > kLdsLimit) return false;
+        q.kind = gu ? KIND_GU_MFMA_LT : KIND_DN_MFMA_LT;
+        q.block = ki.block;
+        q.rows_per_group = 16;
+        q.groups = (int)ceil_div(q.rows, 16);
+        const int occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
+        const long wg_items = ceil_div(q.groups, waves / ki.waves_per_item);
+        q.grid = (int)std::max(1L, std::min((long)cus * occ, wg_items));
+        q.fn = ki.fn;
+        *out = q;
+        return true;
+    }
+    if (trav != TRAV_ROW || B > kF8MaxBatch) return false;
     Plan q{};
     q.op = op;
     q.engine = ENGINE_VALU;
@@ -3277,6 +3407,13 @@ bool make_fp8_plan(Op op, int B, int d_model, int d_ff, int cus, Plan *out) {
 
 hipError_t launch_gate_up_fp8(const Plan &p, const uint16_t *x, const uint8_t *q_gate, const float *s_gate,
                               const uint8_t *q_up, const float *s_up, float *h, hipStream_t stream) {
+    if (p.kind == KIND_GU_MFMA_LT) {
+        GateUpArgs a{};
+        a.x = x; a.qg = q_gate; a.qu = q_up; a.sg = s_gate; a.su = s_up; a.h = h;
+        a.B = p.B; a.K = p.K; a.N = p.rows; a.C = p.K / 8; a.groups = p.groups; a.ldw = p.K;
+        void *argv[] = {&a};
+        return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    }
     if (p.kind != KIND_GU_FP8_ROW) return hipErrorInvalidValue;
     GateUpF8Args a{};
     a.x = x; a.qg = q_gate; a.qu = q_up; a.sg = s_gate; a.su = s_up; a.h = h;
@@ -3287,6 +3424,13 @@ hipError_t launch_gate_up_fp8(const Plan &p, const uint16_t *x, const uint8_t *q
 
 hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down, const float *s_down, uint16_t *y,
                            float *partial, hipStream_t stream) {
+    if (p.kind == KIND_DN_MFMA_LT) {
+        DownArgs a{};
+        a.h = h; a.qd = q_down; a.sd = s_down; a.y = y;
+        a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.groups = p.groups;
+        void *argv[] = {&a};
+        return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    }
     if (p.kind != KIND_DN_FP8_ROW) return hipErrorInvalidValue;
     if (p.splits > 1 && !partial) return hipErrorInvalidValue;
     DownF8Args a{};

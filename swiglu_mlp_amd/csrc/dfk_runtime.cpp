@@ -848,11 +848,37 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
     }
 }
 
-// FP8 plans: the VALU row kernels (AUTO, ROW and ROW_VALU all mean them).
+// FP8 plans.  AUTO (measured at the Llama-3-8B layer shape): gate-up on the
+// VALU row walk up to B = 3, the matrix cores' column traversal up to B = 16,
+// their row traversal above; down on the VALU row walk up to B = 4, the
+// matrix cores' column traversal above.  ROW: VALU up to B = 8, else the
+// matrix cores; COL: the matrix cores; *_VALU / *_MFMA force the engine
+// (there is no VALU column walk for FP8).
 static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int dev, Plan *p) {
-    if (layout != DFK_LAYOUT_AUTO && layout != DFK_LAYOUT_ROW && layout != DFK_LAYOUT_ROW_VALU)
-        return DFK_ERR_UNSUPPORTED;
-    if (!dfk::make_fp8_plan(op, B, d_model, d_ff, device_cus(dev), p)) return DFK_ERR_UNSUPPORTED;
+    using dfk::ENGINE_MFMA;
+    using dfk::ENGINE_VALU;
+    using dfk::TRAV_COL;
+    using dfk::TRAV_ROW;
+    Engine e;
+    Traversal tr;
+    switch (layout) {
+        case DFK_LAYOUT_AUTO:
+            if (op == dfk::OP_GATE_UP) {
+                if (B <= 3) e = ENGINE_VALU, tr = TRAV_ROW;
+                else e = ENGINE_MFMA, tr = (B <= 16 ? TRAV_COL : TRAV_ROW);
+            } else {
+                if (B <= 4) e = ENGINE_VALU, tr = TRAV_ROW;
+                else e = ENGINE_MFMA, tr = TRAV_COL;
+            }
+            break;
+        case DFK_LAYOUT_ROW: e = B <= dfk::kF8MaxBatch ? ENGINE_VALU : ENGINE_MFMA, tr = TRAV_ROW; break;
+        case DFK_LAYOUT_COL: e = ENGINE_MFMA, tr = TRAV_COL; break;
+        case DFK_LAYOUT_ROW_VALU: e = ENGINE_VALU, tr = TRAV_ROW; break;
+        case DFK_LAYOUT_ROW_MFMA: e = ENGINE_MFMA, tr = TRAV_ROW; break;
+        case DFK_LAYOUT_COL_MFMA: e = ENGINE_MFMA, tr = TRAV_COL; break;
+        default: return DFK_ERR_UNSUPPORTED;  // COL_VALU, ROW_PERSISTENT
+    }
+    if (!dfk::make_fp8_plan(op, e, tr, B, d_model, d_ff, device_cus(dev), p)) return DFK_ERR_UNSUPPORTED;
     log_plan(op == dfk::OP_GATE_UP ? "gate_up_fp8" : "down_fp8", *p);
     return DFK_OK;
 }

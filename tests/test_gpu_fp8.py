@@ -5,8 +5,9 @@ fp64 oracle over the dequantized weights W = s[row] * e4m3(q).
   the codes, so y is s * e4m3(q) itself, exact in bf16 for power-of-two
   scales (bit for bit against the oracle), and h is SiLU(1) * that value.
 - Ragged shapes (chunk counts not a multiple of 64, a single chunk, h past the
-  LDS limit, so K panels), batches 1 to 8, the Llama-3-8B layer shape: h
-  within 1e-4 and y within the usual normwise bars of the oracle.
+  LDS limit, so K panels), batches 1 to 128 on the vector-ALU (B <= 8) and
+  matrix-core variants, the Llama-3-8B layer shape: h within 1e-4 and y
+  within the usual normwise bars of the oracle.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,11 @@ from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
 
-LAYOUTS = [Layout.AUTO, Layout.ROW, Layout.ROW_VALU]
+LAYOUTS = [Layout.AUTO, Layout.ROW, Layout.COL, Layout.ROW_VALU, Layout.ROW_MFMA, Layout.COL_MFMA]
+
+
+def layouts_for(B):
+    return [l for l in LAYOUTS if B <= 8 or l != Layout.ROW_VALU]
 
 
 @pytest.fixture(scope="module")
@@ -45,8 +50,11 @@ def code_matrix(rows, cols, shift=0):
     return q
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 6, 8])
-def test_every_code_through_down(dev, orc, B):
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 6, 8, 20])
+@pytest.mark.parametrize("layout", [Layout.ROW_VALU, Layout.ROW_MFMA, Layout.COL_MFMA])
+def test_every_code_through_down(dev, orc, B, layout):
+    if layout == Layout.ROW_VALU and B > 8:
+        pytest.skip("the vector-ALU FP8 kernels take B <= 8")
     M = K = 256
     q = code_matrix(M, K)
     s = np.array([2.0 ** -(m % 4) for m in range(M)], dtype=np.float32)
@@ -55,12 +63,13 @@ def test_every_code_through_down(dev, orc, B):
         for b in range(B):
             h[b, (k0 + 7 * b) % K] = 1.0
         want = orc.bf16_rne_array(orc.down_fp8(h.astype(np.float64), q, s))
-        y = dfk.dfk_down_proj_fp8(to_dev(h, dev), to_dev(q, dev), to_dev(s, dev))
+        y = dfk.dfk_down_proj_fp8(to_dev(h, dev), to_dev(q, dev), to_dev(s, dev), layout=layout)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(H.host_bits(y), want, err_msg=f"k0={k0}")
 
 
-def test_every_code_through_gate_up(dev, orc):
+@pytest.mark.parametrize("layout", [Layout.ROW_VALU, Layout.ROW_MFMA, Layout.COL_MFMA])
+def test_every_code_through_gate_up(dev, orc, layout):
     N = K = 256
     qu = code_matrix(N, K, shift=3)
     qg = np.full((N, K), 0x38, dtype=np.uint8)  # every gate weight 1.0
@@ -72,7 +81,7 @@ def test_every_code_through_gate_up(dev, orc):
         xb = inputs.to_bf16_bits(torch.from_numpy(x))
         want = orc.gate_up_fp8(xb, qg, sg, qu, su)
         h = dfk.dfk_gate_up_silu_mul_fp8(H.dev_bf16(xb, dev), to_dev(qg, dev), to_dev(sg, dev), to_dev(qu, dev),
-                                         to_dev(su, dev))
+                                         to_dev(su, dev), layout=layout)
         torch.cuda.synchronize()
         got = h.double().cpu().numpy()
         np.testing.assert_allclose(got, want, rtol=5e-7, atol=0, err_msg=f"k0={k0}")
@@ -82,7 +91,8 @@ def test_every_code_through_gate_up(dev, orc):
 # a single chunk, every batch, h beyond the LDS limit at B = 4
 SHAPES = [(1, 256, 688), (1, 528, 1008), (2, 272, 80), (3, 1040, 208), (4, 144, 272), (2, 16, 16),
           (4, 4112, 272), (4, 64, 8208), (1, 2064, 4112), (5, 528, 1008), (6, 272, 4112), (7, 1040, 208),
-          (8, 144, 8208), (8, 16, 16)]
+          (8, 144, 8208), (8, 16, 16), (16, 528, 1008), (17, 272, 464), (40, 1040, 208), (64, 144, 272),
+          (128, 64, 48)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_%dx%d" % s)
@@ -93,7 +103,7 @@ def test_fp8_small_shapes(dev, orc, shape):
     y_ref, h_ref = orc.mlp_fp8(L["x"], L["q_gate"], L["s_gate"], L["q_up"], L["s_up"], L["q_down"], L["s_down"])
     h_in = inputs.h_like(B, dff, seed=9450 + B)
     yd_ref = orc.down_fp8(h_in.astype(np.float64), L["q_down"], L["s_down"])
-    for layout in LAYOUTS:
+    for layout in layouts_for(B):
         what = f"{layout.name} {shape}"
         h = dfk.dfk_gate_up_silu_mul_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], layout=layout)
         y = dfk.dfk_swiglu_mlp_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], d["q_down"],
@@ -105,7 +115,7 @@ def test_fp8_small_shapes(dev, orc, shape):
         H.assert_y_close(H.host_bf16_as_f64(yd), yd_ref, f"down_fp8 {what}")
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 16, 64])
 def test_fp8_llama8b_shape(dev, orc, B):
     L = inputs.fp8_layer(B, 4096, 14336, seed=9300, std=0.02)
     d = {k: (H.dev_bf16(v, dev) if k == "x" else to_dev(v, dev)) for k, v in L.items()}
@@ -122,8 +132,9 @@ def test_fp8_unsupported(dev):
         L = inputs.fp8_layer(B, dm, dff, seed=1, std=0.1)
         return {k: (H.dev_bf16(v, dev) if k == "x" else to_dev(v, dev)) for k, v in L.items()}
 
-    cases = [(mk(9, 64, 48), Layout.AUTO), (mk(1, 72, 48), Layout.AUTO), (mk(1, 64, 40), Layout.AUTO)]
-    cases += [(mk(1, 64, 48), l) for l in (Layout.COL, Layout.ROW_MFMA, Layout.COL_VALU, Layout.ROW_PERSISTENT)]
+    cases = [(mk(129, 64, 48), Layout.AUTO), (mk(9, 64, 48), Layout.ROW_VALU), (mk(1, 72, 48), Layout.AUTO),
+             (mk(1, 64, 40), Layout.AUTO)]
+    cases += [(mk(1, 64, 48), l) for l in (Layout.COL_VALU, Layout.ROW_PERSISTENT)]
     for d, layout in cases:
         with pytest.raises(dfk.DfkError) as e:
             dfk.dfk_swiglu_mlp_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], d["q_down"],
