@@ -2365,8 +2365,10 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
     }
 }
 
-// down: h staged as bf16 hi + lo planes; work item = (row-tile group, K split)
-template <int BT, int WAVES, int NBUF, int WPE>
+// down: h staged as bf16 hi + lo planes; work item = (row-tile group, K split);
+// each wave owns TR consecutive 16-row tiles, so every B fragment it reads
+// from LDS feeds TR tiles (LDS traffic per weight byte / TR)
+template <int BT, int WAVES, int NBUF, int WPE, int TR>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_staged_kernel(
     DownArgs a, float *partial, int S, int CS) {
     constexpr int NT = WAVES * kWave;
@@ -2381,19 +2383,23 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
     const int lr = lane & 15, lq = lane >> 4;
     const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
-    const int row_groups = (a.groups + WAVES - 1) / WAVES;
+    const int row_groups = (a.groups + WAVES * TR - 1) / (WAVES * TR);
     const int items = row_groups * S;
 
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int sp = it % S, g = it / S;
         const int c0 = sp * CS, c1 = min(c0 + CS, a.C);
         const int nb = (c1 - c0 + kStKbc - 1) / kStKbc;
-        const int tile = g * WAVES + wave;
-        const int row = min(tile * 16 + lr, a.M - 1);
-        const u32x4_t *pw = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)row * a.K);
-        f32x4_t acc[BT];
+        const int tile0 = (g * WAVES + wave) * TR;
+        const u32x4_t *pw[TR];
 #pragma unroll
-        for (int bt = 0; bt < BT; ++bt) acc[bt] = f32x4_t{0, 0, 0, 0};
+        for (int t = 0; t < TR; ++t)
+            pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)min((tile0 + t) * 16 + lr, a.M - 1) * a.K);
+        f32x4_t acc[TR][BT];
+#pragma unroll
+        for (int t = 0; t < TR; ++t)
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) acc[t][bt] = f32x4_t{0, 0, 0, 0};
 
         auto load_h = [&](f32x4_t (&hr)[XPT][2], int kb) {
             const int cs = st_block_start(kb, c0, c1);
@@ -2422,12 +2428,15 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
                 dlo[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, lo);
             }
         };
-        auto load_w = [&](u32x4_t (&wr)[8], int kb) {
+        auto load_w = [&](u32x4_t (&wr)[TR][8], int kb) {
             const int cs = st_block_start(kb, c0, c1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wr[j] = load_stream(pw + min(cs + 4 * j + lq, a.C - 1));
+            for (int t = 0; t < TR; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) wr[t][j] = load_stream(pw[t] + min(cs + 4 * j + lq, a.C - 1));
         };
-        auto compute = [&](const u32x4_t (&wr)[8], int kb) {
+        // each B fragment read from LDS serves the wave's TR row tiles
+        auto compute = [&](const u32x4_t (&wr)[TR][8], int kb) {
             const u32x4_t *shi = smem + (NBUF == 2 ? (kb & 1) : 0) * 2 * PLANE;
             const u32x4_t *slo = shi + PLANE;
 #pragma unroll
@@ -2435,12 +2444,16 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
                     const int o = (bt * 16 + lr) * kStPitch + 4 * j + lq;
-                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[j]), as_bf16x8(shi[o]), acc[bt], 0, 0, 0);
-                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[j]), as_bf16x8(slo[o]), acc[bt], 0, 0, 0);
+                    const bf16x8_t bhi = as_bf16x8(shi[o]), blo = as_bf16x8(slo[o]);
+#pragma unroll
+                    for (int t = 0; t < TR; ++t) {
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[t][j]), bhi, acc[t][bt], 0, 0, 0);
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[t][j]), blo, acc[t][bt], 0, 0, 0);
+                    }
                 }
         };
         f32x4_t hr[XPT][2];
-        u32x4_t w0[8], w1[8];
+        u32x4_t w0[TR][8], w1[TR][8];
         auto step = [&](auto &cw, auto &nw, int kb) {
             load_h(hr, kb + 1);
             load_w(nw, kb + 1);
@@ -2468,19 +2481,145 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
         } else {
             last(w0, kb);
         }
-        if (tile < a.groups) {
-            const int m = tile * 16 + 4 * lq;
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+            if (tile0 + t >= a.groups) break;
+            const int m = (tile0 + t) * 16 + 4 * lq;
 #pragma unroll
             for (int bt = 0; bt < BT; ++bt) {
                 const int b = bt * 16 + lr;
                 if (b < a.B && m < a.M) {
                     if (S == 1) {
-                        const unsigned lo = to_bf16_rne(acc[bt][0]) | ((unsigned)to_bf16_rne(acc[bt][1]) << 16);
-                        const unsigned hi = to_bf16_rne(acc[bt][2]) | ((unsigned)to_bf16_rne(acc[bt][3]) << 16);
+                        const unsigned lo = to_bf16_rne(acc[t][bt][0]) | ((unsigned)to_bf16_rne(acc[t][bt][1]) << 16);
+                        const unsigned hi = to_bf16_rne(acc[t][bt][2]) | ((unsigned)to_bf16_rne(acc[t][bt][3]) << 16);
                         *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
                     } else {
-                        *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = acc[bt];
+                        *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = acc[t][bt];
                     }
+                }
+            }
+        }
+    }
+}
+
+// -------------------------- MFMA, LDS-transposed weights + x staged in LDS --
+//
+// Gate-up for a few batch tiles (BT >= 2): the LDS-transposed weight stream of
+// the kernels above (2 rows x 512 B per load instruction, parked in a
+// wave-private padded LDS tile, read back in A-fragment order, one block
+// ahead in registers) with x staged in LDS per workgroup, block by block, as
+// the B-operand-staged kernels do: the B fragments of every tile of the
+// workgroup come from one staged copy instead of from L2 per wave.  One
+// staged x buffer: a barrier before it is overwritten and one after.  A wave
+// owns one 16-row tile (rows of W_gate and W_up); waves whose tile is past
+// the end stream clamped rows and write nothing, so every wave reaches every
+// barrier.
+template <int BT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpArgs a) {
+    using L = Lt<32>;
+    constexpr int KBC = 32;
+    constexpr int NT = WAVES * kWave;
+    constexpr int XR = 16 * BT;           // staged x rows: the padded batch
+    constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
+    static_assert(XR * KBC % NT == 0, "staging split");
+    extern __shared__ u32x4_t smem[];     // x block [XR][kStPitch], then [WAVES][2][L::kTile]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    u32x4_t *xs = smem;
+    u32x4_t *ltg = smem + XR * kStPitch + (size_t)wave * 2 * L::kTile;
+    u32x4_t *ltu = ltg + L::kTile;
+    const int nb = (a.C + KBC - 1) / KBC;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const u32x4_t *xg = reinterpret_cast<const u32x4_t *>(a.x);
+    const int wg_items = (a.groups + WAVES - 1) / WAVES;
+
+    auto load_x = [&](u32x4_t (&xr)[XPT], int kb) {
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+            const int i = t * NT + tid;
+            const int b = min(i / KBC, a.B - 1);
+            const int c = min(kb * KBC + i % KBC, a.C - 1);
+            xr[t] = xg[(size_t)b * a.C + c];
+        }
+    };
+    auto store_x = [&](const u32x4_t (&xr)[XPT], int kb) {
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+            const int i = t * NT + tid;
+            const int b = i / KBC, cc = i % KBC;
+            const bool ok = b < a.B && kb * KBC + cc < a.C;
+            xs[b * kStPitch + cc] = ok ? xr[t] : zero;
+        }
+    };
+
+    for (int g = blockIdx.x; g < wg_items; g += gridDim.x) {
+        const int tile = g * WAVES + wave;
+        const int row0 = tile * 16;
+        f32x4_t accg[BT], accu[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) accg[bt] = accu[bt] = f32x4_t{0, 0, 0, 0};
+        auto load_w = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
+            L::load(vg, a.wg, a.ldw, a.C, row0, a.N, kb, lane);
+            L::load(vu, a.wu, a.ldw, a.C, row0, a.N, kb, lane);
+        };
+        auto compute = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
+            L::store(ltg, vg, kb, a.C, lane);
+            L::store(ltu, vu, kb, a.C, lane);
+#pragma unroll
+            for (int j = 0; j < L::kSteps; ++j) {
+                const bf16x8_t ag = L::frag(ltg, j, lr, lq);
+                const bf16x8_t au = L::frag(ltu, j, lr, lq);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const bf16x8_t xb = as_bf16x8(xs[(bt * 16 + lr) * kStPitch + 4 * j + lq]);
+                    accg[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb, accg[bt], 0, 0, 0);
+                    accu[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb, accu[bt], 0, 0, 0);
+                }
+            }
+        };
+        u32x4_t xr[XPT];
+        u32x4_t vg0[L::kInsts], vu0[L::kInsts], vg1[L::kInsts], vu1[L::kInsts];
+        // prefetch block kb + 1 (x first, then the weights), multiply block
+        // kb, then park x(kb + 1) once every wave is done with x(kb)
+        auto step = [&](auto &cg, auto &cu, auto &ng, auto &nu, int kb) {
+            load_x(xr, kb + 1);
+            load_w(ng, nu, kb + 1);
+            compute(cg, cu, kb);
+            __syncthreads();
+            store_x(xr, kb + 1);
+            __syncthreads();
+        };
+        auto last = [&](auto &cg, auto &cu, int kb) {
+            compute(cg, cu, kb);
+            __syncthreads();
+        };
+        load_x(xr, 0);
+        load_w(vg0, vu0, 0);
+        store_x(xr, 0);
+        __syncthreads();
+        int kb = 0;
+        for (; kb + 2 < nb; kb += 2) {
+            step(vg0, vu0, vg1, vu1, kb);
+            step(vg1, vu1, vg0, vu0, kb + 1);
+        }
+        if (kb + 1 < nb) {
+            step(vg0, vu0, vg1, vu1, kb);
+            last(vg1, vu1, kb + 1);
+        } else {
+            last(vg0, vu0, kb);
+        }
+        if (tile < a.groups) {
+            const int n = row0 + 4 * lq;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (b < a.B && n < a.N) {
+                    f32x4_t o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
                 }
             }
         }
@@ -2815,6 +2954,17 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 // this batch (h panels in LDS), and the in-workgroup K split above it
 // MFMA row/col kernels: the LDS-transposed weight stream (1) or the direct
 // 16-row fragment loads (0); the transposed kernels cover B <= 128
+// gate-up row traversal for BT in [2, DFK_GU_LTS_MAX_BT]: LDS-transposed
+// weights with x staged in LDS (DFK_GU_LTS_WAVES waves per workgroup).  At
+// the Llama-3-8B shape this took B = 32 from 49.8 to 44.1 us and B = 64 from
+// 58.1 to 53.9 us against the B-operand-staged kernel; 2 waves per workgroup
+// were ~1 us faster at BT = 2 there but 22 us slower at the 70B shape
+#ifndef DFK_GU_LTS_MAX_BT
+#define DFK_GU_LTS_MAX_BT 4
+#endif
+#ifndef DFK_GU_LTS_WAVES
+#define DFK_GU_LTS_WAVES 4
+#endif
 #ifndef DFK_MFMA_LT
 #define DFK_MFMA_LT 1
 #endif
@@ -2872,6 +3022,13 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 // CU's resident workgroups, with no split shorter than this many chunks
 #ifndef DFK_ST_DN_MIN_CHUNKS
 #define DFK_ST_DN_MIN_CHUNKS 128
+#endif
+// 16-row tiles per wave in the staged down kernel: two in the 8-wave
+// kernels (many row tiles or BT >= 3) up to BT = 4, where they fit in
+// registers without spilling (at the Llama-3-70B shape, B = 64: 136 us
+// instead of 160 us); one otherwise
+#ifndef DFK_ST_DN_TR
+#define DFK_ST_DN_TR(W, BT) ((W) >= 8 && (BT) <= 4 ? 2 : 1)
 #endif
 // Workgroup-cooperative down kernel (ROW traversal, B <= 16): waves per
 // workgroup and K chunks per stage
@@ -2997,9 +3154,10 @@ template <int W, int BT> KernelInfo gu_staged_w() {
     constexpr int NB = DFK_ST_GU_NBUF(BT);
     return {(const void *)gate_up_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1)>, 16, W * kWave, NB, 0};
 }
+// rows_per_group: the 16 TR rows one wave owns
 template <int W, int BT> KernelInfo dn_staged_w() {
-    constexpr int NB = DFK_ST_DN_NBUF(BT);
-    return {(const void *)down_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1)>, 16, W * kWave, NB, 0};
+    constexpr int NB = DFK_ST_DN_NBUF(BT), TR = DFK_ST_DN_TR(W, BT);
+    return {(const void *)down_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1), TR>, 16 * TR, W * kWave, NB, 0};
 }
 template <int BT> KernelInfo gu_staged4() { return gu_staged_w<4, BT>(); }
 template <int BT> KernelInfo gu_staged8() { return gu_staged_w<8, BT>(); }
@@ -3217,6 +3375,25 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
+        if (gu && row && BT >= 2 && BT <= DFK_GU_LTS_MAX_BT) {
+            // LDS-transposed weights, x staged in LDS per workgroup
+            constexpr int W = DFK_GU_LTS_WAVES;
+            static const void *const lts[4] = {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W>,
+                                               (const void *)gate_up_mfma_lts_kernel<3, W>,
+                                               (const void *)gate_up_mfma_lts_kernel<4, W>};
+            static_assert(DFK_GU_LTS_MAX_BT <= 4, "instantiated for BT <= 4");
+            q.kind = KIND_GU_MFMA_LT;
+            q.block = W * kWave;
+            q.lds_bytes = (size_t)16 * BT * kStPitch * 16 + (size_t)W * 2 * Lt<32>::kTile * 16;
+            if (q.lds_bytes > kLdsLimit) return false;
+            q.rows_per_group = 16;
+            q.groups = (int)ceil_div(q.rows, 16);
+            q.fn = lts[BT - 1];
+            const long occ = blocks_per_cu(q.fn, q.block, q.lds_bytes);
+            q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)W)));
+            *out = q;
+            return true;
+        }
         if (BT >= (gu ? DFK_ST_GU_MIN_BT : DFK_ST_DN_MIN_BT) && BT <= kStMaxBT && (gu ? row : !row)) {
             // B operand staged in LDS per workgroup: gate-up ROW, down COL
             const long tiles = ceil_div(q.rows, 16);
@@ -3230,7 +3407,7 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             q.rows_per_group = 16;
             q.groups = (int)ceil_div(q.rows, 16);
             const long occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
-            const long row_groups = ceil_div(q.groups, waves);
+            const long row_groups = ceil_div((long)q.groups, (long)waves * (ki.rows_per_group / 16));
             const long target = (long)cus * occ;
             long S = 1;
             if (!gu) {
