@@ -2365,10 +2365,21 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
     }
 }
 
+// F8 staging: a 16-byte load of E4M3 codes carries the A fragments of two
+// MFMA steps.  Lane (r, q) loads code chunk 4 i + q of its row (16 codes,
+// 16 (4 i + q) .. + 15 of the block) and feeds the first 8 to step 2 i and the
+// last 8 to step 2 i + 1, so the block's K order is permuted: bf16 chunk a of
+// the block (8 elements) is consumed in step j = 2 (a / 8) + a % 2 by lanes
+// q = (a / 2) % 4, i.e. from B-fragment slot 4 j + q.  The staged h takes the
+// same permutation (the contraction does not depend on the order of K).
+__device__ __forceinline__ int f8_step_slot(int a) { return 4 * (2 * (a / 8) + a % 2) + (a / 2) % 4; }
+
 // down: h staged as bf16 hi + lo planes; work item = (row-tile group, K split);
 // each wave owns TR consecutive 16-row tiles, so every B fragment it reads
-// from LDS feeds TR tiles (LDS traffic per weight byte / TR)
-template <int BT, int WAVES, int NBUF, int WPE, int TR>
+// from LDS feeds TR tiles (LDS traffic per weight byte / TR).
+// F8: W_down is FP8 codes (a.qd, loaded as above) with row scales (a.sd),
+// applied to each split's sums.
+template <int BT, int WAVES, int NBUF, int WPE, int TR, bool F8 = false>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_staged_kernel(
     DownArgs a, float *partial, int S, int CS) {
     constexpr int NT = WAVES * kWave;
@@ -2392,9 +2403,18 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
         const int nb = (c1 - c0 + kStKbc - 1) / kStKbc;
         const int tile0 = (g * WAVES + wave) * TR;
         const u32x4_t *pw[TR];
+        float scd[TR][4];  // F8: the scales of this lane's output rows
 #pragma unroll
-        for (int t = 0; t < TR; ++t)
-            pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)min((tile0 + t) * 16 + lr, a.M - 1) * a.K);
+        for (int t = 0; t < TR; ++t) {
+            const size_t row = (size_t)min((tile0 + t) * 16 + lr, a.M - 1);
+            if constexpr (F8) {
+                pw[t] = reinterpret_cast<const u32x4_t *>(a.qd + row * a.K);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) scd[t][e] = a.sd[min((tile0 + t) * 16 + 4 * lq + e, a.M - 1)];
+            } else {
+                pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + row * a.K);
+            }
+        }
         f32x4_t acc[TR][BT];
 #pragma unroll
         for (int t = 0; t < TR; ++t)
@@ -2424,33 +2444,49 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
                 const bool ok = b < a.B && c >= c0 + kb * kStKbc && c < c1;
                 bf16x8_t hi, lo;
                 split_hi_lo(ok ? hr[t][0] : fzero, ok ? hr[t][1] : fzero, hi, lo);
-                dhi[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, hi);
-                dlo[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, lo);
+                const int v = F8 ? f8_step_slot(cc) : cc;
+                dhi[b * kStPitch + v] = __builtin_bit_cast(u32x4_t, hi);
+                dlo[b * kStPitch + v] = __builtin_bit_cast(u32x4_t, lo);
             }
         };
         auto load_w = [&](u32x4_t (&wr)[TR][8], int kb) {
             const int cs = st_block_start(kb, c0, c1);
 #pragma unroll
-            for (int t = 0; t < TR; ++t)
+            for (int t = 0; t < TR; ++t) {
+                if constexpr (F8) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) wr[t][j] = load_stream(pw[t] + min(cs + 4 * j + lq, a.C - 1));
+                    for (int i = 0; i < 4; ++i) wr[t][i] = load_stream(pw[t] + min(cs / 2 + 4 * i + lq, a.C / 2 - 1));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) wr[t][j] = load_stream(pw[t] + min(cs + 4 * j + lq, a.C - 1));
+                }
+            }
         };
         // each B fragment read from LDS serves the wave's TR row tiles
         auto compute = [&](const u32x4_t (&wr)[TR][8], int kb) {
             const u32x4_t *shi = smem + (NBUF == 2 ? (kb & 1) : 0) * 2 * PLANE;
             const u32x4_t *slo = shi + PLANE;
+            u32x4_t wf[TR][2];  // F8: the widened codes of steps j (even) and j + 1
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (F8) {
+                    if (j % 2 == 0) {
+#pragma unroll
+                        for (int t = 0; t < TR; ++t) e4m3x16_to_bf16(wr[t][j / 2], wf[t][0], wf[t][1]);
+                    }
+                }
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
                     const int o = (bt * 16 + lr) * kStPitch + 4 * j + lq;
                     const bf16x8_t bhi = as_bf16x8(shi[o]), blo = as_bf16x8(slo[o]);
 #pragma unroll
                     for (int t = 0; t < TR; ++t) {
-                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[t][j]), bhi, acc[t][bt], 0, 0, 0);
-                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[t][j]), blo, acc[t][bt], 0, 0, 0);
+                        const bf16x8_t aw = as_bf16x8(F8 ? wf[t][j % 2] : wr[t][j]);
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bhi, acc[t][bt], 0, 0, 0);
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, blo, acc[t][bt], 0, 0, 0);
                     }
                 }
+            }
         };
         f32x4_t hr[XPT][2];
         u32x4_t w0[TR][8], w1[TR][8];
@@ -2489,12 +2525,17 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
             for (int bt = 0; bt < BT; ++bt) {
                 const int b = bt * 16 + lr;
                 if (b < a.B && m < a.M) {
+                    f32x4_t v = acc[t][bt];
+                    if constexpr (F8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] *= scd[t][e];
+                    }
                     if (S == 1) {
-                        const unsigned lo = to_bf16_rne(acc[t][bt][0]) | ((unsigned)to_bf16_rne(acc[t][bt][1]) << 16);
-                        const unsigned hi = to_bf16_rne(acc[t][bt][2]) | ((unsigned)to_bf16_rne(acc[t][bt][3]) << 16);
+                        const unsigned lo = to_bf16_rne(v[0]) | ((unsigned)to_bf16_rne(v[1]) << 16);
+                        const unsigned hi = to_bf16_rne(v[2]) | ((unsigned)to_bf16_rne(v[3]) << 16);
                         *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
                     } else {
-                        *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = acc[t][bt];
+                        *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = v;
                     }
                 }
             }
@@ -2514,9 +2555,10 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
 // owns one 16-row tile (rows of W_gate and W_up); waves whose tile is past
 // the end stream clamped rows and write nothing, so every wave reaches every
 // barrier.
-template <int BT, int WAVES>
+// F8: the weights are FP8 codes (a.qg, a.qu) with row scales (a.sg, a.su).
+template <int BT, int WAVES, bool F8 = false>
 __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpArgs a) {
-    using L = Lt<32>;
+    using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
     constexpr int KBC = 32;
     constexpr int NT = WAVES * kWave;
     constexpr int XR = 16 * BT;           // staged x rows: the padded batch
@@ -2560,9 +2602,23 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
         f32x4_t accg[BT], accu[BT];
 #pragma unroll
         for (int bt = 0; bt < BT; ++bt) accg[bt] = accu[bt] = f32x4_t{0, 0, 0, 0};
+        float scg[4], scu[4];  // F8: the scales of this lane's output rows, loaded ahead of the weights
+        if constexpr (F8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = min(row0 + 4 * lq + e, a.N - 1);
+                scg[e] = a.sg[n];
+                scu[e] = a.su[n];
+            }
+        }
         auto load_w = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
-            L::load(vg, a.wg, a.ldw, a.C, row0, a.N, kb, lane);
-            L::load(vu, a.wu, a.ldw, a.C, row0, a.N, kb, lane);
+            if constexpr (F8) {
+                L::load(vg, a.qg, a.K, a.C, row0, a.N, kb, lane);
+                L::load(vu, a.qu, a.K, a.C, row0, a.N, kb, lane);
+            } else {
+                L::load(vg, a.wg, a.ldw, a.C, row0, a.N, kb, lane);
+                L::load(vu, a.wu, a.ldw, a.C, row0, a.N, kb, lane);
+            }
         };
         auto compute = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
             L::store(ltg, vg, kb, a.C, lane);
@@ -2618,7 +2674,10 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
                 if (b < a.B && n < a.N) {
                     f32x4_t o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (F8) o[e] = silu_mul(scg[e] * accg[bt][e], scu[e] * accu[bt][e]);
+                        else o[e] = silu_mul(accg[bt][e], accu[bt][e]);
+                    }
                     *reinterpret_cast<f32x4_t *>(a.h + (size_t)b * a.N + n) = o;
                 }
             }
@@ -3159,6 +3218,12 @@ template <int W, int BT> KernelInfo dn_staged_w() {
     constexpr int NB = DFK_ST_DN_NBUF(BT), TR = DFK_ST_DN_TR(W, BT);
     return {(const void *)down_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1), TR>, 16 * TR, W * kWave, NB, 0};
 }
+template <int W, int BT> KernelInfo dn_staged_w_f8() {
+    constexpr int NB = DFK_ST_DN_NBUF(BT), TR = DFK_ST_DN_TR(W, BT);
+    return {(const void *)down_mfma_staged_kernel<BT, W, NB, (W >= 8 ? 2 : 1), TR, true>, 16 * TR, W * kWave, NB, 0};
+}
+template <int BT> KernelInfo dn_staged4_f8() { return dn_staged_w_f8<4, BT>(); }
+template <int BT> KernelInfo dn_staged8_f8() { return dn_staged_w_f8<8, BT>(); }
 template <int BT> KernelInfo gu_staged4() { return gu_staged_w<4, BT>(); }
 template <int BT> KernelInfo gu_staged8() { return gu_staged_w<8, BT>(); }
 template <int BT> KernelInfo dn_staged4() { return dn_staged_w<4, BT>(); }
@@ -3217,6 +3282,8 @@ static const KernelInfo kGuStaged4[kStMaxBT] = DFK_B_TABLE(gu_staged4);
 static const KernelInfo kGuStaged8[kStMaxBT] = DFK_B_TABLE(gu_staged8);
 static const KernelInfo kDnStaged4[kStMaxBT] = DFK_B_TABLE(dn_staged4);
 static const KernelInfo kDnStaged8[kStMaxBT] = DFK_B_TABLE(dn_staged8);
+static const KernelInfo kDnStaged4F8[kStMaxBT] = DFK_B_TABLE(dn_staged4_f8);
+static const KernelInfo kDnStaged8F8[kStMaxBT] = DFK_B_TABLE(dn_staged8_f8);
 
 // FP8 row kernels: rows per work item (R) and 16-byte weight loads per lane
 // and row in one load group (U).
@@ -3279,6 +3346,44 @@ static int blocks_per_cu(const void *fn, int block, size_t lds) {
     if (ncache < 512) cache[ncache++] = Entry{fn, block, lds, n};
     return n;
 }
+
+// Workgroups of 8 waves for the B-operand-staged kernels (see the tile
+// parameters above).
+static bool staged_wide(bool gu, int BT, long tiles, int cus) {
+    return gu ? ceil_div(tiles, 8L) * 8 >= 7L * cus : (BT >= 3 || tiles >= 2L * cus);
+}
+
+// Fill the launch shape of a B-operand-staged kernel (q holds the op, B,
+// rows and K): LDS per workgroup, a grid that fills every CU's resident
+// workgroups, and for down the K splits (none shorter than
+// DFK_ST_DN_MIN_CHUNKS chunks, a multiple of the 32-chunk block).
+static bool plan_staged(bool gu, int B, int BT, int C, int cus, const KernelInfo &ki, Plan *q) {
+    const int waves = ki.block / kWave;
+    q->lds_bytes = (size_t)ki.waves_per_item * (gu ? 1 : 2) * 16 * BT * kStPitch * 16;
+    if (q->lds_bytes > kLdsLimit) return false;
+    q->kind = gu ? KIND_GU_MFMA_STAGED : KIND_DN_MFMA_STAGED;
+    q->block = ki.block;
+    q->rows_per_group = 16;
+    q->groups = (int)ceil_div(q->rows, 16);
+    const long occ = blocks_per_cu(ki.fn, q->block, q->lds_bytes);
+    const long row_groups = ceil_div((long)q->groups, (long)waves * (ki.rows_per_group / 16));
+    const long target = (long)cus * occ;
+    long S = 1;
+    if (!gu) {
+        const long max_s = std::max(1L, (long)C / DFK_ST_DN_MIN_CHUNKS);
+        S = std::min(max_s, std::max(1L, ceil_div(target, row_groups)));
+        long cs = ceil_div((long)C, S);
+        if (C >= kStKbc) cs = ceil_div(cs, (long)kStKbc) * kStKbc;
+        S = ceil_div((long)C, cs);
+        q->chunks_per_split = (int)cs;
+    }
+    q->splits = (int)S;
+    q->partial_floats = S > 1 ? (size_t)S * B * q->rows : 0;
+    q->grid = (int)std::max(1L, std::min(target, row_groups * S));
+    q->fn = ki.fn;
+    return true;
+}
+
 
 
 bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out,
@@ -3397,31 +3502,9 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
         if (BT >= (gu ? DFK_ST_GU_MIN_BT : DFK_ST_DN_MIN_BT) && BT <= kStMaxBT && (gu ? row : !row)) {
             // B operand staged in LDS per workgroup: gate-up ROW, down COL
             const long tiles = ceil_div(q.rows, 16);
-            const bool wide = gu ? ceil_div(tiles, 8L) * 8 >= 7L * cus : (BT >= 3 || tiles >= 2L * cus);
-            ki = gu ? (wide ? kGuStaged8 : kGuStaged4)[BT - 1] : (wide ? kDnStaged8 : kDnStaged4)[BT - 1];
-            const int waves = ki.block / kWave;
-            q.lds_bytes = (size_t)ki.waves_per_item * (gu ? 1 : 2) * 16 * BT * kStPitch * 16;
-            if (q.lds_bytes > kLdsLimit) return false;
-            q.kind = gu ? KIND_GU_MFMA_STAGED : KIND_DN_MFMA_STAGED;
-            q.block = ki.block;
-            q.rows_per_group = 16;
-            q.groups = (int)ceil_div(q.rows, 16);
-            const long occ = blocks_per_cu(ki.fn, q.block, q.lds_bytes);
-            const long row_groups = ceil_div((long)q.groups, (long)waves * (ki.rows_per_group / 16));
-            const long target = (long)cus * occ;
-            long S = 1;
-            if (!gu) {
-                const long max_s = std::max(1L, (long)C / DFK_ST_DN_MIN_CHUNKS);
-                S = std::min(max_s, std::max(1L, ceil_div(target, row_groups)));
-                long cs = ceil_div((long)C, S);
-                if (C >= kStKbc) cs = ceil_div(cs, (long)kStKbc) * kStKbc;
-                S = ceil_div((long)C, cs);
-                q.chunks_per_split = (int)cs;
-            }
-            q.splits = (int)S;
-            q.partial_floats = S > 1 ? (size_t)S * B * q.rows : 0;
-            q.grid = (int)std::max(1L, std::min(target, row_groups * S));
-            q.fn = ki.fn;
+            ki = gu ? (staged_wide(true, BT, tiles, cus) ? kGuStaged8 : kGuStaged4)[BT - 1]
+                    : (staged_wide(false, BT, tiles, cus) ? kDnStaged8 : kDnStaged4)[BT - 1];
+            if (!plan_staged(gu, B, BT, C, cus, ki, &q)) return false;
             *out = q;
             return true;
         }
@@ -3513,6 +3596,50 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
         const int BT = (int)ceil_div(B, 16);
         if (BT > kLtMaxBT) return false;
         const bool row = (trav == TRAV_ROW);
+        if (!gu && !row && BT >= DFK_ST_DN_MIN_BT && BT <= kStMaxBT) {
+            // h staged in LDS per workgroup, codes loaded as A fragments (as
+            // for bf16 weights)
+            Plan q{};
+            q.op = op;
+            q.engine = ENGINE_MFMA;
+            q.trav = trav;
+            q.B = B;
+            q.rows = d_model;
+            q.K = d_ff;
+            q.chunks_per_split = q.K / 8;
+            const long tiles = ceil_div((long)d_model, 16L);
+            const KernelInfo ki = (staged_wide(false, BT, tiles, cus) ? kDnStaged8F8 : kDnStaged4F8)[BT - 1];
+            if (!plan_staged(false, B, BT, d_ff / 8, cus, ki, &q)) return false;
+            *out = q;
+            return true;
+        }
+        if (gu && row && BT >= 2 && BT <= DFK_GU_LTS_MAX_BT) {
+            // x staged in LDS per workgroup (as for bf16 weights)
+            constexpr int W = DFK_GU_LTS_WAVES;
+            static const void *const lts[4] = {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W, true>,
+                                               (const void *)gate_up_mfma_lts_kernel<3, W, true>,
+                                               (const void *)gate_up_mfma_lts_kernel<4, W, true>};
+            Plan q{};
+            q.op = op;
+            q.engine = ENGINE_MFMA;
+            q.trav = trav;
+            q.B = B;
+            q.rows = d_ff;
+            q.K = d_model;
+            q.splits = 1;
+            q.chunks_per_split = q.K / 8;
+            q.kind = KIND_GU_MFMA_LT;
+            q.block = W * kWave;
+            q.lds_bytes = (size_t)16 * BT * kStPitch * 16 + (size_t)W * 2 * Lt8<32>::kTile * 16;
+            if (q.lds_bytes > kLdsLimit) return false;
+            q.rows_per_group = 16;
+            q.groups = (int)ceil_div(q.rows, 16);
+            q.fn = lts[BT - 1];
+            const long occ = blocks_per_cu(q.fn, q.block, q.lds_bytes);
+            q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)W)));
+            *out = q;
+            return true;
+        }
         const KernelInfo ki = row ? (gu ? kGuLtRowF8 : kDnLtRowF8)[BT - 1] : (gu ? kGuLtColF8 : kDnLtColF8)[BT - 1];
         Plan q{};
         q.op = op;
@@ -3607,6 +3734,22 @@ hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down,
         a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.groups = p.groups;
         void *argv[] = {&a};
         return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    }
+    if (p.kind == KIND_DN_MFMA_STAGED) {
+        DownArgs a{};
+        a.h = h; a.qd = q_down; a.sd = s_down; a.y = y;
+        a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 8; a.groups = p.groups;
+        int S = p.splits, CS = p.chunks_per_split;
+        if (S > 1 && !partial) return hipErrorInvalidValue;
+        float *part = S > 1 ? partial : nullptr;
+        void *argv[] = {&a, &part, &S, &CS};
+        hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+        if (e != hipSuccess || S == 1) return e;
+        int n = p.B * p.rows;
+        const float *cpartial = partial;
+        void *rargv[] = {&cpartial, &y, &S, &n};
+        return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256),
+                               rargv, 0, stream);
     }
     if (p.kind != KIND_DN_FP8_ROW) return hipErrorInvalidValue;
     if (p.splits > 1 && !partial) return hipErrorInvalidValue;
