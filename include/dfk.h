@@ -180,11 +180,12 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * multiplied by its scale once.  The computed h and out are those of the bf16
  * entry points over the dequantized weights (to fp32 summation order).
  * Engines: the vector-ALU row walk (B <= 8; x kept in LDS, so
- * B * d_model * 2 <= 160 KiB) and the LDS-transposed matrix-core kernels
- * (B <= 128), which widen the codes to bf16 on their way into LDS.  Layouts:
+ * B * d_model * 2 <= 160 KiB) and the matrix-core kernels (B <= 128),
+ * which widen the codes to bf16 exactly: on their way into LDS, or in
+ * registers (the down projection's column traversal).  Layouts:
  * AUTO = the measured best at the Llama-3-8B layer shape (gate-up: vector
  * ALU to B = 3, matrix-core column traversal to B = 16, row traversal above;
- * down: vector ALU to B = 4, matrix-core column traversal above); ROW =
+ * down: vector ALU to B = 3, matrix-core column traversal above); ROW =
  * vector ALU up to B = 8, else matrix cores; COL = matrix
  * cores; ROW_VALU, ROW_MFMA, COL_MFMA force the engine; COL_VALU and
  * ROW_PERSISTENT are DFK_ERR_UNSUPPORTED.  d_model and d_ff must be

@@ -3070,6 +3070,12 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_ST_GU_NBUF
 #define DFK_ST_GU_NBUF(BT) ((BT) <= 4 ? 2 : 1)
 #endif
+// FP8 down column traversal on the staged kernel from this many batch tiles
+// (B = 6-16 at the Llama-3-8B shape: 23-25 us, against 28-32 us for the
+// LDS-transposed kernel)
+#ifndef DFK_ST_DN_F8_MIN_BT
+#define DFK_ST_DN_F8_MIN_BT 1
+#endif
 #ifndef DFK_ST_DN_NBUF
 #define DFK_ST_DN_NBUF(BT) ((BT) <= 2 ? 2 : 1)
 #endif
@@ -3137,8 +3143,10 @@ template <int B, bool HLDS> KernelInfo dn_valu_col_t() {
     constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
     return {(const void *)down_valu_col_kernel<B, R, U, HLDS>, R, kValuBlock, kValuBlock / kWave, R * B};
 }
+// load groups in flight per lane in the K-panel down walk (B = 4: one, which
+// took the 70B shape from 79.0 to 76.3 us and the 8B shape from 24.8 to 24.0 us)
 #ifndef DFK_DN_PANEL_VALU_U
-#define DFK_DN_PANEL_VALU_U(B) 2
+#define DFK_DN_PANEL_VALU_U(B) ((B) == 4 ? 1 : 2)
 #endif
 template <int B> KernelInfo dn_valu_panel() {
     constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_PANEL_VALU_U(B);
@@ -3596,7 +3604,7 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
         const int BT = (int)ceil_div(B, 16);
         if (BT > kLtMaxBT) return false;
         const bool row = (trav == TRAV_ROW);
-        if (!gu && !row && BT >= DFK_ST_DN_MIN_BT && BT <= kStMaxBT) {
+        if (!gu && !row && BT >= DFK_ST_DN_F8_MIN_BT && BT <= kStMaxBT) {
             // h staged in LDS per workgroup, codes loaded as A fragments (as
             // for bf16 weights)
             Plan q{};
