@@ -3477,6 +3477,14 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
+        if (!gu && !row && BT == 1 && B >= DFK_DN_PANEL_MIN_B && ceil_div(q.rows, 16) >= 2L * cus) {
+            // many row tiles (two per CU or more): the wide B-operand-staged
+            // kernel, two tiles per wave (Llama-3-70B, B = 16: 105 us against
+            // 116 us for the K panels below; at the 8B shape it is slower)
+            if (!plan_staged(false, B, BT, C, cus, kDnStaged8[0], &q)) return false;
+            *out = q;
+            return true;
+        }
         if (!gu && !row && B >= DFK_DN_PANEL_MIN_B && B <= DFK_DN_PANEL_MAX_B && B <= 16) {
             // down column traversal as K panels across workgroups (+ a reduce
             // kernel); the h panel sits in LDS as bf16 hi + lo (32 B per chunk
