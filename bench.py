@@ -216,6 +216,43 @@ def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
     return res
 
 
+def time_shape_sweep(device, steps=100, warmup=10, min_rotated_bytes=600e6):
+    """The scheduler's shape sweep: whole-MLP us per call for every
+    (d_model, d_ff) x batch of the sweep, under AUTO and with both kernels
+    forced to ROW or to COL (the scheduler picks per kernel among four
+    variants, so AUTO should be at least as fast as either).  Enough weight
+    sets are rotated that they do not fit in the 256 MB last-level cache."""
+    import math
+    import torch
+    import swiglu_mlp_amd as dfk
+    from swiglu_mlp_amd import Layout, inputs
+
+    res = {}
+    for s, (dm, dff) in enumerate(inputs.SWEEP_SHAPES):
+        set_bytes = 3 * dm * dff * 2
+        R = max(2, math.ceil(min_rotated_bytes / set_bytes))
+        sets = [(inputs.randn_bf16_device((dff, dm), 0.02, 8000 + 100 * s + 10 * r + 1, device),
+                 inputs.randn_bf16_device((dff, dm), 0.02, 8000 + 100 * s + 10 * r + 2, device),
+                 inputs.randn_bf16_device((dm, dff), 0.02, 8000 + 100 * s + 10 * r + 3, device)) for r in range(R)]
+        shape = {}
+        for B in inputs.SWEEP_BATCHES:
+            x = inputs.randn_bf16_device((B, dm), 1.0, 8900 + B, device)
+            out = torch.empty((B, dm), dtype=torch.bfloat16, device=device)
+            # burn-in: the first timed variant of a fresh batch otherwise runs
+            # a few per cent slow
+            _timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % R], out), steps, warmup)
+            t = {}
+            for name, layout in (("auto", Layout.AUTO), ("row", Layout.ROW), ("col", Layout.COL)):
+                t[name] = _timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % R], out, layout=layout), steps, warmup) * 1e3
+            gbps = mlp_bytes(B, dm, dff) / (t["auto"] * 1e-6) / 1e9
+            shape[str(B)] = {"us_per_call": round(t["auto"], 2), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                             "row_us": round(t["row"], 2), "col_us": round(t["col"], 2)}
+        res[f"{dm}x{dff}"] = shape
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_persistent(sets, device, batches=(1, 2), steps=300, warmup=30):
     """Context: the persistent MLP kernel (both row walks in one cooperative
     launch, DFK_LAYOUT_ROW_PERSISTENT) against the scheduler's two-kernel
@@ -421,8 +458,9 @@ def main():
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
 
-    stack, shape70b, norm, persistent, packed, fp8 = None, None, None, None, None, None
+    stack, shape70b, norm, persistent, packed, fp8, sweep = None, None, None, None, None, None, None
     if not args.no_sweep:
+        sweep = time_shape_sweep(device)
         fp8 = time_fp8(device)
         packed = time_packed(sets, device)
         persistent = time_persistent(sets, device)
@@ -471,6 +509,7 @@ def main():
         "persistent_mlp_llama8b": persistent,
         "packed_gate_up_llama8b": packed,
         "fp8_weights_mlp_llama8b": fp8,
+        "shape_sweep": sweep,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets)

@@ -3024,6 +3024,21 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_GU_LTS_WAVES
 #define DFK_GU_LTS_WAVES 4
 #endif
+// fewer waves per workgroup (more workgroups) when the 16-row tiles number
+// fewer than DFK_GU_LTS_NARROW_X2 / 2 per CU (DFK_GU_LTS_NARROW_X2_BT2 / 2 at
+// BT = 2).  Swept over the scheduler's shapes at B = 32 / 48 / 64: d_model
+// 2048 (352 tiles) 21.5 / 23.9 / 26.3 -> 16.7 / 22.4 / 24.0 us; d_model 3072
+// at B = 32 (512 tiles) 33.5 -> 25.8 us; 2 waves at BT = 3-4 with 864-896
+// tiles were 9-11 us slower, at the 70B shape (1792 tiles) slower too
+#ifndef DFK_GU_LTS_NARROW_WAVES
+#define DFK_GU_LTS_NARROW_WAVES 2
+#endif
+#ifndef DFK_GU_LTS_NARROW_X2
+#define DFK_GU_LTS_NARROW_X2 4
+#endif
+#ifndef DFK_GU_LTS_NARROW_X2_BT2
+#define DFK_GU_LTS_NARROW_X2_BT2 8
+#endif
 #ifndef DFK_MFMA_LT
 #define DFK_MFMA_LT 1
 #endif
@@ -3073,6 +3088,18 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 // FP8 down column traversal on the staged kernel from this many batch tiles
 // (B = 6-16 at the Llama-3-8B shape: 23-25 us, against 28-32 us for the
 // LDS-transposed kernel)
+// wide (8-wave) staged down kernels from BT = 3 only when the row tiles
+// number more than DFK_ST_DN_WIDE_X2 / 2 per CU; splits down to this many
+// chunks when the row groups times the regular splits do not reach one work
+// item per CU.  At d_model 2048 (d_ff 5632), B = 48 / 64: 17.4 / 20.8 us
+// instead of 42.2 / 46.3 us (40 work items on 256 CUs before); no change at
+// the larger shapes of the sweep
+#ifndef DFK_ST_DN_WIDE_X2
+#define DFK_ST_DN_WIDE_X2 1
+#endif
+#ifndef DFK_ST_DN_SMALL_MIN_CHUNKS
+#define DFK_ST_DN_SMALL_MIN_CHUNKS 64
+#endif
 #ifndef DFK_ST_DN_F8_MIN_BT
 #define DFK_ST_DN_F8_MIN_BT 1
 #endif
@@ -3358,7 +3385,8 @@ static int blocks_per_cu(const void *fn, int block, size_t lds) {
 // Workgroups of 8 waves for the B-operand-staged kernels (see the tile
 // parameters above).
 static bool staged_wide(bool gu, int BT, long tiles, int cus) {
-    return gu ? ceil_div(tiles, 8L) * 8 >= 7L * cus : (BT >= 3 || tiles >= 2L * cus);
+    return gu ? ceil_div(tiles, 8L) * 8 >= 7L * cus
+              : ((BT >= 3 && 2 * tiles > (long)DFK_ST_DN_WIDE_X2 * cus) || tiles >= 2L * cus);
 }
 
 // Fill the launch shape of a B-operand-staged kernel (q holds the op, B,
@@ -3378,7 +3406,8 @@ static bool plan_staged(bool gu, int B, int BT, int C, int cus, const KernelInfo
     const long target = (long)cus * occ;
     long S = 1;
     if (!gu) {
-        const long max_s = std::max(1L, (long)C / DFK_ST_DN_MIN_CHUNKS);
+        long max_s = std::max(1L, (long)C / DFK_ST_DN_MIN_CHUNKS);
+        if (row_groups * max_s < cus) max_s = std::max(1L, (long)C / DFK_ST_DN_SMALL_MIN_CHUNKS);
         S = std::min(max_s, std::max(1L, ceil_div(target, row_groups)));
         long cs = ceil_div((long)C, S);
         if (C >= kStKbc) cs = ceil_div(cs, (long)kStKbc) * kStKbc;
@@ -3498,20 +3527,24 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
         }
         if (gu && row && BT >= 2 && BT <= DFK_GU_LTS_MAX_BT) {
             // LDS-transposed weights, x staged in LDS per workgroup
-            constexpr int W = DFK_GU_LTS_WAVES;
-            static const void *const lts[4] = {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W>,
-                                               (const void *)gate_up_mfma_lts_kernel<3, W>,
-                                               (const void *)gate_up_mfma_lts_kernel<4, W>};
+            constexpr int W = DFK_GU_LTS_WAVES, WN = DFK_GU_LTS_NARROW_WAVES;
+            static const void *const lts[2][4] = {
+                {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W>, (const void *)gate_up_mfma_lts_kernel<3, W>,
+                 (const void *)gate_up_mfma_lts_kernel<4, W>},
+                {nullptr, (const void *)gate_up_mfma_lts_kernel<2, WN>, (const void *)gate_up_mfma_lts_kernel<3, WN>,
+                 (const void *)gate_up_mfma_lts_kernel<4, WN>}};
             static_assert(DFK_GU_LTS_MAX_BT <= 4, "instantiated for BT <= 4");
+            q.groups = (int)ceil_div(q.rows, 16);
+            const bool narrow = 2L * q.groups < (long)(BT == 2 ? DFK_GU_LTS_NARROW_X2_BT2 : DFK_GU_LTS_NARROW_X2) * cus;
+            const int w = narrow ? WN : W;
             q.kind = KIND_GU_MFMA_LT;
-            q.block = W * kWave;
-            q.lds_bytes = (size_t)16 * BT * kStPitch * 16 + (size_t)W * 2 * Lt<32>::kTile * 16;
+            q.block = w * kWave;
+            q.lds_bytes = (size_t)16 * BT * kStPitch * 16 + (size_t)w * 2 * Lt<32>::kTile * 16;
             if (q.lds_bytes > kLdsLimit) return false;
             q.rows_per_group = 16;
-            q.groups = (int)ceil_div(q.rows, 16);
-            q.fn = lts[BT - 1];
+            q.fn = lts[narrow ? 1 : 0][BT - 1];
             const long occ = blocks_per_cu(q.fn, q.block, q.lds_bytes);
-            q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)W)));
+            q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)w)));
             *out = q;
             return true;
         }
