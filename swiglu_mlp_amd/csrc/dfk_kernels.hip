@@ -3108,9 +3108,10 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #endif
 // Workgroups of 8 waves share each staged block among more tiles; they are
 // used when they still give (almost) every CU a workgroup, i.e. when
-// ceil(tiles / 8) >= 7/8 of the CUs (gate-up), and for down when BT >= 3 or
-// the row tiles number at least two per CU (its K split fills the machine).
-// the staged down kernel splits K so that (row groups x splits) fills every
+// ceil(tiles / 8) >= 7/8 of the CUs (gate-up), and for down when the row
+// tiles number at least two per CU, or BT >= 3 with more than
+// DFK_ST_DN_WIDE_X2 / 2 tiles per CU (its K split fills the machine).
+// The staged down kernel splits K so that (row groups x splits) fills every
 // CU's resident workgroups, with no split shorter than this many chunks
 #ifndef DFK_ST_DN_MIN_CHUNKS
 #define DFK_ST_DN_MIN_CHUNKS 128
