@@ -22,8 +22,6 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // per CU at the top; measured faster than reading h through the caches), else
 // they read it through the caches.
 constexpr size_t kHLdsLimit = 128 * 1024;
-// LDS budget of one h panel of the K-panel down kernel (two workgroups per CU).
-constexpr size_t kPanelLds = 64 * 1024;
 
 enum Kind {
     KIND_GU_VALU_ROW = 0,
@@ -34,7 +32,6 @@ enum Kind {
     KIND_GU_MFMA_COL = 5,
     KIND_DN_MFMA_ROW = 6,
     KIND_DN_MFMA_COL = 7,
-    KIND_DN_MFMA_PANEL = 8,  // down col traversal, K panels across workgroups + a reduce kernel
     KIND_GU_MFMA_LT = 10,    // gate-up, weights streamed through a wave-private LDS transpose
     KIND_DN_MFMA_LT = 11,
     KIND_GU_MFMA_STAGED = 12,  // gate-up, B operand staged in LDS per workgroup (B > 16)

@@ -2685,6 +2685,130 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
     }
 }
 
+// Down for a few batch tiles: LDS-transposed weight streaming (as the
+// LT kernels) with h staged in LDS per workgroup, block by block, already
+// split into bf16 hi + lo planes (as the B-operand-staged kernels), so the
+// split and the h reads from L2 are shared by the workgroup's WAVES tiles.
+// A work item is (WAVES row tiles, one of S K splits); S > 1 writes fp32
+// partial sums that panel_reduce_kernel adds in split order.  Waves whose tile
+// is past the end stream clamped rows and write nothing, so every wave
+// reaches every barrier.
+template <int BT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void down_mfma_lts_kernel(DownArgs a, float *partial, int S, int CS) {
+    using L = Lt<32>;
+    constexpr int KBC = 32;
+    constexpr int NT = WAVES * kWave;
+    constexpr int XR = 16 * BT;           // staged h rows: the padded batch
+    constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
+    static_assert(XR * KBC % NT == 0, "staging split");
+    constexpr int PLANE = XR * kStPitch;
+    extern __shared__ u32x4_t smem[];     // h hi [XR][kStPitch], lo [XR][kStPitch], then [WAVES][L::kTile]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    u32x4_t *shi = smem, *slo = smem + PLANE;
+    u32x4_t *ltw = smem + 2 * PLANE + (size_t)wave * L::kTile;
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    const int row_groups = (a.groups + WAVES - 1) / WAVES;
+    const int items = row_groups * S;
+
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int sp = it % S, g = it / S;
+        const int c0 = sp * CS, nch = min(CS, a.C - c0);
+        const int nb = (nch + KBC - 1) / KBC;
+        const int tile = g * WAVES + wave;
+        const int row0 = tile * 16;
+        f32x4_t acc[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) acc[bt] = fzero;
+        auto load_h = [&](f32x4_t (&hr)[XPT][2], int kb) {
+#pragma unroll
+            for (int t = 0; t < XPT; ++t) {
+                const int i = t * NT + tid;
+                const int b = min(i / KBC, a.B - 1);
+                const int c = min(c0 + kb * KBC + i % KBC, a.C - 1);
+                hr[t][0] = hg[(size_t)b * 2 * a.C + 2 * c];
+                hr[t][1] = hg[(size_t)b * 2 * a.C + 2 * c + 1];
+            }
+        };
+        auto store_h = [&](const f32x4_t (&hr)[XPT][2], int kb) {
+#pragma unroll
+            for (int t = 0; t < XPT; ++t) {
+                const int i = t * NT + tid;
+                const int b = i / KBC, cc = i % KBC;
+                const bool ok = b < a.B && kb * KBC + cc < nch;
+                bf16x8_t hi, lo;
+                split_hi_lo(ok ? hr[t][0] : fzero, ok ? hr[t][1] : fzero, hi, lo);
+                shi[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, hi);
+                slo[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, lo);
+            }
+        };
+        auto load_w = [&](u32x4_t (&v)[L::kInsts], int kb) {
+            L::load(v, a.wd + (size_t)c0 * 8, a.K, nch, row0, a.M, kb, lane);
+        };
+        auto compute = [&](u32x4_t (&v)[L::kInsts], int kb) {
+            L::store(ltw, v, kb, nch, lane);
+#pragma unroll
+            for (int j = 0; j < L::kSteps; ++j) {
+                const bf16x8_t aw = L::frag(ltw, j, lr, lq);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const int o = (bt * 16 + lr) * kStPitch + 4 * j + lq;
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, as_bf16x8(shi[o]), acc[bt], 0, 0, 0);
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, as_bf16x8(slo[o]), acc[bt], 0, 0, 0);
+                }
+            }
+        };
+        f32x4_t hr[XPT][2];
+        u32x4_t v0[L::kInsts], v1[L::kInsts];
+        // prefetch block kb + 1 (h first, then the weights), multiply block
+        // kb, then park h(kb + 1) once every wave is done with h(kb)
+        auto step = [&](auto &cv, auto &nv, int kb) {
+            load_h(hr, kb + 1);
+            load_w(nv, kb + 1);
+            compute(cv, kb);
+            __syncthreads();
+            store_h(hr, kb + 1);
+            __syncthreads();
+        };
+        auto last = [&](auto &cv, int kb) {
+            compute(cv, kb);
+            __syncthreads();
+        };
+        load_h(hr, 0);
+        load_w(v0, 0);
+        store_h(hr, 0);
+        __syncthreads();
+        int kb = 0;
+        for (; kb + 2 < nb; kb += 2) {
+            step(v0, v1, kb);
+            step(v1, v0, kb + 1);
+        }
+        if (kb + 1 < nb) {
+            step(v0, v1, kb);
+            last(v1, kb + 1);
+        } else {
+            last(v0, kb);
+        }
+        const int m = row0 + 4 * lq;
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) {
+            const int b = bt * 16 + lr;
+            if (tile < a.groups && b < a.B && m < a.M) {
+                if (S == 1) {
+                    const unsigned lo = to_bf16_rne(acc[bt][0]) | ((unsigned)to_bf16_rne(acc[bt][1]) << 16);
+                    const unsigned hi = to_bf16_rne(acc[bt][2]) | ((unsigned)to_bf16_rne(acc[bt][3]) << 16);
+                    *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
+                } else {
+                    *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = acc[bt];
+                }
+            }
+        }
+    }
+}
+
 // ----------------------- MFMA, workgroup-cooperative weight tile (down) -----
 //
 // The down projection's row traversal on the matrix cores, for batches up to
@@ -2843,109 +2967,6 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_coop_kernel(DownArgs 
     }
 }
 
-// ------------------------------------------------------ MFMA K panels -----
-//
-// Down-projection column traversal on the matrix cores for batches 9..16: the
-// K columns of W_down are cut into S panels across workgroups.  Workgroup (s, part)
-// stages panel s of its operand in LDS once, already in MFMA fragment order
-// (entry [chunk][b] is the 16 bytes lane (b mod 16, chunk mod 4) needs), and
-// its waves stream 16-row tiles over that panel, so each operand byte crosses
-// L2 once per panel instead of once per row tile, and there are S times more
-// work items than row tiles.  Panel sums go to a partial buffer; a reduce
-// kernel, next on the same stream, adds the S panels in panel order and runs
-// the epilogue.  Stream order is the only synchronisation (no atomics, no
-// cross-workgroup fences).
-
-// down: partial[s][b][m] = panel-s sum; h staged as bf16 hi + lo fragments.
-template <int BT, int TR, int U>
-__global__ __launch_bounds__(kValuBlock) void down_mfma_panel_kernel(DownArgs a, float *partial, int S, int CS) {
-    extern __shared__ u32x4_t hf[];  // hi plane [CS][B], then lo plane [CS][B]
-    const int lane = threadIdx.x & (kWave - 1);
-    const int waves = blockDim.x / kWave;
-    const int wave = threadIdx.x / kWave;
-    const int lr = lane & 15, lq = lane >> 4;
-    const int s = blockIdx.x % S;
-    const int part = blockIdx.x / S, parts = gridDim.x / S;
-    const int c_beg = s * CS;
-    const int nch = min(CS, a.C - c_beg);
-    const int steps = (nch + 3) / 4;
-    const size_t plane = (size_t)CS * a.B;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);  // [B][2C]
-    for (int i = threadIdx.x; i < a.B * nch; i += blockDim.x) {
-        const int b = i / nch;
-        const int ci = i - b * nch;
-        const size_t o = (size_t)b * 2 * a.C + 2 * (size_t)(c_beg + ci);
-        bf16x8_t hi, lo;
-        split_hi_lo(hg[o], hg[o + 1], hi, lo);
-        hf[(size_t)ci * a.B + b] = __builtin_bit_cast(u32x4_t, hi);
-        hf[plane + (size_t)ci * a.B + b] = __builtin_bit_cast(u32x4_t, lo);
-    }
-    __syncthreads();
-
-    bool bvalid[BT];
-#pragma unroll
-    for (int bt = 0; bt < BT; ++bt) bvalid[bt] = bt * 16 + lr < a.B;
-
-    for (int tg = part * waves + wave; tg < a.groups; tg += parts * waves) {
-        const int row0 = tg * 16 * TR;
-        const u32x4_t *pw[TR];
-#pragma unroll
-        for (int t = 0; t < TR; ++t) {
-            const int m = min(row0 + t * 16 + lr, a.M - 1);
-            pw[t] = reinterpret_cast<const u32x4_t *>(a.wd + (size_t)m * a.K + (size_t)c_beg * 8);
-        }
-        f32x4_t acc[TR][BT];
-#pragma unroll
-        for (int t = 0; t < TR; ++t)
-#pragma unroll
-            for (int bt = 0; bt < BT; ++bt) acc[t][bt] = f32x4_t{0, 0, 0, 0};
-
-        for (int st = 0; st < steps; st += U) {
-            u32x4_t aw[U][TR];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int ci = min((st + u) * 4 + lq, nch - 1);
-#pragma unroll
-                for (int t = 0; t < TR; ++t) aw[u][t] = load_stream(pw[t] + ci);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int ci = (st + u) * 4 + lq;
-                const bool kv = ci < nch;
-                bf16x8_t hhi[BT], hlo[BT];
-#pragma unroll
-                for (int bt = 0; bt < BT; ++bt) {
-                    const bool ok = kv && bvalid[bt];
-                    const size_t o = (size_t)ci * a.B + bt * 16 + lr;
-                    hhi[bt] = as_bf16x8(ok ? hf[o] : zero);
-                    hlo[bt] = as_bf16x8(ok ? hf[plane + o] : zero);
-                }
-#pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    const bf16x8_t wa = as_bf16x8(kv ? aw[u][t] : zero);
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
-                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hhi[bt], acc[t][bt], 0, 0, 0);
-                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, hlo[bt], acc[t][bt], 0, 0, 0);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < TR; ++t) {
-            const int m = row0 + t * 16 + 4 * lq;
-#pragma unroll
-            for (int bt = 0; bt < BT; ++bt) {
-                const int b = bt * 16 + lr;
-                if (b < a.B && m < a.M)
-                    *reinterpret_cast<f32x4_t *>(partial + ((size_t)s * a.B + b) * a.M + m) = acc[t][bt];
-            }
-        }
-    }
-}
-
 // y[i] = RNE_bf16(sum_{s ascending} partial[s][i]) for i < n (n % 4 == 0),
 // four outputs per thread.
 __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial, uint16_t *y, int S, int n) {
@@ -3064,14 +3085,22 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #ifndef DFK_LT_DN_KSPLIT
 #define DFK_LT_DN_KSPLIT(BT) 4
 #endif
-#ifndef DFK_DN_PANEL_MIN_B
-#define DFK_DN_PANEL_MIN_B 9
+// down column traversal at one batch tile (B <= 16): the LDS-transposed
+// kernel with staged h, DFK_DN_LTS_WAVES tiles per workgroup
+// (DFK_DN_LTS_WIDE_WAVES above B = 8 when the row tiles number two per CU or
+// more), K splits of at least DFK_DN_LTS_MIN_CHUNKS chunks.  Event-timed down,
+// us, Llama-3-8B shape B = 8 / 16: 25.6 / 26.6 against 27.5 / 32.4 for the LT
+// column kernel and the K-panel kernel it replaced; Llama-3-70B shape B = 8 /
+// 16: 78.7 / 84.0 against 95.6 / 104.9.  Two batch tiles (B = 17-32) gained
+// about 1 us at the 8B shape and nothing at 70B: the staged kernel stays.
+#ifndef DFK_DN_LTS_WAVES
+#define DFK_DN_LTS_WAVES 2
 #endif
-#ifndef DFK_DN_PANEL_MAX_B
-#define DFK_DN_PANEL_MAX_B 16
+#ifndef DFK_DN_LTS_WIDE_WAVES
+#define DFK_DN_LTS_WIDE_WAVES 4
 #endif
-#ifndef DFK_DN_PANEL_U
-#define DFK_DN_PANEL_U 4
+#ifndef DFK_DN_LTS_MIN_CHUNKS
+#define DFK_DN_LTS_MIN_CHUNKS 128
 #endif
 // B-operand-staged MFMA kernels: used from this many batch tiles up to
 // kStMaxBT (gate-up ROW traversal, down COL traversal); waves per workgroup
@@ -3133,14 +3162,6 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 #endif
 #ifndef DFK_COOP_DN_KSC
 #define DFK_COOP_DN_KSC 128
-#endif
-// K panels are chosen so that panels x row tiles >= CUs x this many waves
-#ifndef DFK_PANEL_WAVES_PER_CU
-#define DFK_PANEL_WAVES_PER_CU 16
-#endif
-// ... but no panel shorter than this many 16-byte chunks
-#ifndef DFK_PANEL_MIN_CHUNKS
-#define DFK_PANEL_MIN_CHUNKS 32
 #endif
 
 struct KernelInfo {
@@ -3204,29 +3225,6 @@ template <int BT> KernelInfo dn_mfma_col() {
 
 static long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-static const void *kPanelFn = (const void *)down_mfma_panel_kernel<1, 1, DFK_DN_PANEL_U>;
-
-// K panels for a panel kernel: each panel's operand (bytes_per_chunk per
-// 16-byte weight chunk) must fit the LDS budget, panels x row tiles should
-// give every CU DFK_PANEL_WAVES_PER_CU waves, panels stay >= the minimum
-// length (unless the LDS forces them shorter).
-static void plan_panels(int C, size_t bytes_per_chunk, int groups, int cus, Plan *q) {
-    const long max_cs = std::max<long>(4, (long)(kPanelLds / bytes_per_chunk) / 4 * 4);
-    const long s_lds = ceil_div(C, max_cs);
-    const long s_par = ceil_div((long)cus * DFK_PANEL_WAVES_PER_CU, groups);
-    const long s_len = std::max(1L, (long)C / DFK_PANEL_MIN_CHUNKS);
-    long S = std::max(s_lds, std::min(s_par, s_len));
-    S = std::min<long>(S, ceil_div(C, 4));
-    const long cs = ceil_div(ceil_div(C, S), 4) * 4;
-    S = ceil_div(C, cs);
-    q->splits = (int)S;
-    q->chunks_per_split = (int)cs;
-    q->block = kValuBlock;
-    q->rows_per_group = 16;
-    q->groups = groups;
-    q->lds_bytes = bytes_per_chunk * cs;
-    q->grid = (int)(S * ceil_div(groups, kValuBlock / kWave));
-}
 
 template <int BT> KernelInfo gu_lt_row() {
     constexpr int W = DFK_LT_GU_ROW_WAVES(BT);
@@ -3507,22 +3505,31 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
-        if (!gu && !row && BT == 1 && B >= DFK_DN_PANEL_MIN_B && ceil_div(q.rows, 16) >= 2L * cus) {
-            // many row tiles (two per CU or more): the wide B-operand-staged
-            // kernel, two tiles per wave (Llama-3-70B, B = 16: 105 us against
-            // 116 us for the K panels below; at the 8B shape it is slower)
-            if (!plan_staged(false, B, BT, C, cus, kDnStaged8[0], &q)) return false;
-            *out = q;
-            return true;
-        }
-        if (!gu && !row && B >= DFK_DN_PANEL_MIN_B && B <= DFK_DN_PANEL_MAX_B && B <= 16) {
-            // down column traversal as K panels across workgroups (+ a reduce
-            // kernel); the h panel sits in LDS as bf16 hi + lo (32 B per chunk
-            // and batch row)
-            plan_panels(C, (size_t)B * 32, (int)ceil_div(q.rows, 16), cus, &q);
-            q.kind = KIND_DN_MFMA_PANEL;
-            q.partial_floats = (size_t)q.splits * B * q.rows;
-            q.fn = kPanelFn;
+        if (!gu && !row && BT == 1) {
+            // LDS-transposed weights with h staged in LDS per workgroup
+            constexpr int W = DFK_DN_LTS_WAVES, WW = DFK_DN_LTS_WIDE_WAVES;
+            q.groups = (int)ceil_div(q.rows, 16);
+            const bool wide = B > 8 && q.groups >= 2L * cus;
+            const int w = wide ? WW : W;
+            const void *fn = wide ? (const void *)down_mfma_lts_kernel<1, WW> : (const void *)down_mfma_lts_kernel<1, W>;
+            q.kind = KIND_DN_MFMA_STAGED;
+            q.block = w * kWave;
+            q.lds_bytes = (size_t)2 * 16 * BT * kStPitch * 16 + (size_t)w * Lt<32>::kTile * 16;
+            if (q.lds_bytes > kLdsLimit) return false;
+            q.rows_per_group = 16;
+            const long occ = blocks_per_cu(fn, q.block, q.lds_bytes);
+            const long row_groups = ceil_div((long)q.groups, (long)w);
+            const long target = (long)cus * occ;
+            const long max_s = std::max(1L, (long)C / DFK_DN_LTS_MIN_CHUNKS);
+            long S = std::min(max_s, std::max(1L, ceil_div(target, row_groups)));
+            long cs = ceil_div((long)C, S);
+            if (C >= 32) cs = ceil_div(cs, 32L) * 32;
+            S = ceil_div((long)C, cs);
+            q.splits = (int)S;
+            q.chunks_per_split = (int)cs;
+            q.partial_floats = S > 1 ? (size_t)S * B * q.rows : 0;
+            q.grid = (int)std::max(1L, std::min(target, row_groups * S));
+            q.fn = fn;
             *out = q;
             return true;
         }
@@ -3860,7 +3867,7 @@ hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, ui
         return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256),
                                rargv, 0, stream);
     }
-    if (p.kind != KIND_DN_MFMA_PANEL && p.kind != KIND_DN_MFMA_STAGED) {
+    if (p.kind != KIND_DN_MFMA_STAGED) {
         void *argv[] = {&a};
         return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
     }
