@@ -17,7 +17,7 @@ Timers:
            call's (a block's calls run back to back, so this is the kernel
            time plus the launch gap before it: what a stream of decode calls
            pays per call).  The profile ranks every variant; those within
-           10 % of its best are then re-timed untraced (HIP events around
+           50 % of its best are then re-timed untraced (HIP events around
            back-to-back calls) and the confirmation picks among them;
   events   HIP events around groups of back-to-back launches only.
 
@@ -54,8 +54,10 @@ TIE = 0.02
 # back with HIP events and no profiler attached, and that decides among them:
 # measured on MI355X, the traced run reads the LDS-transposed MFMA kernels up
 # to ~5 % faster, relative to the VALU kernels, than the same calls run
-# untraced.
-CONFIRM_BAND = 0.10
+# untraced, and calls of two kernels (a K-split kernel plus the reduce
+# kernel) up to ~35 % slower (Llama-3-8B down at B = 16: 36.0 us traced,
+# 27.9 us untraced).  The profile still rules out the variants far behind.
+CONFIRM_BAND = 0.50
 ROTATE_BYTES = 1.5e9
 
 
