@@ -115,11 +115,12 @@ dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate,
 /*
  * Down projection, a separate kernel (same passage: the down projection stays
  * out of the fused kernel).  out[b,m] = RNE_bf16( sum_n h[b,n] W_down[m,n] ),
- * fp32 accumulation from the fp32 h.  The column traversal on the matrix
- * cores for 9 <= B <= 16 cuts K into panels across workgroups and adds the
- * panel sums with a second, small kernel on the same stream; its scratch
- * (panels * B * d_model * 4 bytes) is library-owned per (device, stream).
- * Every other variant is one launch with no scratch memory.
+ * fp32 accumulation from the fp32 h.  Variants that split K across
+ * workgroups (the vector-ALU row walk when h exceeds its LDS budget, and
+ * the matrix-core column traversal) add the split sums with a second, small
+ * kernel on the same stream, in split order; their scratch (splits * B *
+ * d_model * 4 bytes) is library-owned per (device, stream).  The other
+ * variants are one launch with no scratch memory.
  */
 dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out, int B,
                            int d_model, int d_ff, dfk_layout_t layout, hipStream_t stream);
