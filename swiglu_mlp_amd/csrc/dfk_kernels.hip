@@ -2556,7 +2556,8 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
 // the end stream clamped rows and write nothing, so every wave reaches every
 // barrier.
 // F8: the weights are FP8 codes (a.qg, a.qu) with row scales (a.sg, a.su).
-template <int BT, int WAVES, bool F8 = false>
+// NBUF = 2 double-buffers the staged x block (one barrier per block).
+template <int BT, int WAVES, bool F8 = false, int NBUF = 1>
 __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpArgs a) {
     using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
     constexpr int KBC = 32;
@@ -2564,13 +2565,13 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
     constexpr int XR = 16 * BT;           // staged x rows: the padded batch
     constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
     static_assert(XR * KBC % NT == 0, "staging split");
-    extern __shared__ u32x4_t smem[];     // x block [XR][kStPitch], then [WAVES][2][L::kTile]
+    constexpr int XBUF = XR * kStPitch;
+    extern __shared__ u32x4_t smem[];     // x blocks [NBUF][XR][kStPitch], then [WAVES][2][L::kTile]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lr = lane & 15, lq = lane >> 4;
-    u32x4_t *xs = smem;
-    u32x4_t *ltg = smem + XR * kStPitch + (size_t)wave * 2 * L::kTile;
+    u32x4_t *ltg = smem + NBUF * XBUF + (size_t)wave * 2 * L::kTile;
     u32x4_t *ltu = ltg + L::kTile;
     const int nb = (a.C + KBC - 1) / KBC;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
@@ -2587,6 +2588,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
         }
     };
     auto store_x = [&](const u32x4_t (&xr)[XPT], int kb) {
+        u32x4_t *xs = smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
 #pragma unroll
         for (int t = 0; t < XPT; ++t) {
             const int i = t * NT + tid;
@@ -2621,6 +2623,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
             }
         };
         auto compute = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
+            const u32x4_t *xs = smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
             L::store(ltg, vg, kb, a.C, lane);
             L::store(ltu, vu, kb, a.C, lane);
 #pragma unroll
@@ -2638,12 +2641,14 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
         u32x4_t xr[XPT];
         u32x4_t vg0[L::kInsts], vu0[L::kInsts], vg1[L::kInsts], vu1[L::kInsts];
         // prefetch block kb + 1 (x first, then the weights), multiply block
-        // kb, then park x(kb + 1) once every wave is done with x(kb)
+        // kb, then park x(kb + 1) (with one buffer, once every wave is done
+        // with x(kb); with two, the other buffer was released by the barrier
+        // that ended block kb - 1)
         auto step = [&](auto &cg, auto &cu, auto &ng, auto &nu, int kb) {
             load_x(xr, kb + 1);
             load_w(ng, nu, kb + 1);
             compute(cg, cu, kb);
-            __syncthreads();
+            if constexpr (NBUF == 1) __syncthreads();
             store_x(xr, kb + 1);
             __syncthreads();
         };
@@ -3051,6 +3056,13 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 // 2048 (352 tiles) 21.5 / 23.9 / 26.3 -> 16.7 / 22.4 / 24.0 us; d_model 3072
 // at B = 32 (512 tiles) 33.5 -> 25.8 us; 2 waves at BT = 3-4 with 864-896
 // tiles were 9-11 us slower, at the 70B shape (1792 tiles) slower too
+// staged x buffers of the regular-width kernel at BT = 3 (two: one barrier
+// per block; measured at B = 48, 8B / 5120 x 13824 / 70B shapes: 48.7 /
+// 62.6 / 178.3 us against 50.5 / 64.2 / 186.0 with one; at BT = 4 two were
+// slower)
+#ifndef DFK_GU_LTS_NBUF_BT3
+#define DFK_GU_LTS_NBUF_BT3 2
+#endif
 #ifndef DFK_GU_LTS_NARROW_WAVES
 #define DFK_GU_LTS_NARROW_WAVES 2
 #endif
@@ -3536,8 +3548,10 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
         if (gu && row && BT >= 2 && BT <= DFK_GU_LTS_MAX_BT) {
             // LDS-transposed weights, x staged in LDS per workgroup
             constexpr int W = DFK_GU_LTS_WAVES, WN = DFK_GU_LTS_NARROW_WAVES;
+            constexpr int NB3 = DFK_GU_LTS_NBUF_BT3;
             static const void *const lts[2][4] = {
-                {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W>, (const void *)gate_up_mfma_lts_kernel<3, W>,
+                {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W>,
+                 (const void *)gate_up_mfma_lts_kernel<3, W, false, NB3>,
                  (const void *)gate_up_mfma_lts_kernel<4, W>},
                 {nullptr, (const void *)gate_up_mfma_lts_kernel<2, WN>, (const void *)gate_up_mfma_lts_kernel<3, WN>,
                  (const void *)gate_up_mfma_lts_kernel<4, WN>}};
@@ -3547,7 +3561,8 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             const int w = narrow ? WN : W;
             q.kind = KIND_GU_MFMA_LT;
             q.block = w * kWave;
-            q.lds_bytes = (size_t)16 * BT * kStPitch * 16 + (size_t)w * 2 * Lt<32>::kTile * 16;
+            const int nbuf = (!narrow && BT == 3) ? NB3 : 1;
+            q.lds_bytes = (size_t)nbuf * 16 * BT * kStPitch * 16 + (size_t)w * 2 * Lt<32>::kTile * 16;
             if (q.lds_bytes > kLdsLimit) return false;
             q.rows_per_group = 16;
             q.fn = lts[narrow ? 1 : 0][BT - 1];
