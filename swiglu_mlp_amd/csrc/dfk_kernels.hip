@@ -3054,23 +3054,24 @@ __global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial,
 // fewer than DFK_GU_LTS_NARROW_X2 / 2 per CU (DFK_GU_LTS_NARROW_X2_BT2 / 2 at
 // BT = 2).  Swept over the scheduler's shapes at B = 32 / 48 / 64: d_model
 // 2048 (352 tiles) 21.5 / 23.9 / 26.3 -> 16.7 / 22.4 / 24.0 us; d_model 3072
-// at B = 32 (512 tiles) 33.5 -> 25.8 us; 2 waves at BT = 3-4 with 864-896
+// (512 tiles, where 4-wave workgroups would fill half of the CUs) 33.5 /
+// 34.9 / 38.4 -> 25.8 / 34.2 / 34.4 us; 2 waves at BT = 3-4 with 864-896
 // tiles were 9-11 us slower, at the 70B shape (1792 tiles) slower too
+#ifndef DFK_GU_LTS_NARROW_WAVES
+#define DFK_GU_LTS_NARROW_WAVES 2
+#endif
+#ifndef DFK_GU_LTS_NARROW_X2
+#define DFK_GU_LTS_NARROW_X2 5
+#endif
+#ifndef DFK_GU_LTS_NARROW_X2_BT2
+#define DFK_GU_LTS_NARROW_X2_BT2 8
+#endif
 // staged x buffers of the regular-width kernel at BT = 3 (two: one barrier
 // per block; measured at B = 48, 8B / 5120 x 13824 / 70B shapes: 48.7 /
 // 62.6 / 178.3 us against 50.5 / 64.2 / 186.0 with one; at BT = 4 two were
 // slower)
 #ifndef DFK_GU_LTS_NBUF_BT3
 #define DFK_GU_LTS_NBUF_BT3 2
-#endif
-#ifndef DFK_GU_LTS_NARROW_WAVES
-#define DFK_GU_LTS_NARROW_WAVES 2
-#endif
-#ifndef DFK_GU_LTS_NARROW_X2
-#define DFK_GU_LTS_NARROW_X2 4
-#endif
-#ifndef DFK_GU_LTS_NARROW_X2_BT2
-#define DFK_GU_LTS_NARROW_X2_BT2 8
 #endif
 #ifndef DFK_MFMA_LT
 #define DFK_MFMA_LT 1

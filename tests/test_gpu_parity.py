@@ -130,6 +130,25 @@ def test_worked_example_bits(dev):
         assert list(bits[0]) == [0x3F91, 0x3FA4, 0, 0, 0, 0, 0, 0], layout.name
 
 
+# Three batch tiles (33 <= B <= 48) with at least 640 row tiles (d_ff >= 10240
+# on a 256-CU part): the regular-width staged-x gate-up kernel, whose x block
+# is double-buffered.  Odd and even block counts, ragged last block and last
+# row tile.
+LTS_BT3_SHAPES = [(33, 1032, 10248), (48, 2048, 10240), (40, 520, 14344)]
+
+
+@pytest.mark.parametrize("shape", LTS_BT3_SHAPES, ids=lambda s: "B%d_%dx%d" % s)
+def test_gate_up_three_batch_tiles_wide(dev, orc, shape):
+    B, dm, dff = shape
+    L = inputs.random_layer(B, dm, dff, seed=7300 + B)
+    T = to_dev(L, dev)
+    _, _, h_ref = orc.gate_up(L.x, L.w_gate, L.w_up)
+    y_ref, _ = orc.mlp(L.x, L.w_gate, L.w_up, L.w_down)
+    for layout in (Layout.ROW_MFMA, Layout.ROW, Layout.AUTO):
+        H.assert_h_close(gpu_gate_up(T, layout), h_ref, f"gate_up {layout.name} {shape}")
+    H.assert_y_close(H.host_bf16_as_f64(gpu_mlp(T, Layout.ROW_MFMA)), y_ref, f"mlp ROW_MFMA {shape}")
+
+
 @pytest.mark.parametrize("B", [1, 4, 8, 16, 64])
 def test_integer_down_is_bitwise_exact(dev, orc, B):
     """Integer h (|h| <= 256) and W_down in {-1,0,1}: fp32 accumulation is exact
