@@ -2973,15 +2973,43 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_coop_kernel(DownArgs 
 }
 
 // y[i] = RNE_bf16(sum_{s ascending} partial[s][i]) for i < n (n % 4 == 0),
-// four outputs per thread.
-__global__ __launch_bounds__(256) void panel_reduce_kernel(const float *partial, uint16_t *y, int S, int n) {
+// four outputs per thread.  The partial sums were written by workgroups on
+// every die, so each load goes to the memory-side cache or HBM: a thread
+// issues DFK_REDUCE_BATCH of its loads before it adds them (still in
+// ascending s), and small workgroups spread the few threads over many CUs.
+#ifndef DFK_REDUCE_BLOCK
+#define DFK_REDUCE_BLOCK 64
+#endif
+#ifndef DFK_REDUCE_BATCH
+#define DFK_REDUCE_BATCH 8
+#endif
+constexpr int kReduceBlock = DFK_REDUCE_BLOCK;
+
+__global__ __launch_bounds__(kReduceBlock) void panel_reduce_kernel(const float *partial, uint16_t *y, int S, int n) {
     const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i >= n) return;
-    f32x4_t v = *reinterpret_cast<const f32x4_t *>(partial + i);
-    for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4_t *>(partial + (size_t)s * n + i);
+    const f32x4_t *p = reinterpret_cast<const f32x4_t *>(partial + i);
+    const size_t stride = (size_t)n / 4;  // one split, in 16-byte vectors
+    constexpr int kBatch = DFK_REDUCE_BATCH;
+    f32x4_t v = p[0];
+    for (int s0 = 1; s0 < S; s0 += kBatch) {
+        f32x4_t t[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (s0 + q < S) t[q] = p[(size_t)(s0 + q) * stride];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (s0 + q < S) v += t[q];
+    }
     const unsigned lo = to_bf16_rne(v[0]) | ((unsigned)to_bf16_rne(v[1]) << 16);
     const unsigned hi = to_bf16_rne(v[2]) | ((unsigned)to_bf16_rne(v[3]) << 16);
     *reinterpret_cast<uint2 *>(y + i) = make_uint2(lo, hi);
+}
+
+static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n, hipStream_t stream) {
+    void *rargv[] = {&partial, &y, &S, &n};
+    return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)((n / 4 + kReduceBlock - 1) / kReduceBlock)),
+                           dim3(kReduceBlock), rargv, 0, stream);
 }
 
 // ======================================================== kernel tables ====
@@ -3818,11 +3846,7 @@ hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down,
         void *argv[] = {&a, &part, &S, &CS};
         hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
         if (e != hipSuccess || S == 1) return e;
-        int n = p.B * p.rows;
-        const float *cpartial = partial;
-        void *rargv[] = {&cpartial, &y, &S, &n};
-        return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256),
-                               rargv, 0, stream);
+        return launch_reduce(partial, y, S, p.B * p.rows, stream);
     }
     if (p.kind != KIND_DN_FP8_ROW) return hipErrorInvalidValue;
     if (p.splits > 1 && !partial) return hipErrorInvalidValue;
@@ -3833,11 +3857,7 @@ hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down,
     void *argv[] = {&a, &partial, &cs};
     hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid, p.splits), dim3(p.block), argv, p.lds_bytes, stream);
     if (e != hipSuccess || p.splits == 1) return e;
-    int S = p.splits, n = p.B * p.rows;
-    const float *cpartial = partial;
-    void *rargv[] = {&cpartial, &y, &S, &n};
-    return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256), rargv,
-                           0, stream);
+    return launch_reduce(partial, y, p.splits, p.B * p.rows, stream);
 }
 
 hipError_t launch_gate_up(const Plan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
@@ -3877,11 +3897,7 @@ hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, ui
         void *argv[] = {&a, &partial, &cs};
         hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid, p.splits), dim3(p.block), argv, p.lds_bytes, stream);
         if (e != hipSuccess) return e;
-        int S = p.splits, n = p.B * p.rows;
-        const float *cpartial = partial;
-        void *rargv[] = {&cpartial, &y, &S, &n};
-        return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256),
-                               rargv, 0, stream);
+        return launch_reduce(partial, y, p.splits, p.B * p.rows, stream);
     }
     if (p.kind != KIND_DN_MFMA_STAGED) {
         void *argv[] = {&a};
@@ -3897,11 +3913,7 @@ hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, ui
     void *argv[] = {&a, &partial, &S, &CS};
     hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
     if (e != hipSuccess) return e;
-    int n = p.B * p.rows;
-    const float *cpartial = partial;
-    void *rargv[] = {&cpartial, &y, &S, &n};
-    return hipLaunchKernel((const void *)panel_reduce_kernel, dim3((unsigned)ceil_div(n / 4, 256)), dim3(256), rargv,
-                           0, stream);
+    return launch_reduce(partial, y, S, p.B * p.rows, stream);
 }
 
 }  // namespace dfk
