@@ -2565,12 +2565,19 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
     constexpr int XR = 16 * BT;           // staged x rows: the padded batch
     constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
     static_assert(XR * KBC % NT == 0, "staging split");
+    static_assert(!(F8 && NBUF == 2), "FP8 instances keep one x buffer");
     constexpr int XBUF = XR * kStPitch;
     extern __shared__ u32x4_t smem[];     // x blocks [NBUF][XR][kStPitch], then [WAVES][2][L::kTile]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lr = lane & 15, lq = lane >> 4;
+    // F8 (one x buffer) reaches its x block through xs, the bf16 kernels
+    // through smem directly: the same addresses, but the two forms compile
+    // to different schedules, and each is the faster one for its weights
+    // (measured at the Llama-3-8B shape: FP8 at B = 64 49.9 us against
+    // 56.8 us; bf16 at B = 17-32 with few row tiles 0.5-1.5 us faster)
+    u32x4_t *xs = smem;
     u32x4_t *ltg = smem + NBUF * XBUF + (size_t)wave * 2 * L::kTile;
     u32x4_t *ltu = ltg + L::kTile;
     const int nb = (a.C + KBC - 1) / KBC;
@@ -2588,13 +2595,13 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
         }
     };
     auto store_x = [&](const u32x4_t (&xr)[XPT], int kb) {
-        u32x4_t *xs = smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
+        u32x4_t *xd = F8 ? xs : smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
 #pragma unroll
         for (int t = 0; t < XPT; ++t) {
             const int i = t * NT + tid;
             const int b = i / KBC, cc = i % KBC;
             const bool ok = b < a.B && kb * KBC + cc < a.C;
-            xs[b * kStPitch + cc] = ok ? xr[t] : zero;
+            xd[b * kStPitch + cc] = ok ? xr[t] : zero;
         }
     };
 
@@ -2623,7 +2630,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
             }
         };
         auto compute = [&](u32x4_t (&vg)[L::kInsts], u32x4_t (&vu)[L::kInsts], int kb) {
-            const u32x4_t *xs = smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
+            const u32x4_t *xd = F8 ? xs : smem + (NBUF == 2 ? (kb & 1) : 0) * XBUF;
             L::store(ltg, vg, kb, a.C, lane);
             L::store(ltu, vu, kb, a.C, lane);
 #pragma unroll
@@ -2632,7 +2639,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
                 const bf16x8_t au = L::frag(ltu, j, lr, lq);
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
-                    const bf16x8_t xb = as_bf16x8(xs[(bt * 16 + lr) * kStPitch + 4 * j + lq]);
+                    const bf16x8_t xb = as_bf16x8(xd[(bt * 16 + lr) * kStPitch + 4 * j + lq]);
                     accg[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb, accg[bt], 0, 0, 0);
                     accu[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb, accu[bt], 0, 0, 0);
                 }
