@@ -186,7 +186,7 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * registers (the down projection's column traversal).  Layouts:
  * AUTO = the measured best at the Llama-3-8B layer shape (gate-up: vector
  * ALU to B = 3, matrix-core column traversal to B = 16, row traversal above;
- * down: vector ALU to B = 3, matrix-core column traversal above); ROW =
+ * down: vector ALU to B = 2, matrix-core column traversal above); ROW =
  * vector ALU up to B = 8, else matrix cores; COL = matrix
  * cores; ROW_VALU, ROW_MFMA, COL_MFMA force the engine; COL_VALU and
  * ROW_PERSISTENT are DFK_ERR_UNSUPPORTED.  d_model and d_ff must be
