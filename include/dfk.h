@@ -33,6 +33,17 @@
  *     vectors), d_model * d_ff < 2^31.
  *   - Inputs are assumed finite; NaN or Inf propagate through the arithmetic
  *     and are not checked.
+ *   - Library-owned workspace (h between the two kernels, K-split partial
+ *     sums): one buffer per (device, stream), allocated on the first call
+ *     that needs it and grown (at least doubled) by a later call that needs
+ *     more.  Growing never frees the earlier buffer, since work already queued
+ *     or a HIP graph captured on the stream may still use it; all of a
+ *     device's buffers are freed by dfk_release_workspace.  While `stream` is
+ *     being captured into a graph nothing is allocated: a call that would
+ *     have to grow the workspace returns DFK_ERR_UNSUPPORTED and enqueues
+ *     nothing (make one eager call of the largest shape on the stream before
+ *     capturing).  A graph uses the workspace of the stream it was captured
+ *     on: its replays must not overlap other work of that stream.
  */
 #ifndef DFK_H
 #define DFK_H
@@ -48,7 +59,8 @@ extern "C" {
 
 /*
  * Weight-traversal variant ("Deep Kernel Fusion for Transformer Decoding",
- * episode summary: row-major and column-major kernel variants).  Weights are
+ * episode summary: the kernel comes in two variants, one walking the weights
+ * by rows and one by columns).  Weights are
  * always stored row-major ([out, in], as nn.Linear keeps them); the layout
  * picks how a kernel walks them.  ROW: a wave or workgroup owns whole output
  * rows and walks all of K.  COL: K is split, among the waves of a workgroup or
@@ -119,7 +131,7 @@ dfk_status_t dfk_gate_up_silu_mul(const uint16_t *x, const uint16_t *W_gate,
  * workgroups (the vector-ALU row walk when h exceeds its LDS budget, and
  * the matrix-core column traversal) add the split sums with a second, small
  * kernel on the same stream, in split order; their scratch (splits * B *
- * d_model * 4 bytes) is library-owned per (device, stream).  The other
+ * d_model * 4 bytes) is the library-owned workspace (above).  The other
  * variants are one launch with no scratch memory.
  */
 dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out, int B,
@@ -127,9 +139,9 @@ dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out
 
 /*
  * The whole MLP: dfk_gate_up_silu_mul then dfk_down_proj on the same stream,
- * with h in a library-owned fp32 workspace (B * d_ff * 4 bytes) kept per
- * (device, stream) and grown on demand; it lives until the library is
- * unloaded.  Two launches per call.  The layout applies to both kernels; with
+ * with h in the library-owned workspace (B * d_ff * 4 bytes, plus the down
+ * projection's split sums; see the conventions above).  Two launches per
+ * call (three when down adds K splits).  The layout applies to both kernels; with
  * AUTO each kernel takes the scheduler's own choice.
  */
 dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up,
@@ -254,9 +266,9 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
 
 /*
  * Profiler-driven variant choice ("Deep Kernel Fusion for Transformer
- * Decoding", episode summary: runtime scheduling across row-major and
- * column-major kernel variants; "Deep Kernel Fusion for Transformers",
- * abstract: a kernel scheduler).  Host only; never touches the device.
+ * Decoding", episode summary: profiling decides, while serving, which of the
+ * row- and column-walking kernel variants runs; "Deep Kernel Fusion for
+ * Transformers", abstract: a kernel scheduler).  Host only; never touches the device.
  * Looks the shape up in the tuning table (the file named by the environment
  * variable DFK_TUNING_TABLE, else the table installed beside the library):
  * exact (B, d_model, d_ff) entry, else the entry for the same (d_model, d_ff)
@@ -291,9 +303,11 @@ dfk_status_t dfk_load_tuning_table(const char *path);
 const char *dfk_tuning_table_source(void);
 
 /*
- * Release the workspaces the library holds for the current device (waits for
- * the device first).  Optional: they are also released when the library is
- * unloaded.
+ * Free every workspace buffer the library holds for the current device (the
+ * current ones and those retired by growth), after waiting for the device.
+ * HIP graphs captured against them must not be replayed afterwards; later
+ * calls allocate afresh.  Without this call the buffers are held until the
+ * process ends.
  */
 dfk_status_t dfk_release_workspace(void);
 

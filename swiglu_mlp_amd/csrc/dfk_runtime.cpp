@@ -74,15 +74,24 @@ int device_cus(int dev) {
 // ------------------------------------------------------------ workspace ---
 //
 // dfk_swiglu_mlp keeps h (fp32 [B, d_ff]) in a library-owned buffer per
-// (device, stream), and the K-panel kernels keep their partial sums there.  Kernels on one stream run in order, so one buffer per
-// stream is enough; calls on one stream from several host threads serialise
-// on the slot's mutex while they enqueue.  Growing frees the old buffer
-// (hipFree waits for the device).
+// (device, stream), and the K-split kernels keep their partial sums there.
+// Kernels on one stream run in order, so one buffer per stream is enough;
+// calls on one stream from several host threads serialise on the slot's mutex
+// while they enqueue.
+//
+// A buffer the slot has handed out may be referenced by work still queued and
+// by HIP graphs captured on the stream, which keep the address they saw.  So
+// growing never frees: the old buffer is retired, and retired buffers are
+// freed only by dfk_release_workspace (after a device synchronisation).  Sizes
+// at least double, so a slot's retired buffers add up to less than its
+// current one.  While the stream is being captured nothing is allocated: a
+// call that would need a larger buffer is refused.
 
 struct Slot {
     std::mutex mu;
     void *data = nullptr;
     size_t bytes = 0;
+    std::vector<void *> retired;  // earlier, smaller buffers (graphs may hold them)
     unsigned *barrier = nullptr;  // the persistent kernel's grid-barrier state
 };
 
@@ -96,20 +105,39 @@ Slot *slot_for(int dev, hipStream_t stream) {
     return p.get();
 }
 
+// Capture state of a stream: 0 not capturing, 1 capturing (or, for the null
+// stream, another stream's capture forbids implicit synchronisation with it),
+// -1 the query failed.
+int capture_state(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return e == hipErrorStreamCaptureImplicit ? 1 : -1;
+    }
+    return st != hipStreamCaptureStatusNone ? 1 : 0;
+}
+
 // Caller holds slot->mu.
-dfk_status_t ensure_workspace(Slot *slot, size_t bytes, void **out) {
+dfk_status_t ensure_workspace(Slot *slot, size_t bytes, hipStream_t stream, void **out) {
     if (bytes > slot->bytes) {
-        if (slot->data) {
-            if (hipFree(slot->data) != hipSuccess) return DFK_ERR_HIP;
-            slot->data = nullptr;
-            slot->bytes = 0;
-        }
-        const size_t grow = std::max(bytes, size_t(1) << 20);
-        if (hipMalloc(&slot->data, grow) != hipSuccess) {
-            slot->data = nullptr;
+        const int cap = capture_state(stream);
+        if (cap < 0) return DFK_ERR_HIP;
+        if (cap > 0) return DFK_ERR_UNSUPPORTED;  // no allocation inside a capture
+        size_t grow = std::max(std::max(bytes, 2 * slot->bytes), size_t(1) << 20);
+        void *p = nullptr;
+        if (hipMalloc(&p, grow) != hipSuccess) {
             (void)hipGetLastError();
-            return DFK_ERR_OOM;
+            p = nullptr;
+            // the doubled size may not fit where the request does
+            if (grow == bytes || hipMalloc(&p, bytes) != hipSuccess) {
+                (void)hipGetLastError();
+                return DFK_ERR_OOM;
+            }
+            grow = bytes;
         }
+        if (slot->data) slot->retired.push_back(slot->data);
+        slot->data = p;
         slot->bytes = grow;
     }
     *out = slot->data;
@@ -136,12 +164,7 @@ dfk_status_t ensure_barrier(Slot *slot, hipStream_t stream, unsigned **out) {
 }
 
 bool stream_capturing(hipStream_t stream) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
-        (void)hipGetLastError();
-        return true;  // unknown: treat as capturing (no cooperative launch)
-    }
-    return st != hipStreamCaptureStatusNone;
+    return capture_state(stream) != 0;  // unknown: treat as capturing (no cooperative launch)
 }
 
 // ------------------------------------------------------------ tiny JSON ---
@@ -490,7 +513,7 @@ dfk_status_t gate_up_impl(const uint16_t *x, const uint16_t *W_gate, const uint1
             slot = slot_for(dev, stream);
             lock = std::unique_lock<std::mutex>(slot->mu);
             void *ws = nullptr;
-            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), stream, &ws)) != DFK_OK) return st;
             partial = static_cast<float *>(ws);
         }
         if (dfk::launch_gate_up(p, x, W_gate, W_up, h, partial, stream, nullptr, ldw) != hipSuccess)
@@ -525,7 +548,7 @@ dfk_status_t mlp_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t 
             std::lock_guard<std::mutex> lock(slot->mu);
             void *ws = nullptr;
             unsigned *barrier = nullptr;
-            if ((st = ensure_workspace(slot, (size_t)B * d_ff * sizeof(float), &ws)) != DFK_OK) return st;
+            if ((st = ensure_workspace(slot, (size_t)B * d_ff * sizeof(float), stream, &ws)) != DFK_OK) return st;
             if ((st = ensure_barrier(slot, stream, &barrier)) != DFK_OK) return st;
             if (dfk::launch_mlp(mp, x, W_gate, W_up, W_down, static_cast<float *>(ws), out, barrier, stream) !=
                 hipSuccess) {
@@ -545,7 +568,7 @@ dfk_status_t mlp_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t 
         const size_t h_bytes = ((size_t)B * d_ff * sizeof(float) + 255) & ~size_t(255);
         // the two kernels run in stream order, so their panel partials share one region
         const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
-        if ((st = ensure_workspace(slot, h_bytes + partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+        if ((st = ensure_workspace(slot, h_bytes + partial_floats * sizeof(float), stream, &ws)) != DFK_OK) return st;
         float *h = static_cast<float *>(ws);
         float *partial = partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
         if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream, nullptr, ldw) != hipSuccess)
@@ -670,7 +693,7 @@ dfk_status_t dfk_down_proj(const float *h, const uint16_t *W_down, uint16_t *out
             slot = slot_for(dev, stream);
             lock = std::unique_lock<std::mutex>(slot->mu);
             void *ws = nullptr;
-            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), stream, &ws)) != DFK_OK) return st;
             partial = static_cast<float *>(ws);
         }
         if (dfk::launch_down(p, h, W_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
@@ -784,7 +807,7 @@ dfk_status_t dfk_rmsnorm_gate_up_silu_mul(const uint16_t *x, const uint16_t *gai
             slot = slot_for(dev, stream);
             lock = std::unique_lock<std::mutex>(slot->mu);
             void *w = nullptr;
-            if ((st = ensure_workspace(slot, bytes, &w)) != DFK_OK) return st;
+            if ((st = ensure_workspace(slot, bytes, stream, &w)) != DFK_OK) return st;
             ws = static_cast<char *>(w);
         }
         float *partial = p.partial_floats ? reinterpret_cast<float *>(ws + xn_bytes) : nullptr;
@@ -829,7 +852,7 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
         const size_t xn_bytes = pg.fused_norm ? 0 : round256((size_t)B * d_model * 2);
         const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
         void *w = nullptr;
-        if ((st = ensure_workspace(slot, h_bytes + xn_bytes + partial_floats * sizeof(float), &w)) != DFK_OK)
+        if ((st = ensure_workspace(slot, h_bytes + xn_bytes + partial_floats * sizeof(float), stream, &w)) != DFK_OK)
             return st;
         char *ws = static_cast<char *>(w);
         float *h = reinterpret_cast<float *>(ws);
@@ -923,7 +946,7 @@ dfk_status_t dfk_down_proj_fp8(const float *h, const uint8_t *Wq_down, const flo
             slot = slot_for(dev, stream);
             lock = std::unique_lock<std::mutex>(slot->mu);
             void *ws = nullptr;
-            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+            if ((st = ensure_workspace(slot, p.partial_floats * sizeof(float), stream, &ws)) != DFK_OK) return st;
             partial = static_cast<float *>(ws);
         }
         if (dfk::launch_down_fp8(p, h, Wq_down, s_down, out, partial, stream) != hipSuccess) return DFK_ERR_HIP;
@@ -954,7 +977,7 @@ dfk_status_t dfk_swiglu_mlp_fp8(const uint16_t *x, const uint8_t *Wq_gate, const
         std::lock_guard<std::mutex> lock(slot->mu);
         void *ws = nullptr;
         const size_t h_bytes = round256((size_t)B * d_ff * sizeof(float));
-        if ((st = ensure_workspace(slot, h_bytes + pd.partial_floats * sizeof(float), &ws)) != DFK_OK) return st;
+        if ((st = ensure_workspace(slot, h_bytes + pd.partial_floats * sizeof(float), stream, &ws)) != DFK_OK) return st;
         float *h = static_cast<float *>(ws);
         float *partial = pd.partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
         if (dfk::launch_gate_up_fp8(pg, x, Wq_gate, s_gate, Wq_up, s_up, h, stream) != hipSuccess) return DFK_ERR_HIP;
@@ -979,6 +1002,9 @@ dfk_status_t dfk_release_workspace(void) {
             }
             {
                 std::lock_guard<std::mutex> l2(it->second->mu);
+                for (void *old : it->second->retired)
+                    if (hipFree(old) != hipSuccess) st = DFK_ERR_HIP;
+                it->second->retired.clear();
                 if (it->second->data && hipFree(it->second->data) != hipSuccess) st = DFK_ERR_HIP;
                 if (it->second->barrier && hipFree(it->second->barrier) != hipSuccess) st = DFK_ERR_HIP;
                 it->second->data = nullptr;

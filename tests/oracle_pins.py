@@ -274,6 +274,23 @@ def check_rms_rescale(orc):
     # a row that is a power-of-two multiple of a ones vector maps to exactly ones
     ones = bf16_of(np.full((1, 64), 8.0))
     assert np.all(widen(orc.rms_rescale(ones, eps=0.0)) == 1.0)
+    # eps > 0 against 60-digit arithmetic and an independent ties-to-even
+    # rounding, on rows whose mean square is of the order of eps (so eps
+    # placed outside the square root, or dropped, moves every value)
+    mpmath.mp.dps = 60
+    try:
+        small = inputs.randn_bf16((2, 48), 0.01, seed=801)
+        sf = widen(small)
+        for eps in (1e-4, 1e-6, 0.5):
+            got = orc.rms_rescale(small, eps=eps)
+            for b in range(2):
+                ms = mpmath.fsum(mpmath.mpf(float(v)) ** 2 for v in sf[b]) / 48
+                inv = 1 / mpmath.sqrt(ms + mpmath.mpf(eps))
+                for k in range(48):
+                    want = _mp_rne_bf16_bits(mpmath.mpf(float(sf[b, k])) * inv)
+                    assert int(got[b, k]) == want, (eps, b, k)
+    finally:
+        mpmath.mp.dps = 40
 
 
 def _mp_rne_bf16_bits(v):

@@ -36,6 +36,10 @@ MUTANTS = {
                        "double inv = 1.0 / sqrt(ss / (double)d_model);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
     "rmsnorm_no_sqrt": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn[",
                         "double inv = 1.0 / (ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            xn["),
+    "rescale_eps_outside_sqrt": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            x_next[",
+                                 "double inv = 1.0 / sqrt(ss / (double)d_model) + eps;\n        for (int k = 0; k < d_model; ++k)\n            x_next["),
+    "rescale_no_eps": ("double inv = 1.0 / sqrt(ss / (double)d_model + eps);\n        for (int k = 0; k < d_model; ++k)\n            x_next[",
+                       "double inv = 1.0 / sqrt(ss / (double)d_model);\n        for (int k = 0; k < d_model; ++k)\n            x_next["),
     "rmsnorm_gain_first_only": ("* widen_bf16(gain[k])", "* widen_bf16(gain[0])"),
     "rmsnorm_batch_stride": ("const uint16_t *row = x + (size_t)b * d_model;", "const uint16_t *row = x + (size_t)b;"),
     "fp8_bias_8": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
