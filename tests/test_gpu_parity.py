@@ -206,9 +206,9 @@ def uses_mfma(layout, B):
 def test_linearity_in_w_down_bitwise(dev, B):
     """y(2 W_down) = 2 y(W_down) bit for bit on every variant, and
     y(-W_down) = -y(W_down) bit for bit on the IEEE fp32 (VALU) path.  The
-    matrix cores' internal accumulation is not sign-symmetric (measured: a
-    rare 1-ulp difference), so on MFMA variants negation holds to one bf16
-    ulp per element."""
+    matrix cores' accumulation is not sign-symmetric (isolated in
+    test_sign_asymmetry_of_the_accumulators below), so on MFMA variants
+    negation holds to one bf16 ulp per element."""
     L = inputs.random_layer(B, 1032, 1000, seed=8400 + B)
     T = to_dev(L, dev)
     T2 = dict(T, w_down=(T["w_down"].float() * 2).to(torch.bfloat16))
@@ -223,6 +223,67 @@ def test_linearity_in_w_down_bitwise(dev, B):
             assert torch.all((yn + y).abs() <= bf16_ulp(y)), layout.name
         else:
             assert torch.equal(yn, -y), layout.name
+
+
+# Rows of W_up whose sum u = sum_k W_up[n, k] (x all ones) is the exact value
+# 1 + 2^-23 + 2^-24 - 2^-40, just below the fp32 tie between 1 + 2^-23 and
+# 1 + 2^-22, so correct rounding gives 0x3f800001; the terms sit in one or
+# two 32-element K steps of the matrix-core contraction (and one or two
+# 8-element lane chunks of the vector-ALU walk).
+_SIGN_ROWS = {
+    "a": {0: 1.0, 1: 2.0 ** -23, 32: 2.0 ** -24, 33: -2.0 ** -40},   # two K steps
+    "b": {0: -2.0 ** -40, 32: 1.0, 33: 2.0 ** -23, 34: 2.0 ** -24},  # tiny term first
+    "c": {0: 1.0, 1: 2.0 ** -23, 2: 2.0 ** -24, 3: -2.0 ** -40},     # one K step, one lane
+}
+# (u, u with W_up negated) as fp32 bits, measured on MI355X.
+_SIGN_BITS = {
+    "valu": {"a": (0x3F800001, 0xBF800001), "b": (0x3F800002, 0xBF800002), "c": (0x3F800001, 0xBF800002)},
+    "mfma": {"a": (0x3F800001, 0xBF800002), "b": (0x3F800001, 0xBF800002), "c": (0x3F800002, 0xBF800002)},
+}
+
+
+def test_sign_asymmetry_of_the_accumulators(dev):
+    """The smallest library calls that show why negating a weight matrix is
+    not bit-exact on every engine.  With x = 1 and W_gate[n] = (64, 0, ...),
+    g = 64 and SiLU(64) = 64 exactly in fp32, so h / 64 is u's fp32 sum.
+
+    - Vector ALU (bf16 dot2 into an fp32 lane sum, then an fp32 lane
+      reduction): row c, whose tiny opposite-signed term shares a dot2 with
+      the tie-making term, rounds toward minus infinity (two's complement
+      truncation of the aligned addend): 0x3f800001 but 0xbf800002.
+    - Matrix cores (v_mfma_f32_16x16x32_bf16): inside one instruction the
+      products' tiny term is dropped toward zero (row c: symmetric, tie to
+      even), but when the products are added to a non-zero accumulator from
+      an earlier K step (rows a, b) the tiny opposite-signed term again
+      rounds toward minus infinity: asymmetric.
+    - The fp32 FMA of the vector-ALU down projection is IEEE and symmetric
+      (test_linearity_in_w_down_bitwise holds negation bit for bit there).
+    All of these stay within one ulp of the correctly rounded sum."""
+    K, N = 256, 16
+    x = torch.ones((1, K), dtype=torch.bfloat16, device=dev)
+    wg = torch.zeros((N, K), dtype=torch.float32)
+    wg[:, 0] = 64.0
+    wu = torch.zeros((N, K), dtype=torch.float32)
+    names = sorted(_SIGN_ROWS)
+    for n, name in enumerate(names):
+        for k, v in _SIGN_ROWS[name].items():
+            wu[n, k] = v
+    assert torch.equal(wu.to(torch.bfloat16).float(), wu)  # every term is a bf16 value
+    wg_d = wg.to(torch.bfloat16).to(dev)
+    for engine, layouts in (("valu", [Layout.ROW_VALU, Layout.COL_VALU]),
+                            ("mfma", [Layout.ROW_MFMA, Layout.COL_MFMA])):
+        for layout in layouts:
+            got = {}
+            for sign in (1.0, -1.0):
+                h = dfk.dfk_gate_up_silu_mul(x, wg_d, (sign * wu).to(torch.bfloat16).to(dev), layout=layout)
+                torch.cuda.synchronize()
+                u = (h[0].cpu() / 64.0).numpy().astype(np.float32).view(np.uint32)
+                got[sign] = u
+            for n, name in enumerate(names):
+                want = _SIGN_BITS[engine][name]
+                assert (int(got[1.0][n]), int(got[-1.0][n])) == want, (layout.name, name, hex(got[1.0][n]),
+                                                                         hex(got[-1.0][n]))
+            assert np.all(got[1.0][len(names):] == 0) and np.all(got[-1.0][len(names):] == 0)
 
 
 def test_run_to_run_determinism(dev):
