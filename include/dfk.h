@@ -148,6 +148,34 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
                             const uint16_t *W_down, uint16_t *out, int B, int d_model,
                             int d_ff, dfk_layout_t layout, hipStream_t stream);
 
+/* Bytes of the static device buffer behind dfk_swiglu_mlp_noalloc (per device). */
+#define DFK_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * dfk_swiglu_mlp for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results (bit for bit) as
+ * dfk_swiglu_mlp with the same layout; h and the down projection's split sums
+ * live in a buffer of DFK_NOALLOC_SCRATCH_BYTES that the library keeps in
+ * static device memory (each device holds its own copy until the process
+ * ends) instead of the growable per-stream workspace.  It never calls
+ * hipMalloc, hipFree or any other allocating routine.  The first call on a
+ * device looks the buffer's address up (hipGetSymbolAddress) and caches it;
+ * make that first call outside a graph capture.
+ *   - A call whose h (B * d_ff * 4 bytes, rounded up to 256) plus split sums
+ *     exceed the buffer returns DFK_ERR_UNSUPPORTED with nothing enqueued
+ *     (every Llama-3-8B and -70B layer shape fits up to B = 64).
+ *   - Every call on a device shares that device's buffer, which keeps the
+ *     last call's contents; nothing in it needs to start at zero.  Calls that
+ *     can overlap on one device (other streams, graph replays beside eager
+ *     calls) race on it: the caller must order them.
+ *   - DFK_LAYOUT_ROW_PERSISTENT is DFK_ERR_UNSUPPORTED; other errors as for
+ *     dfk_swiglu_mlp.
+ */
+dfk_status_t dfk_swiglu_mlp_noalloc(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up,
+                                    const uint16_t *W_down, uint16_t *out, int B, int d_model,
+                                    int d_ff, dfk_layout_t layout, hipStream_t stream);
+
 /*
  * How W_gate and W_up share one packed weight tensor W_gu [2 * d_ff, d_model]
  * ("Optimizing QKV Projection with Operator Fusion", "Implementing Fusion:

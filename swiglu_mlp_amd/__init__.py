@@ -60,6 +60,7 @@ EXPORTED = (
     "dfk_tuning_table_source", "dfk_release_workspace", "dfk_rmsnorm",
     "dfk_rmsnorm_gate_up_silu_mul", "dfk_rmsnorm_swiglu_mlp", "dfk_gate_up_silu_mul_packed",
     "dfk_swiglu_mlp_packed", "dfk_gate_up_silu_mul_fp8", "dfk_down_proj_fp8", "dfk_swiglu_mlp_fp8",
+    "dfk_swiglu_mlp_noalloc",
 )
 
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.dfk_down_proj.restype = i
     L.dfk_swiglu_mlp.argtypes = [u16p, u16p, u16p, u16p, u16p, i, i, i, i, vp]
     L.dfk_swiglu_mlp.restype = i
+    L.dfk_swiglu_mlp_noalloc.argtypes = [u16p, u16p, u16p, u16p, u16p, i, i, i, i, vp]
+    L.dfk_swiglu_mlp_noalloc.restype = i
     L.dfk_schedule_select.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     L.dfk_schedule_select.restype = i
     L.dfk_status_string.argtypes = [i]
@@ -211,6 +214,24 @@ def dfk_swiglu_mlp(x, W_gate, W_up, W_down, out=None, layout: int = Layout.AUTO,
                               out.data_ptr(), B, d_model, d_ff, int(layout),
                               _stream_handle(stream, x.device))
     _check(st, "dfk_swiglu_mlp")
+    return out
+
+
+def dfk_swiglu_mlp_noalloc(x, W_gate, W_up, W_down, out, layout: int = Layout.AUTO, stream=None):
+    """dfk_swiglu_mlp with h and the split sums in the library's static device
+    scratch: the library allocates nothing (the caller passes `out`)."""
+    import torch
+    B, d_model = x.shape
+    d_ff = W_gate.shape[0]
+    _expect(x, "x", torch.bfloat16, (B, d_model))
+    _expect(W_gate, "W_gate", torch.bfloat16, (d_ff, d_model))
+    _expect(W_up, "W_up", torch.bfloat16, (d_ff, d_model))
+    _expect(W_down, "W_down", torch.bfloat16, (d_model, d_ff))
+    _expect(out, "out", torch.bfloat16, (B, d_model))
+    st = lib().dfk_swiglu_mlp_noalloc(x.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(), W_down.data_ptr(),
+                                      out.data_ptr(), B, d_model, d_ff, int(layout),
+                                      _stream_handle(stream, x.device))
+    _check(st, "dfk_swiglu_mlp_noalloc")
     return out
 
 

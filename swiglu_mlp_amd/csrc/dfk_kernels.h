@@ -120,6 +120,14 @@ bool make_mlp_plan(int B, int d_model, int d_ff, int cus, MlpPlan *plan);
 constexpr int kBarrierWords = (16 + 1 + 16) * 32;
 hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gate, const uint16_t *w_up,
                       const uint16_t *w_down, float *h, uint16_t *y, unsigned *barrier, hipStream_t stream);
+// Fixed-size scratch in static device memory for the entry point that
+// allocates nothing (h and the split sums of one whole-MLP call).  Each
+// device holds its own copy for the life of the process.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+// The scratch's device address on device `dev`, which must be the current
+// device: looked up with hipGetSymbolAddress on the first request for that
+// device and cached; later requests only read the cache.
+hipError_t static_scratch(int dev, void **ptr);
 // `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y,
                        float *partial, hipStream_t stream);

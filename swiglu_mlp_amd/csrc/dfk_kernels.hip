@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
 
 #include "dfk_kernels.h"
@@ -3921,6 +3922,36 @@ hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, ui
     hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
     if (e != hipSuccess) return e;
     return launch_reduce(partial, y, S, p.B * p.rows, stream);
+}
+
+// --------------------------------------------- static scratch (no alloc) --
+//
+// The whole-MLP entry point for callers that cannot allocate keeps h and the
+// down projection's split sums here instead of in the library's growable
+// workspace.  Host code must never pass `scratch` itself to a kernel: on the
+// host the name stands for a host-side shadow, not a device address.  Kernels
+// get the address that hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(int dev, void **ptr) {
+    static std::mutex mu;
+    static std::map<int, void *> addr;  // device -> address of its copy
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(dev);
+    if (it != addr.end()) {
+        *ptr = it->second;
+        return hipSuccess;
+    }
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    }
+    addr[dev] = p;
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace dfk

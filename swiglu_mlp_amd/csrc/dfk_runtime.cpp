@@ -522,10 +522,12 @@ dfk_status_t gate_up_impl(const uint16_t *x, const uint16_t *W_gate, const uint1
     }
 }
 
-// dfk_swiglu_mlp with W_gate / W_up rows `ldw` elements apart.
+// dfk_swiglu_mlp with W_gate / W_up rows `ldw` elements apart.  noalloc: h
+// and the split sums go to the device's static scratch (never allocated,
+// never locked) instead of the stream's workspace.
 dfk_status_t mlp_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up, int ldw,
                       const uint16_t *W_down, uint16_t *out, int B, int d_model, int d_ff, dfk_layout_t layout,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool noalloc = false) {
     {
         if (!x || !W_gate || !W_up || !W_down || !out || !valid_layout(layout)) return DFK_ERR_INVALID_ARG;
         dfk_status_t st = check_dims(B, d_model, d_ff);
@@ -536,7 +538,7 @@ dfk_status_t mlp_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t 
         if ((st = current_device(&dev)) != DFK_OK) return st;
         const int cus = device_cus(dev);
         if (layout == DFK_LAYOUT_ROW_PERSISTENT) {
-            if (ldw != d_model) return DFK_ERR_UNSUPPORTED;  // dense gate / up only
+            if (ldw != d_model || noalloc) return DFK_ERR_UNSUPPORTED;  // dense gate / up, own barrier state
             dfk::MlpPlan mp;
             if (!dfk::make_mlp_plan(B, d_model, d_ff, cus, &mp)) return DFK_ERR_UNSUPPORTED;
             // a cooperative launch is not captured into graphs here
@@ -562,13 +564,20 @@ dfk_status_t mlp_impl(const uint16_t *x, const uint16_t *W_gate, const uint16_t 
         if ((st = resolve(dfk::OP_DOWN, layout, B, d_model, d_ff, cus, &pd)) != DFK_OK) return st;
         log_plan("gate_up", pg);
         log_plan("down", pd);
-        Slot *slot = slot_for(dev, stream);
-        std::lock_guard<std::mutex> lock(slot->mu);
         void *ws = nullptr;
         const size_t h_bytes = ((size_t)B * d_ff * sizeof(float) + 255) & ~size_t(255);
         // the two kernels run in stream order, so their panel partials share one region
         const size_t partial_floats = std::max(pg.partial_floats, pd.partial_floats);
-        if ((st = ensure_workspace(slot, h_bytes + partial_floats * sizeof(float), stream, &ws)) != DFK_OK) return st;
+        const size_t need = h_bytes + partial_floats * sizeof(float);
+        std::unique_lock<std::mutex> lock;
+        if (noalloc) {
+            if (need > dfk::kStaticScratchBytes) return DFK_ERR_UNSUPPORTED;
+            if (dfk::static_scratch(dev, &ws) != hipSuccess) return DFK_ERR_HIP;
+        } else {
+            Slot *slot = slot_for(dev, stream);
+            lock = std::unique_lock<std::mutex>(slot->mu);
+            if ((st = ensure_workspace(slot, need, stream, &ws)) != DFK_OK) return st;
+        }
         float *h = static_cast<float *>(ws);
         float *partial = partial_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + h_bytes) : nullptr;
         if (dfk::launch_gate_up(pg, x, W_gate, W_up, h, partial, stream, nullptr, ldw) != hipSuccess)
@@ -708,6 +717,17 @@ dfk_status_t dfk_swiglu_mlp(const uint16_t *x, const uint16_t *W_gate, const uin
                             dfk_layout_t layout, hipStream_t stream) {
     try {
         return mlp_impl(x, W_gate, W_up, d_model, W_down, out, B, d_model, d_ff, layout, stream);
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
+dfk_status_t dfk_swiglu_mlp_noalloc(const uint16_t *x, const uint16_t *W_gate, const uint16_t *W_up,
+                                    const uint16_t *W_down, uint16_t *out, int B, int d_model, int d_ff,
+                                    dfk_layout_t layout, hipStream_t stream) {
+    static_assert(dfk::kStaticScratchBytes == (size_t)DFK_NOALLOC_SCRATCH_BYTES, "scratch size mismatch");
+    try {
+        return mlp_impl(x, W_gate, W_up, d_model, W_down, out, B, d_model, d_ff, layout, stream, true);
     } catch (...) {
         return DFK_ERR_HIP;
     }

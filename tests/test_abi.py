@@ -69,6 +69,10 @@ def mlp(L, x=A, wg=A, wu=A, wd=A, out=A, B=1, dm=256, dff=688, layout=0):
     return L.dfk_swiglu_mlp(x, wg, wu, wd, out, B, dm, dff, layout, None)
 
 
+def mlp_noalloc(L, x=A, wg=A, wu=A, wd=A, out=A, B=1, dm=256, dff=688, layout=0):
+    return L.dfk_swiglu_mlp_noalloc(x, wg, wu, wd, out, B, dm, dff, layout, None)
+
+
 def norm_gate_up(L, x=A, gain=A, eps=1e-5, wg=A, wu=A, h=A, B=1, dm=256, dff=688, layout=0):
     return L.dfk_rmsnorm_gate_up_silu_mul(x, gain, eps, wg, wu, h, B, dm, dff, layout, None)
 
@@ -119,8 +123,9 @@ def rmsnorm(L, x=A, gain=A, eps=1e-5, out=A, B=1, dm=256):
     return L.dfk_rmsnorm(x, gain, eps, out, B, dm, None)
 
 
-@pytest.mark.parametrize("fn", [gate_up, down, mlp, norm_gate_up, norm_mlp, gu_packed, mlp_packed],
-                         ids=["gate_up", "down", "mlp", "norm_gate_up", "norm_mlp", "gu_packed", "mlp_packed"])
+@pytest.mark.parametrize("fn", [gate_up, down, mlp, mlp_noalloc, norm_gate_up, norm_mlp, gu_packed, mlp_packed],
+                         ids=["gate_up", "down", "mlp", "mlp_noalloc", "norm_gate_up", "norm_mlp", "gu_packed",
+                              "mlp_packed"])
 def test_invalid_arguments(L, fn):
     import inspect
     ptrs = [p for p in inspect.signature(fn).parameters
