@@ -1,7 +1,7 @@
 """Benchmark: decode-stage SwiGLU MLP on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
-                    [--no-cpu-baseline] [--no-sweep]
+                    [--no-cpu-baseline] [--no-sweep] [--sections a,b,...]
 
 A step is one call of the whole hot path, dfk_swiglu_mlp (the fused gate-up
 kernel, then the down-projection kernel), on a Llama-3-8B-shaped layer
@@ -9,13 +9,17 @@ kernel, then the down-projection kernel), on a Llama-3-8B-shaped layer
 already resident in HBM.  Weights rotate over 5 seeded sets (5 x 352 MB, far
 beyond the 256 MB Infinity Cache) so every call streams its weights from HBM.
 
-Printed: one JSON line with the metric (us per MLP call; lower is better),
-the dominant kernel's roofline (algorithmic bytes / measured launch duration
-vs the 8 TB/s HBM peak), per-batch figures for B = 1..64 (and, as context,
-for the Llama-3-70B layer shape), the 32-layer Llama-3-8B MLP stack per layer
-(eager calls, and the same chain captured once into a HIP graph and
-replayed), and the fp64 CPU oracle timed on the host cores over a bounded
-sample.
+Printed: one JSON line with the metric (us per MLP call, the mean over K
+back-to-back calls; lower is better) and its per-call p10 / p50 / p90, the
+dominant kernel's roofline (algorithmic bytes / measured launch duration vs
+the 8 TB/s HBM peak), the practical ceiling (a plain streaming read of the
+same weight bytes on this machine, dfk_stream_read) and the call's fraction of
+it, and context sections: per-batch figures for B = 1..64, the scheduler's
+shape sweep, FP8 weights, packed gate/up weights, the persistent kernel, the
+RMS-normalized MLP, the Llama-3-70B layer shape, and the 32-layer Llama-3-8B
+MLP stack with its between-layer RMS rescale (timed separately and
+excluded), eager and as one captured HIP graph; then the fp64 CPU oracle
+timed on the host cores over a bounded sample.
 """
 from __future__ import annotations
 
@@ -105,6 +109,26 @@ def _timed(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def _per_call_us(fn, steps, warmup):
+    """(p10, p50, p90) us of single calls of fn(i): a pair of HIP events
+    around each call, on the current stream, calls back to back."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    def q(f):
+        return t[min(len(t) - 1, max(0, int(round(f * (len(t) - 1)))))]
+    return q(0.10), q(0.50), q(0.90)
+
+
 def time_batch(B, sets, steps, warmup, device):
     """Per batch B: ms per whole-MLP call (dfk_swiglu_mlp, the step), and ms
     per launch of each kernel timed back to back on its own.  Weights rotate
@@ -137,54 +161,124 @@ def time_batch(B, sets, steps, warmup, device):
 
 def time_stack(device, B=1, layers=32, steps=20, warmup=3):
     """The 32-layer Llama-3-8B MLP stack (11.3 GB of distinct weights, cold by
-    construction), each layer's y the next layer's x: us per layer, eager and
-    as one captured HIP graph replayed."""
+    construction), chained y_l -> RMS rescale -> x_{l+1}.  The rescale is
+    dfk_rmsnorm with a unit gain and eps 1e-6: bf16_RNE(y / sqrt(mean(y^2) +
+    eps)) per batch row, bit for bit the oracle's between-layer rescale.  It is
+    timed separately and excluded from the per-layer MLP figure.  Eager (with
+    HIP events around every MLP call) and as one captured HIP graph; and the
+    same chain with each rescale fused into the next layer's gate-up
+    (dfk_rmsnorm_swiglu_mlp), as context."""
     import torch
     import swiglu_mlp_amd as dfk
     from swiglu_mlp_amd import inputs
 
     W = [inputs.stack_layer_weights_device(l, device) for l in range(layers)]
     x0 = inputs.randn_bf16_device((B, D_MODEL), 1.0, 3000, device)
-    outs = [torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device) for _ in range(layers)]
+    ones = torch.ones(D_MODEL, dtype=torch.bfloat16, device=device)
+    ys = [torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device) for _ in range(layers)]
+    xs = [x0] + [torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device) for _ in range(layers - 1)]
     s = torch.cuda.Stream()
+    EPS = 1e-6
 
-    def chain():
-        cur = x0
-        for w, o in zip(W, outs):
-            dfk.dfk_swiglu_mlp(cur, *w, out=o)
-            cur = o
+    def chain(ev=None):
+        for l in range(layers):
+            if ev is not None:
+                ev[l][0].record(s)
+            dfk.dfk_swiglu_mlp(xs[l], *W[l], out=ys[l])
+            if ev is not None:
+                ev[l][1].record(s)
+            if l + 1 < layers:
+                dfk.dfk_rmsnorm(ys[l], ones, EPS, xs[l + 1])
+
+    def rescales():
+        for l in range(layers - 1):
+            dfk.dfk_rmsnorm(ys[l], ones, EPS, xs[l + 1])
+
+    def fused_chain():
+        dfk.dfk_swiglu_mlp(xs[0], *W[0], out=ys[0])
+        for l in range(1, layers):
+            dfk.dfk_rmsnorm_swiglu_mlp(ys[l - 1], ones, EPS, *W[l], out=ys[l])
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(n):
+            fn()
+        e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n  # us per chain
 
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
         for _ in range(warmup):
             chain()
+            fused_chain()
         s.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
+        eager_chain_us = timed(chain, steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+        mlp_us = 0.0
         for _ in range(steps):
-            chain()
-        e1.record(s)
-    e1.synchronize()
-    eager_us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        chain()
+            chain(ev)
+            s.synchronize()
+            mlp_us += sum(a.elapsed_time(b) * 1e3 for a, b in ev)
+        mlp_us /= steps * layers
+        rescale_us = timed(rescales, steps) / (layers - 1)
+        eager_fused_us = timed(fused_chain, steps)
+    graphs = {}
+    for name, fn in (("chain", chain), ("rescales", rescales), ("fused", fused_chain)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        graphs[name] = g
     with torch.cuda.stream(s):
-        for _ in range(warmup):
-            g.replay()
+        for g in graphs.values():
+            for _ in range(warmup):
+                g.replay()
         s.synchronize()
-        e0.record(s)
-        for _ in range(steps):
-            g.replay()
-        e1.record(s)
-    e1.synchronize()
-    graph_us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+        gt = {name: timed(g.replay, steps) for name, g in graphs.items()}
+    graph_mlp_us = (gt["chain"] - gt["rescales"]) / layers
     bytes_layer = mlp_bytes(B)
-    del g, W
+    del graphs, W
     torch.cuda.empty_cache()
     return {"layers": layers, "batch": B, "weights_GB": round(layers * 3 * D_MODEL * D_FF * 2 / 1e9, 2),
-            "eager_us_per_layer": round(eager_us, 2), "graph_us_per_layer": round(graph_us, 2),
-            "graph_GBps": round(bytes_layer / (graph_us * 1e-6) / 1e9, 1)}
+            "rescale": "dfk_rmsnorm, unit gain, eps 1e-6, between layers",
+            "eager_us_per_layer_with_rescale": round(eager_chain_us / layers, 2),
+            "eager_mlp_us_per_layer": round(mlp_us, 2),
+            "rescale_us": round(rescale_us, 2),
+            "graph_us_per_layer_with_rescale": round(gt["chain"] / layers, 2),
+            "graph_mlp_us_per_layer": round(graph_mlp_us, 2),
+            "graph_mlp_GBps": round(bytes_layer / (graph_mlp_us * 1e-6) / 1e9, 1),
+            "fused_rescale_eager_us_per_layer": round(eager_fused_us / layers, 2),
+            "fused_rescale_graph_us_per_layer": round(gt["fused"] / layers, 2)}
+
+
+def time_stream_ceiling(device, steps=100, warmup=10, rotate=5):
+    """The practical HBM read ceiling on this machine: dfk_stream_read (plain
+    16-byte streaming loads, no arithmetic) over `rotate` buffers of the 8B
+    layer's weight bytes, read as the MLP call reads them (gate-up's bytes in
+    one launch, then down's) and in one launch; us and GB/s."""
+    import torch
+    import swiglu_mlp_amd as dfk
+
+    gu, dn = 2 * 2 * D_FF * D_MODEL, 2 * D_MODEL * D_FF
+    bufs = [torch.ones(gu + dn, dtype=torch.uint8, device=device) for _ in range(rotate)]
+    sink = torch.zeros(64, dtype=torch.int32, device=device)
+
+    def two(i):
+        b = bufs[i % rotate]
+        dfk.dfk_stream_read(b[:gu], sink)
+        dfk.dfk_stream_read(b[gu:], sink)
+
+    res = {}
+    for name, fn, nbytes in (("gate_up_bytes", lambda i: dfk.dfk_stream_read(bufs[i % rotate][:gu], sink), gu),
+                             ("down_bytes", lambda i: dfk.dfk_stream_read(bufs[i % rotate][gu:], sink), dn),
+                             ("both_two_launches", two, gu + dn),
+                             ("both_one_launch", lambda i: dfk.dfk_stream_read(bufs[i % rotate], sink), gu + dn)):
+        us = _timed(fn, steps, warmup) * 1e3
+        res[name] = {"bytes": nbytes, "us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    del bufs
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
@@ -399,6 +493,9 @@ def cpu_baseline(sets, budget_s=12.0, max_calls=400):
                       f"weight set, {dt:.1f} s wall"}
 
 
+SECTIONS = ("ceiling", "per_batch", "sweep", "fp8", "packed", "persistent", "norm", "70b", "stack")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,7 +504,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the per-batch sweep, the 70B-shape context and the 32-layer stack")
+                    help="only the headline batch and the streaming-read ceiling (no context sections)")
+    ap.add_argument("--sections", default=None,
+                    help="comma-separated context sections to run (default: all): " + ",".join(SECTIONS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes)")
@@ -417,6 +516,14 @@ def main():
         print("bench.py measures one GPU only: the decode MLP here runs on a single MI355X "
               "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sections is not None:
+        sections = {x for x in args.sections.split(",") if x}
+        unknown = sections - set(SECTIONS)
+        if unknown:
+            print(f"unknown sections: {sorted(unknown)}; known: {', '.join(SECTIONS)}", file=sys.stderr)
+            sys.exit(2)
+    else:
+        sections = {"ceiling"} if args.no_sweep else set(SECTIONS)
 
     import torch
     import swiglu_mlp_amd as dfk
@@ -446,9 +553,15 @@ def main():
     bytes_call = mlp_bytes(B)
     achieved_call = bytes_call / (us_per_call * 1e-6) / 1e9
     gu_achieved = gate_up_bytes(B) / (gu_us * 1e-6) / 1e9
+    from swiglu_mlp_amd import inputs as _inputs
+    x = _inputs.randn_bf16_device((B, D_MODEL), 1.0, 6100 + B, device)
+    out = torch.empty((B, D_MODEL), dtype=torch.bfloat16, device=device)
+    p10, p50, p90 = _per_call_us(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % ROTATE], out),
+                                 max(args.steps, 20), args.warmup)
 
+    ceiling = time_stream_ceiling(device) if "ceiling" in sections else None
     per_batch = {}
-    if not args.no_sweep:
+    if "per_batch" in sections:
         for b in (1, 2, 4, 8, 16, 32, 64):
             t, g, d, v = time_batch(b, sets, 200, 20, device)
             us = t * 1e3
@@ -457,16 +570,17 @@ def main():
                                  "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                                  "gate_up_us": round(g * 1e3, 2), "down_us": round(d * 1e3, 2),
                                  "variants": list(v)}
+            if ceiling:
+                per_batch[str(b)]["frac_of_practical"] = round(
+                    gbps / ceiling["both_two_launches"]["GBps"], 4)
 
-    stack, shape70b, norm, persistent, packed, fp8, sweep = None, None, None, None, None, None, None
-    if not args.no_sweep:
-        sweep = time_shape_sweep(device)
-        fp8 = time_fp8(device)
-        packed = time_packed(sets, device)
-        persistent = time_persistent(sets, device)
-        norm = time_rmsnorm(sets, device)
-        shape70b = time_70b(device)
-        stack = time_stack(device)
+    sweep = time_shape_sweep(device) if "sweep" in sections else None
+    fp8 = time_fp8(device) if "fp8" in sections else None
+    packed = time_packed(sets, device) if "packed" in sections else None
+    persistent = time_persistent(sets, device) if "persistent" in sections else None
+    norm = time_rmsnorm(sets, device) if "norm" in sections else None
+    shape70b = time_70b(device) if "70b" in sections else None
+    stack = time_stack(device) if "stack" in sections else None
 
     result = {
         "metric": METRIC,
@@ -490,6 +604,7 @@ def main():
         },
         "achieved_GBps": round(achieved_call, 1),
         "frac_of_hbm_peak": round(achieved_call / HBM_PEAK_GBPS, 4),
+        "us_per_call_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
         "algorithmic_bytes_per_call": bytes_call,
         "kernel_us": {"gate_up": round(gu_us, 2), "down": round(dn_us, 2)},
         "roofline": {
@@ -502,6 +617,9 @@ def main():
             "traffic": measured_traffic(B),
             "algorithmic_bytes_per_launch": gate_up_bytes(B),
         },
+        "stream_read_ceiling": ceiling,
+        "frac_of_practical": (round(achieved_call / ceiling["both_two_launches"]["GBps"], 4)
+                              if ceiling else None),
         "per_batch": per_batch,
         "per_batch_llama70b_shape": shape70b,
         "stack32_llama8b": stack,

@@ -331,6 +331,20 @@ dfk_status_t dfk_load_tuning_table(const char *path);
 const char *dfk_tuning_table_source(void);
 
 /*
+ * Measurement helper, not part of the MLP: read `bytes` (a positive multiple
+ * of 16) of the device buffer `buf` once, on `stream`, with the access shape
+ * of the vector-ALU weight walk: 16-byte non-temporal loads, 1 KiB per wave
+ * load, each wave walking two contiguous segments (in the two halves of the
+ * buffer) with four loads in flight on each.  It gives the
+ * practical HBM read ceiling the kernels are compared with.  `sink` is a
+ * device array of 64 uint32_t that the kernel may write (only when the folded
+ * words hit a fixed pattern).  Errors: null pointers or bytes = 0
+ * DFK_ERR_INVALID_ARG, bytes not a multiple of 16 DFK_ERR_UNSUPPORTED, buf not
+ * 16-byte or sink not 4-byte aligned DFK_ERR_MISALIGNED.
+ */
+dfk_status_t dfk_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
+/*
  * Free every workspace buffer the library holds for the current device (the
  * current ones and those retired by growth), after waiting for the device.
  * HIP graphs captured against them must not be replayed afterwards; later

@@ -60,7 +60,7 @@ EXPORTED = (
     "dfk_tuning_table_source", "dfk_release_workspace", "dfk_rmsnorm",
     "dfk_rmsnorm_gate_up_silu_mul", "dfk_rmsnorm_swiglu_mlp", "dfk_gate_up_silu_mul_packed",
     "dfk_swiglu_mlp_packed", "dfk_gate_up_silu_mul_fp8", "dfk_down_proj_fp8", "dfk_swiglu_mlp_fp8",
-    "dfk_swiglu_mlp_noalloc",
+    "dfk_swiglu_mlp_noalloc", "dfk_stream_read",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.dfk_swiglu_mlp.restype = i
     L.dfk_swiglu_mlp_noalloc.argtypes = [u16p, u16p, u16p, u16p, u16p, i, i, i, i, vp]
     L.dfk_swiglu_mlp_noalloc.restype = i
+    L.dfk_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    L.dfk_stream_read.restype = i
     L.dfk_schedule_select.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     L.dfk_schedule_select.restype = i
     L.dfk_status_string.argtypes = [i]
@@ -233,6 +235,21 @@ def dfk_swiglu_mlp_noalloc(x, W_gate, W_up, W_down, out, layout: int = Layout.AU
                                       _stream_handle(stream, x.device))
     _check(st, "dfk_swiglu_mlp_noalloc")
     return out
+
+
+def dfk_stream_read(buf, sink, nbytes: Optional[int] = None, stream=None) -> None:
+    """Measurement helper: one plain streaming read of `nbytes` (default: all)
+    of the device tensor `buf`; `sink` is a device tensor of >= 64 int32."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if not isinstance(sink, torch.Tensor) or sink.device.type != "cuda" or sink.numel() * sink.element_size() < 256:
+        raise ValueError("sink must be a GPU tensor of at least 256 bytes")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if n > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    _check(lib().dfk_stream_read(buf.data_ptr(), n, sink.data_ptr(), _stream_handle(stream, buf.device)),
+           "dfk_stream_read")
 
 
 def dfk_gate_up_silu_mul_packed(x, W_gu, packing: int, h=None, layout: int = Layout.AUTO, stream=None):

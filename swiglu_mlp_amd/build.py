@@ -28,7 +28,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["dfk_kernels.hip", "dfk_runtime.cpp"]
+SOURCES = ["dfk_kernels.hip", "dfk_stream.hip", "dfk_runtime.cpp"]
 
 
 def hipcc() -> str:

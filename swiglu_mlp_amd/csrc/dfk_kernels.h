@@ -128,6 +128,10 @@ constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 // device: looked up with hipGetSymbolAddress on the first request for that
 // device and cached; later requests only read the cache.
 hipError_t static_scratch(int dev, void **ptr);
+// The plain streaming read (dfk_stream.hip): `bytes` (a multiple of 16) of
+// `buf` read once with 16-byte loads; `sink` (64 words) is written only when
+// the folded words hit a fixed pattern.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int cus, hipStream_t stream);
 // `partial` must hold p.partial_floats floats when that is non-zero.
 hipError_t launch_down(const Plan &p, const float *h, const uint16_t *w_down, uint16_t *y,
                        float *partial, hipStream_t stream);

@@ -1008,6 +1008,24 @@ dfk_status_t dfk_swiglu_mlp_fp8(const uint16_t *x, const uint8_t *Wq_gate, const
     }
 }
 
+dfk_status_t dfk_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    try {
+        if (!buf || !sink || bytes == 0) return DFK_ERR_INVALID_ARG;
+        if ((bytes % 16) != 0) return DFK_ERR_UNSUPPORTED;
+        if (!aligned16(buf) || !aligned4(sink)) return DFK_ERR_MISALIGNED;
+        int dev;
+        dfk_status_t st = current_device(&dev);
+        if (st != DFK_OK) return st;
+        if (dfk::launch_stream_read(buf, bytes, sink, device_cus(dev), stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return DFK_ERR_HIP;
+        }
+        return DFK_OK;
+    } catch (...) {
+        return DFK_ERR_HIP;
+    }
+}
+
 dfk_status_t dfk_release_workspace(void) {
     try {
         int dev;

@@ -274,3 +274,13 @@ def test_installed_table_parses(restore_table):
         g, d = dfk.dfk_schedule_select(e["B"], e["d_model"], e["d_ff"])
         got = g if e["op"] == "gate_up" else d
         assert dfk.layout_name(got) == e["winner"]
+
+
+def test_stream_read_argument_checks(L):
+    L.dfk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.dfk_stream_read(NULL, 1024, A, None) == Status.INVALID_ARG
+    assert L.dfk_stream_read(A, 1024, NULL, None) == Status.INVALID_ARG
+    assert L.dfk_stream_read(A, 0, A, None) == Status.INVALID_ARG
+    assert L.dfk_stream_read(A, 1000, A, None) == Status.UNSUPPORTED
+    assert L.dfk_stream_read(MIS, 1024, A, None) == Status.MISALIGNED
+    assert L.dfk_stream_read(A, 1024, A + 2, None) == Status.MISALIGNED
