@@ -281,9 +281,10 @@ def time_stream_ceiling(device, steps=100, warmup=10, rotate=5):
     return res
 
 
-def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
+def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10, persistent=True):
     """Context: whole-MLP us per call at the Llama-3-70B layer shape
-    (d_model 8192, d_ff 28672), two weight sets rotated (2.8 GB)."""
+    (d_model 8192, d_ff 28672), two weight sets rotated (2.8 GB); with
+    `persistent`, also the persistent kernel at B = 1 (a cooperative launch)."""
     import torch
     import swiglu_mlp_amd as dfk
     from swiglu_mlp_amd import inputs
@@ -300,7 +301,7 @@ def time_70b(device, batches=(1, 4, 16, 64), steps=100, warmup=10):
         gbps = mlp_bytes(B, dm, dff) / (ms * 1e-3) / 1e9
         res[str(B)] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                        "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-        if B == 1:
+        if B == 1 and persistent:
             from swiglu_mlp_amd import Layout
             ms_p = _timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % 2], out, layout=Layout.ROW_PERSISTENT),
                           steps, warmup)
@@ -579,7 +580,7 @@ def main():
     packed = time_packed(sets, device) if "packed" in sections else None
     persistent = time_persistent(sets, device) if "persistent" in sections else None
     norm = time_rmsnorm(sets, device) if "norm" in sections else None
-    shape70b = time_70b(device) if "70b" in sections else None
+    shape70b = time_70b(device, persistent="persistent" in sections) if "70b" in sections else None
     stack = time_stack(device) if "stack" in sections else None
 
     result = {

@@ -224,10 +224,11 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * B * d_model * 2 <= 160 KiB) and the matrix-core kernels (B <= 128),
  * which widen the codes to bf16 exactly: on their way into LDS, or in
  * registers (the down projection's column traversal).  Layouts:
- * AUTO = the measured best at the Llama-3-8B layer shape (gate-up: vector
- * ALU to B = 3, matrix-core column traversal to B = 16, row traversal above;
- * down: vector ALU to B = 2, matrix-core column traversal above); ROW =
- * vector ALU up to B = 8, else matrix cores; COL = matrix
+ * AUTO = the tuning table's FP8 entry for the shape (see
+ * dfk_schedule_select), else the measured best at the Llama-3-8B layer shape
+ * (gate-up: vector ALU to B = 3, matrix-core column traversal to B = 16, row
+ * traversal above; down: vector ALU to B = 2, matrix-core column traversal
+ * above); ROW = vector ALU up to B = 8, else matrix cores; COL = matrix
  * cores; ROW_VALU, ROW_MFMA, COL_MFMA force the engine; COL_VALU and
  * ROW_PERSISTENT are DFK_ERR_UNSUPPORTED.  d_model and d_ff must be
  * multiples of 16.  Code and tensor pointers must be 16-byte aligned, scale
@@ -302,7 +303,11 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
  * exact (B, d_model, d_ff) entry, else the entry for the same (d_model, d_ff)
  * with the nearest tuned batch at or above B (else the largest below), else
  * a built-in heuristic.  Writes explicit variants (never AUTO) to both
- * outputs.  DFK_FORCE_LAYOUT=row|col overrides the traversal.
+ * outputs.  DFK_FORCE_LAYOUT=row|col overrides the traversal.  The table
+ * records the library and HIP versions it was tuned for; a table for other
+ * versions (or a missing or malformed one) is not used: the heuristic serves
+ * and dfk_tuning_table_source says why.  The same table holds the FP8 entry
+ * points' choices (ops gate_up_fp8, down_fp8), which their AUTO layout reads.
  */
 dfk_status_t dfk_schedule_select(int B, int d_model, int d_ff, dfk_layout_t *gate_up_layout,
                                  dfk_layout_t *down_layout);
@@ -313,19 +318,21 @@ const char *dfk_status_string(dfk_status_t s);
 /* Static name of a layout value, e.g. "row_valu" (never NULL). */
 const char *dfk_layout_name(dfk_layout_t layout);
 
-/* Library version string, e.g. "dfk 0.1.0 gfx950". */
+/* Library version string, e.g. "dfk 0.2.0 gfx950 (HIP 7.2.26015)". */
 const char *dfk_version(void);
 
 /*
  * Reload the tuning table from `path` (NULL: the default location).  Returns
- * DFK_OK when a table was loaded, DFK_ERR_INVALID_ARG when the file is missing
- * or malformed (the scheduler then uses its heuristic).  Host only.
+ * DFK_OK when a table was loaded, DFK_ERR_INVALID_ARG when the file is
+ * missing, malformed or tuned for another library or HIP version (the
+ * scheduler then uses its heuristic).  Host only.
  */
 dfk_status_t dfk_load_tuning_table(const char *path);
 
 /*
  * Where the scheduler's current table came from: the path of the loaded file,
- * or "heuristic" when none is loaded.  Static storage, valid until the next
+ * "heuristic" when none is loaded, or "heuristic (table PATH tuned for ...)"
+ * when the table was for other versions.  Static storage, valid until the next
  * dfk_load_tuning_table call.
  */
 const char *dfk_tuning_table_source(void);

@@ -21,6 +21,8 @@
 #include <utility>
 #include <vector>
 
+#include <hip/hip_version.h>
+
 #include "dfk.h"
 #include "dfk_kernels.h"
 
@@ -32,6 +34,19 @@ using dfk::Plan;
 using dfk::Traversal;
 
 constexpr int kMaxBatch = 256;
+
+// Library and HIP versions, recorded in the tuning table by the tuner; a
+// table tuned for another library or HIP version is not used.
+#define DFK_LIB_VERSION "0.2.0"
+#define DFK_STR2(x) #x
+#define DFK_STR(x) DFK_STR2(x)
+const char *const kLibVersion = DFK_LIB_VERSION;
+const char *const kRocmVersion =
+    DFK_STR(HIP_VERSION_MAJOR) "." DFK_STR(HIP_VERSION_MINOR) "." DFK_STR(HIP_VERSION_PATCH);
+
+// Operations the tuning table holds entries for (bf16 weights use the
+// kernels' own Op numbering).
+enum TableOp { T_GATE_UP = dfk::OP_GATE_UP, T_DOWN = dfk::OP_DOWN, T_GATE_UP_FP8 = 2, T_DOWN_FP8 = 3 };
 
 int log_level() {
     static int level = [] {
@@ -326,7 +341,7 @@ dfk_layout_t layout_of(Variant v) {
 // ------------------------------------------------------------ tuning table -
 
 struct Entry {
-    Op op;
+    int op;  // TableOp
     int B, d_model, d_ff;
     Variant v;
 };
@@ -355,40 +370,73 @@ std::string default_table_path() {
     return "tuning/gfx950.json";
 }
 
-// Parse a table file; false (and no change) on any problem.
-bool load_table_file(const std::string &path, std::vector<Entry> *out) {
+// Parse a table file.  0: parsed, entries in *out; 1: missing or malformed;
+// 2: well formed but tuned for another library or HIP version (*why says
+// which).  *out is only written on success.
+int load_table_file(const std::string &path, std::vector<Entry> *out, std::string *why) {
     std::ifstream f(path, std::ios::binary);
-    if (!f) return false;
+    if (!f) return 1;
     std::stringstream ss;
     ss << f.rdbuf();
     JVal root;
-    if (!parse_json(ss.str(), &root) || root.kind != JVal::OBJ) return false;
+    if (!parse_json(ss.str(), &root) || root.kind != JVal::OBJ) return 1;
     const JVal *fmt = root.get("format");
-    if (!fmt || fmt->kind != JVal::STR || fmt->str != "dfk-tuning-v1") return false;
+    if (!fmt || fmt->kind != JVal::STR || fmt->str != "dfk-tuning-v2") return 1;
     const JVal *arch = root.get("arch");
-    if (!arch || arch->kind != JVal::STR || arch->str != "gfx950") return false;
+    if (!arch || arch->kind != JVal::STR || arch->str != "gfx950") return 1;
+    const JVal *lib = root.get("lib_version"), *rocm = root.get("rocm_version");
+    if (!lib || !rocm || lib->kind != JVal::STR || rocm->kind != JVal::STR) return 1;
     const JVal *ents = root.get("entries");
-    if (!ents || ents->kind != JVal::ARR) return false;
+    if (!ents || ents->kind != JVal::ARR) return 1;
     std::vector<Entry> v;
     for (const JVal &e : ents->arr) {
         const JVal *op = e.get("op"), *B = e.get("B"), *dm = e.get("d_model"), *df = e.get("d_ff"),
                    *w = e.get("winner");
         if (!op || !B || !dm || !df || !w || op->kind != JVal::STR || B->kind != JVal::NUM ||
             dm->kind != JVal::NUM || df->kind != JVal::NUM || w->kind != JVal::STR)
-            return false;
+            return 1;
         Entry en;
-        if (op->str == "gate_up") en.op = dfk::OP_GATE_UP;
-        else if (op->str == "down") en.op = dfk::OP_DOWN;
-        else return false;
+        if (op->str == "gate_up") en.op = T_GATE_UP;
+        else if (op->str == "down") en.op = T_DOWN;
+        else if (op->str == "gate_up_fp8") en.op = T_GATE_UP_FP8;
+        else if (op->str == "down_fp8") en.op = T_DOWN_FP8;
+        else return 1;
         en.B = (int)B->num;
         en.d_model = (int)dm->num;
         en.d_ff = (int)df->num;
-        if (!variant_from_name(w->str, &en.v)) return false;
-        if (en.B < 1 || en.d_model < 1 || en.d_ff < 1) return false;
+        if (!variant_from_name(w->str, &en.v)) return 1;
+        if ((en.op == T_GATE_UP_FP8 || en.op == T_DOWN_FP8) && en.v.engine == dfk::ENGINE_VALU &&
+            en.v.trav == dfk::TRAV_COL)
+            return 1;  // no vector-ALU column walk over FP8 codes
+        if (en.B < 1 || en.d_model < 1 || en.d_ff < 1) return 1;
         v.push_back(en);
     }
+    if (lib->str != kLibVersion || rocm->str != kRocmVersion) {
+        *why = "tuned for dfk " + lib->str + " / HIP " + rocm->str + ", this is dfk " + kLibVersion + " / HIP " +
+               kRocmVersion;
+        return 2;
+    }
     *out = std::move(v);
-    return true;
+    return 0;
+}
+
+// Load `path` into the table (caller holds table().mu); true on success.  On
+// failure the table is empty and its source says why.
+bool install_table(const std::string &path) {
+    Table &t = table();
+    std::vector<Entry> v;
+    std::string why;
+    const int rc = load_table_file(path, &v, &why);
+    if (rc == 0) {
+        t.entries = std::move(v);
+        t.loaded = true;
+        t.source = path;
+        return true;
+    }
+    t.entries.clear();
+    t.loaded = false;
+    t.source = rc == 2 ? "heuristic (table " + path + " " + why + ")" : "heuristic";
+    return false;
 }
 
 // Caller holds table().mu.
@@ -397,13 +445,7 @@ void ensure_table_loaded() {
     if (t.attempted) return;
     t.attempted = true;
     const char *env = std::getenv("DFK_TUNING_TABLE");
-    std::string path = env && *env ? std::string(env) : default_table_path();
-    std::vector<Entry> v;
-    if (load_table_file(path, &v)) {
-        t.entries = std::move(v);
-        t.loaded = true;
-        t.source = path;
-    }
+    install_table(env && *env ? std::string(env) : default_table_path());
     if (log_level() >= 1)
         std::fprintf(stderr, "[dfk] tuning table: %s (%zu entries)\n", t.source.c_str(), t.entries.size());
 }
@@ -417,21 +459,31 @@ Variant heuristic(Op op, int B) {
 }
 
 // Exact entry; else nearest tuned batch >= B for the same (d_model, d_ff);
-// else the largest tuned batch below B; else the heuristic.
-Variant lookup(Op op, int B, int d_model, int d_ff) {
+// else the largest tuned batch below B.  False when the table has nothing
+// for the shape.
+bool find_entry(int op, int B, int d_model, int d_ff, Variant *v) {
     Table &t = table();
     std::lock_guard<std::mutex> lock(t.mu);
     ensure_table_loaded();
     const Entry *above = nullptr, *below = nullptr;
     for (const Entry &e : t.entries) {
         if (e.op != op || e.d_model != d_model || e.d_ff != d_ff) continue;
-        if (e.B == B) return e.v;
+        if (e.B == B) {
+            *v = e.v;
+            return true;
+        }
         if (e.B > B && (!above || e.B < above->B)) above = &e;
         if (e.B < B && (!below || e.B > below->B)) below = &e;
     }
-    if (above) return above->v;
-    if (below) return below->v;
-    return heuristic(op, B);
+    if (above) *v = above->v;
+    else if (below) *v = below->v;
+    return above || below;
+}
+
+// The table's choice, else the heuristic.
+Variant lookup(Op op, int B, int d_model, int d_ff) {
+    Variant v;
+    return find_entry(op, B, d_model, d_ff, &v) ? v : heuristic(op, B);
 }
 
 // Apply DFK_FORCE_LAYOUT=row|col to a traversal.
@@ -619,7 +671,7 @@ const char *dfk_layout_name(dfk_layout_t l) {
     return "invalid";
 }
 
-const char *dfk_version(void) { return "dfk 0.1.0 gfx950"; }
+const char *dfk_version(void) { return "dfk " DFK_LIB_VERSION " gfx950 (HIP " DFK_STR(HIP_VERSION_MAJOR) "." DFK_STR(HIP_VERSION_MINOR) "." DFK_STR(HIP_VERSION_PATCH) ")"; }
 
 dfk_status_t dfk_schedule_select(int B, int d_model, int d_ff, dfk_layout_t *gate_up_layout,
                                  dfk_layout_t *down_layout) {
@@ -649,19 +701,8 @@ dfk_status_t dfk_load_tuning_table(const char *path) {
     try {
         Table &t = table();
         std::lock_guard<std::mutex> lock(t.mu);
-        std::string p = path ? std::string(path) : default_table_path();
-        std::vector<Entry> v;
         t.attempted = true;
-        if (!load_table_file(p, &v)) {
-            t.entries.clear();
-            t.loaded = false;
-            t.source = "heuristic";
-            return DFK_ERR_INVALID_ARG;
-        }
-        t.entries = std::move(v);
-        t.loaded = true;
-        t.source = p;
-        return DFK_OK;
+        return install_table(path ? std::string(path) : default_table_path()) ? DFK_OK : DFK_ERR_INVALID_ARG;
     } catch (...) {
         return DFK_ERR_INVALID_ARG;
     }
@@ -891,13 +932,15 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
     }
 }
 
-// FP8 plans.  AUTO (measured at the Llama-3-8B layer shape): gate-up on the
-// VALU row walk up to B = 3, the matrix cores' column traversal up to B = 16,
-// their row traversal above; down on the VALU row walk up to B = 2, the
-// matrix cores' column traversal above (at B = 3: 19.5 against 20.6 us VALU
-// at the 8B shape, 50.7 against 58.2 us at the 70B shape).  ROW: VALU up to B = 8, else the
-// matrix cores; COL: the matrix cores; *_VALU / *_MFMA force the engine
-// (there is no VALU column walk for FP8).
+// FP8 plans.  AUTO: the tuning table's FP8 entry for the shape (ops
+// gate_up_fp8 / down_fp8, looked up like the bf16 ones), else a built-in rule
+// measured at the Llama-3-8B layer shape: gate-up on the VALU row walk up to
+// B = 3, the matrix cores' column traversal up to B = 16, their row traversal
+// above; down on the VALU row walk up to B = 2, the matrix cores' column
+// traversal above.  ROW: VALU up to B = 8, else the matrix cores; COL: the
+// matrix cores; *_VALU / *_MFMA force the engine (there is no VALU column walk
+// for FP8).  A table choice the VALU kernel cannot run falls back to the
+// matrix cores with the same traversal.
 static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int dev, Plan *p) {
     using dfk::ENGINE_MFMA;
     using dfk::ENGINE_VALU;
@@ -905,9 +948,13 @@ static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model
     using dfk::TRAV_ROW;
     Engine e;
     Traversal tr;
+    bool from_table = false;
     switch (layout) {
-        case DFK_LAYOUT_AUTO:
-            if (op == dfk::OP_GATE_UP) {
+        case DFK_LAYOUT_AUTO: {
+            Variant v;
+            if (find_entry(op == dfk::OP_GATE_UP ? T_GATE_UP_FP8 : T_DOWN_FP8, B, d_model, d_ff, &v)) {
+                e = v.engine, tr = v.trav, from_table = true;
+            } else if (op == dfk::OP_GATE_UP) {
                 if (B <= 3) e = ENGINE_VALU, tr = TRAV_ROW;
                 else e = ENGINE_MFMA, tr = (B <= 16 ? TRAV_COL : TRAV_ROW);
             } else {
@@ -915,6 +962,7 @@ static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model
                 else e = ENGINE_MFMA, tr = TRAV_COL;
             }
             break;
+        }
         case DFK_LAYOUT_ROW: e = B <= dfk::kF8MaxBatch ? ENGINE_VALU : ENGINE_MFMA, tr = TRAV_ROW; break;
         case DFK_LAYOUT_COL: e = ENGINE_MFMA, tr = TRAV_COL; break;
         case DFK_LAYOUT_ROW_VALU: e = ENGINE_VALU, tr = TRAV_ROW; break;
@@ -922,7 +970,10 @@ static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model
         case DFK_LAYOUT_COL_MFMA: e = ENGINE_MFMA, tr = TRAV_COL; break;
         default: return DFK_ERR_UNSUPPORTED;  // COL_VALU, ROW_PERSISTENT
     }
-    if (!dfk::make_fp8_plan(op, e, tr, B, d_model, d_ff, device_cus(dev), p)) return DFK_ERR_UNSUPPORTED;
+    if (!dfk::make_fp8_plan(op, e, tr, B, d_model, d_ff, device_cus(dev), p) &&
+        !(from_table && e == ENGINE_VALU && dfk::make_fp8_plan(op, ENGINE_MFMA, tr, B, d_model, d_ff,
+                                                               device_cus(dev), p)))
+        return DFK_ERR_UNSUPPORTED;
     log_plan(op == dfk::OP_GATE_UP ? "gate_up_fp8" : "down_fp8", *p);
     return DFK_OK;
 }

@@ -180,9 +180,15 @@ def test_schedule_select_argument_checks(L):
 
 # ----------------------------------------------------------------- tables --
 
-def write_table(path, entries, arch="gfx950", fmt="dfk-tuning-v1"):
+def lib_versions():
+    from swiglu_mlp_amd import tune
+    return tune.library_versions()
+
+
+def write_table(path, entries, arch="gfx950", fmt="dfk-tuning-v2", versions=None):
+    lib, rocm = versions or lib_versions()
     with open(path, "w") as f:
-        json.dump({"format": fmt, "arch": arch, "entries": entries}, f)
+        json.dump({"format": fmt, "arch": arch, "lib_version": lib, "rocm_version": rocm, "entries": entries}, f)
     return str(path)
 
 
@@ -240,21 +246,54 @@ def test_force_layout_env(tmp_path, restore_table):
     assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.ROW_VALU, Layout.ROW_MFMA)
 
 
+_V = '"lib_version": "%s", "rocm_version": "%s"'
+
+
 @pytest.mark.parametrize("content", [
-    "not json", '{"format": "dfk-tuning-v1", "arch": "gfx950"}',
-    '{"format": "other", "arch": "gfx950", "entries": []}',
-    '{"format": "dfk-tuning-v1", "arch": "gfx942", "entries": []}',
-    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": [{"op": "gate_up"}]}',
-    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": [{"op": "x", "B": 1, "d_model": 8, "d_ff": 8, "winner": "row_valu"}]}',
-    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": [{"op": "down", "B": 1, "d_model": 8, "d_ff": 8, "winner": "diag"}]}',
+    "not json", '{"format": "dfk-tuning-v2", "arch": "gfx950", %V}',
+    '{"format": "other", "arch": "gfx950", %V, "entries": []}',
+    '{"format": "dfk-tuning-v1", "arch": "gfx950", "entries": []}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx950", "entries": []}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx942", %V, "entries": []}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "gate_up"}]}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "x", "B": 1, "d_model": 8, "d_ff": 8, "winner": "row_valu"}]}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "down", "B": 1, "d_model": 8, "d_ff": 8, "winner": "diag"}]}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "down_fp8", "B": 1, "d_model": 16, "d_ff": 16, "winner": "col_valu"}]}',
 ])
 def test_bad_table_falls_back_to_heuristic(tmp_path, content, restore_table):
     p = tmp_path / "bad.json"
-    p.write_text(content)
+    p.write_text(content.replace("%V", _V % lib_versions()))
     with pytest.raises(dfk.DfkError) as e:
         dfk.dfk_load_tuning_table(str(p))
     assert e.value.status == Status.INVALID_ARG
     assert dfk.dfk_tuning_table_source() == "heuristic"
+    assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.ROW_VALU, Layout.ROW_VALU)
+
+
+@pytest.mark.parametrize("which", ["lib", "rocm"])
+def test_table_for_another_version_is_not_used(tmp_path, which, restore_table):
+    """A table tuned for another library or HIP version falls back to the
+    heuristic, and the table source names the mismatch (re-tune then)."""
+    lib, rocm = lib_versions()
+    vers = ("0.0.1", rocm) if which == "lib" else (lib, "1.2.3")
+    path = write_table(tmp_path / "old.json", [entry("gate_up", 1, 4096, 14336, "col_mfma"),
+                                                entry("down", 1, 4096, 14336, "col_mfma")], versions=vers)
+    with pytest.raises(dfk.DfkError):
+        dfk.dfk_load_tuning_table(path)
+    src = dfk.dfk_tuning_table_source()
+    assert src.startswith("heuristic (table ") and path in src and (vers[0] in src and vers[1] in src)
+    assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.ROW_VALU, Layout.ROW_VALU)
+
+
+def test_fp8_entries_load_beside_bf16(tmp_path, restore_table):
+    """FP8 entries (gate_up_fp8 / down_fp8) load with the bf16 ones and leave
+    the bf16 schedule alone."""
+    path = write_table(tmp_path / "t.json", [entry("gate_up", 1, 4096, 14336, "row_valu"),
+                                               entry("down", 1, 4096, 14336, "row_valu"),
+                                               entry("gate_up_fp8", 1, 4096, 14336, "col_mfma"),
+                                               entry("down_fp8", 1, 4096, 14336, "row_mfma")])
+    dfk.dfk_load_tuning_table(path)
+    assert dfk.dfk_tuning_table_source() == path
     assert dfk.dfk_schedule_select(1, 4096, 14336) == (Layout.ROW_VALU, Layout.ROW_VALU)
 
 
@@ -268,9 +307,13 @@ def test_installed_table_parses(restore_table):
     """The table shipped with the package (if any) loads and names only known variants."""
     if not os.path.exists(dfk.TUNING_TABLE):
         pytest.skip("no tuning table installed yet")
-    dfk.dfk_load_tuning_table(dfk.TUNING_TABLE)
     t = json.load(open(dfk.TUNING_TABLE))
+    assert (t["lib_version"], t["rocm_version"]) == lib_versions(), "the installed table is stale: re-tune"
+    dfk.dfk_load_tuning_table(dfk.TUNING_TABLE)
+    assert dfk.dfk_tuning_table_source() == dfk.TUNING_TABLE
     for e in t["entries"]:
+        if e["op"].endswith("_fp8"):
+            continue  # the FP8 entry points' AUTO reads these; no public query
         g, d = dfk.dfk_schedule_select(e["B"], e["d_model"], e["d_ff"])
         got = g if e["op"] == "gate_up" else d
         assert dfk.layout_name(got) == e["winner"]

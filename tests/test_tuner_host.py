@@ -1,5 +1,6 @@
 """Host logic of the profiler-driven tuner (no GPU): trace parsing, the
-per-call cost taken from kernel-end spacing, and the winner rule."""
+per-call cost taken from summed kernel durations, the winner rule, FP8 ops,
+ineligible variants and the table's version fields."""
 import csv
 import os
 
@@ -26,25 +27,24 @@ def test_parse_merges_reduce_kernels_and_skips_foreign(tmp_path):
         {"Dispatch_Id": 4, "Kernel_Name": "__amd_rocclr_fillBufferAligned", "Start_Timestamp": 300, "End_Timestamp": 310},
     ])
     calls = tune.parse_rocprof(str(d))
-    assert [(s, e) for _, s, e in calls] == [(0, 100), (120, 260)]
+    assert [(s, e) for _, s, e, _ in calls] == [(0, 100), (120, 260)]
     assert "panel_kernel" in calls[1][0]
+    # the K-split call's cost is its two kernels' durations, not the gap between them
+    assert [b for _, _, _, b in calls] == [100, 120 + 10]
 
 
-def test_block_costs_use_end_spacing():
+def test_block_costs_use_summed_durations():
     blocks = [{"reps": 3}, {"reps": 2}]
-    # warm-up 1 per block; block 0 ends at 10, 20, 31, 43 (spacings 10, 11, 12);
-    # block 1 ends at 100, 150, 205 (spacings 50, 55)
-    ends = [10, 20, 31, 43, 100, 150, 205]
-    calls = [("k", e - 5, e) for e in ends]
+    # warm-up 1 per block (not counted); busy times 5 | 10, 11, 12 | 40 | 50, 55
+    busy = [5, 10, 11, 12, 40, 50, 55]
+    calls = [("k", 1000 * i, 1000 * i + b, b) for i, b in enumerate(busy)]
     out = tune.block_costs(calls, blocks, warmup=1)
     assert out == pytest.approx([11e-3, 52.5e-3])
 
 
 def test_block_costs_check_counts():
     with pytest.raises(RuntimeError):
-        tune.block_costs([("k", 0, 1)] * 3, [{"reps": 3}], warmup=1)
-    with pytest.raises(RuntimeError):
-        tune.block_costs([("k", 0, 1)] * 3, [{"reps": 3}], warmup=0)
+        tune.block_costs([("k", 0, 1, 1)] * 3, [{"reps": 3}], warmup=1)
 
 
 def test_choose_tie_goes_to_row():
@@ -84,3 +84,30 @@ def test_near_ties_and_confirmed_winner():
     assert entries["gate_up"]["winner"] == "row_valu"
     assert entries["down"]["winner"] == "row_mfma"
     assert "confirm_us" in entries["gate_up"]
+    assert entries["gate_up"]["decided_by"] == "events"
+    # without a confirmation the profile decides, and the entry says so
+    assert all(e["decided_by"] == "rocprof" for e in tune.build_table(blocks, per))
+
+
+def test_fp8_ops_plan_and_limits():
+    blocks = tune.plan_blocks([(4096, 14336), (4104, 14336)], [1, 16], reps=5,
+                              ops=("gate_up", "gate_up_fp8", "down_fp8"))
+    fp8 = [b for b in blocks if b["op"].endswith("_fp8")]
+    # no vector-ALU column walk over FP8 codes; d_model 4104 is not a multiple of 16
+    assert fp8 and all(b["variant"] != "col_valu" and b["d_model"] == 4096 for b in fp8)
+    assert {b["variant"] for b in fp8 if b["B"] == 1} == {"row_valu", "row_mfma", "col_mfma"}
+    assert {b["variant"] for b in fp8 if b["B"] == 16} == {"row_mfma", "col_mfma"}
+    # per shape, the bf16 blocks come before the FP8 ones (one weight set at a time)
+    for dm in (4096, 4104):
+        kinds = [b["op"].endswith("_fp8") for b in blocks if b["d_model"] == dm]
+        assert kinds == sorted(kinds)
+
+
+def test_ineligible_variant_never_wins():
+    blocks = tune.plan_blocks([(256, 688)], [1], reps=5)
+    per = [1.0 if b["variant"] == "col_mfma" else 5.0 for b in blocks]
+    bad = {("down", 1, 256, 688): {"col_mfma": "DFK_ERR_HIP"}}
+    entries = {e["op"]: e for e in tune.build_table(blocks, per, ineligible=bad)}
+    assert entries["gate_up"]["winner"] == "col_mfma"
+    assert entries["down"]["winner"] != "col_mfma"
+    assert entries["down"]["ineligible"] == {"col_mfma": "DFK_ERR_HIP"}
