@@ -21,7 +21,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "swiglu_oracle.c")
-LIBRARY = os.path.join(_HERE, "liboracle.so")
+# DFK_ORACLE_LIBRARY may name another build of the same source (the
+# sanitizer test runs the pins against an ASan/UBSan build).
+LIBRARY = os.environ.get("DFK_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 # No -ffast-math and no FMA contraction: every product and sum is one IEEE
 # fp64 operation, in source order.

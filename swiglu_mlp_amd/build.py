@@ -72,5 +72,39 @@ def build(verbose: bool = False, output: str = LIBRARY, defines=(), build_dir: s
     return output
 
 
+# Host-side sanitizer build: the C-ABI runtime (host C++ only) compiled with
+# g++ under AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+# regular HIP objects (GPU code is never built with a sanitizer).  Load it
+# with DFK_LIBRARY and libasan preloaded; for the CPU-side tests.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized(output: str, build_dir: str = BUILD_DIR) -> str:
+    """Link libdfk with an ASan/UBSan-instrumented runtime; returns the path.
+    The kernel objects come from `build_dir` (built first when missing)."""
+    os.makedirs(build_dir, exist_ok=True)
+    kernel_objs = []
+    for src in SOURCES:
+        if src.endswith(".cpp"):
+            continue
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(obj):
+            obj = _compile(src, (), build_dir)
+        kernel_objs.append(obj)
+    rt = os.path.join(os.path.dirname(os.path.abspath(output)), "dfk_runtime_san.o")
+    cc = ["g++", "-O1", "-g", "-fno-omit-frame-pointer", *SANITIZE, "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+          "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{INCLUDE}", f"-I{CSRC}",
+          "-c", os.path.join(CSRC, "dfk_runtime.cpp"), "-o", rt]
+    res = subprocess.run(cc, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cc)}\n{res.stderr}")
+    ld = ["g++", "-shared", *SANITIZE, rt, *kernel_objs, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib",
+          "-lamdhip64", "-ldl", "-o", output]
+    res = subprocess.run(ld, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(ld)}\n{res.stderr}")
+    return output
+
+
 if __name__ == "__main__":
     build(verbose=True)
