@@ -45,6 +45,20 @@
 
 namespace dfk {
 
+// Matrix-core steady loops: keep the next block's loads ahead of the current
+// block's work.  Without a scheduling fence the compiler sinks those loads
+// into (or past) the current block's MFMAs, and each block's weights then
+// arrive only after its predecessor is done: memory and matrix work
+// alternate instead of overlapping.
+#ifndef DFK_FENCE_LOADS
+#define DFK_FENCE_LOADS 1
+#endif
+#if DFK_FENCE_LOADS
+#define DFK_ISSUE_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define DFK_ISSUE_FENCE() ((void)0)
+#endif
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -1874,14 +1888,17 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
             int kb = kb_beg;
             for (; kb + 2 < kb_end; kb += 2) {
                 load_w(vg1, vu1, kb + 1);
+                DFK_ISSUE_FENCE();
                 step(vg0, vu0, kb);
                 if constexpr (kPre) load_block(kb + 1);
                 load_w(vg0, vu0, kb + 2);
+                DFK_ISSUE_FENCE();
                 step(vg1, vu1, kb + 1);
                 if constexpr (kPre) load_block(kb + 2);
             }
             if (kb + 1 < kb_end) {
                 load_w(vg1, vu1, kb + 1);
+                DFK_ISSUE_FENCE();
                 step(vg0, vu0, kb);
                 if constexpr (kPre) load_block(kb + 1);
                 step(vg1, vu1, kb + 1);
@@ -2027,14 +2044,17 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a)
             int kb = kb_beg;
             for (; kb + 2 < kb_end; kb += 2) {
                 load_w(v1, kb + 1);
+                DFK_ISSUE_FENCE();
                 step(v0, kb);
                 if constexpr (kPre) load_block(kb + 1);
                 load_w(v0, kb + 2);
+                DFK_ISSUE_FENCE();
                 step(v1, kb + 1);
                 if constexpr (kPre) load_block(kb + 2);
             }
             if (kb + 1 < kb_end) {
                 load_w(v1, kb + 1);
+                DFK_ISSUE_FENCE();
                 step(v0, kb);
                 if constexpr (kPre) load_block(kb + 1);
                 step(v1, kb + 1);
@@ -2326,6 +2346,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
         auto step = [&](auto &cg, auto &cu, auto &ng, auto &nu, int kb) {
             load_x(xr, kb + 1);
             load_w(ng, nu, kb + 1);
+            DFK_ISSUE_FENCE();
             compute(cg, cu, kb);
             if constexpr (NBUF == 1) __syncthreads();
             store_x(xr, kb + 1);
@@ -2494,6 +2515,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
         auto step = [&](auto &cw, auto &nw, int kb) {
             load_h(hr, kb + 1);
             load_w(nw, kb + 1);
+            DFK_ISSUE_FENCE();
             compute(cw, kb);
             if constexpr (NBUF == 1) __syncthreads();
             store_h(hr, kb + 1);
@@ -2655,6 +2677,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
         auto step = [&](auto &cg, auto &cu, auto &ng, auto &nu, int kb) {
             load_x(xr, kb + 1);
             load_w(ng, nu, kb + 1);
+            DFK_ISSUE_FENCE();
             compute(cg, cu, kb);
             if constexpr (NBUF == 1) __syncthreads();
             store_x(xr, kb + 1);
@@ -2781,6 +2804,7 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lts_kernel(DownArgs a
         auto step = [&](auto &cv, auto &nv, int kb) {
             load_h(hr, kb + 1);
             load_w(nv, kb + 1);
+            DFK_ISSUE_FENCE();
             compute(cv, kb);
             __syncthreads();
             store_h(hr, kb + 1);
