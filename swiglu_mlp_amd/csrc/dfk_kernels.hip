@@ -2846,6 +2846,167 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lts_kernel(DownArgs a
     }
 }
 
+// Down for several batch tiles: the LDS-transposed weight stream with h
+// staged per workgroup as bf16 hi + lo planes (as down_mfma_lts_kernel), but
+// each wave owns TR consecutive 16-row tiles.  A wave parks its tiles one after
+// the other in its single LDS tile and keeps their A fragments in registers,
+// so every B fragment read from LDS feeds TR tiles while the LDS holds only
+// one weight tile per wave next to the staged h (at four batch tiles, eight
+// waves: 66 KiB of h planes + 66 KiB of tiles).  The LDS-transposed loads (2
+// rows x 512 B per instruction) stream faster than A fragments loaded straight
+// from HBM (16 rows x 64 B), the shape of down_mfma_staged_kernel.  A work
+// item is (WAVES x TR row tiles, one of S K splits); S > 1 writes fp32 partial
+// sums that panel_reduce_kernel adds in split order.  Waves whose tiles are
+// past the end stream clamped rows and write nothing, so every wave reaches
+// every barrier.  The next block's loads are issued before the current
+// block's work (h first, then the weights); h(kb + 1) is parked once every
+// wave is done with h(kb).  F8: W_down is FP8 codes (a.qd), widened into the
+// tile, with row scales (a.sd) applied to each split's sums.
+template <int BT, int WAVES, int TR, int WPE, bool F8 = false>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_ltsw_kernel(
+    DownArgs a, float *partial, int S, int CS) {
+    using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
+    constexpr int KBC = 32;
+    constexpr int NT = WAVES * kWave;
+    constexpr int XR = 16 * BT;           // staged h rows: the padded batch
+    constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
+    static_assert(XR * KBC % NT == 0, "staging split");
+    constexpr int PLANE = XR * kStPitch;
+    extern __shared__ u32x4_t smem[];     // h hi [XR][kStPitch], lo [XR][kStPitch], then [WAVES][L::kTile]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lr = lane & 15, lq = lane >> 4;
+    u32x4_t *shi = smem, *slo = smem + PLANE;
+    u32x4_t *ltw = smem + 2 * PLANE + (size_t)wave * L::kTile;
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    const int row_groups = (a.groups + WAVES * TR - 1) / (WAVES * TR);
+    const int items = row_groups * S;
+
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int sp = it % S, g = it / S;
+        const int c0 = sp * CS, nch = min(CS, a.C - c0);
+        const int nb = (nch + KBC - 1) / KBC;
+        const int tile0 = (g * WAVES + wave) * TR;
+        f32x4_t acc[TR][BT];
+#pragma unroll
+        for (int t = 0; t < TR; ++t)
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) acc[t][bt] = fzero;
+        auto load_h = [&](f32x4_t (&hr)[XPT][2], int kb) {
+#pragma unroll
+            for (int t = 0; t < XPT; ++t) {
+                const int i = t * NT + tid;
+                const int b = min(i / KBC, a.B - 1);
+                const int c = min(c0 + kb * KBC + i % KBC, a.C - 1);
+                hr[t][0] = hg[(size_t)b * 2 * a.C + 2 * c];
+                hr[t][1] = hg[(size_t)b * 2 * a.C + 2 * c + 1];
+            }
+        };
+        auto store_h = [&](const f32x4_t (&hr)[XPT][2], int kb) {
+#pragma unroll
+            for (int t = 0; t < XPT; ++t) {
+                const int i = t * NT + tid;
+                const int b = i / KBC, cc = i % KBC;
+                const bool ok = b < a.B && kb * KBC + cc < nch;
+                bf16x8_t hi, lo;
+                split_hi_lo(ok ? hr[t][0] : fzero, ok ? hr[t][1] : fzero, hi, lo);
+                shi[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, hi);
+                slo[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, lo);
+            }
+        };
+        auto load_w = [&](u32x4_t (&v)[TR][L::kInsts], int kb) {
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                if constexpr (F8) L::load(v[t], a.qd + (size_t)c0 * 8, a.K, nch, (tile0 + t) * 16, a.M, kb, lane);
+                else L::load(v[t], a.wd + (size_t)c0 * 8, a.K, nch, (tile0 + t) * 16, a.M, kb, lane);
+            }
+        };
+        // each B fragment read from LDS serves the wave's TR row tiles
+        auto compute = [&](u32x4_t (&v)[TR][L::kInsts], int kb) {
+            bf16x8_t af[TR][L::kSteps];
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                L::store(ltw, v[t], kb, nch, lane);
+#pragma unroll
+                for (int j = 0; j < L::kSteps; ++j) af[t][j] = L::frag(ltw, j, lr, lq);
+            }
+#pragma unroll
+            for (int j = 0; j < L::kSteps; ++j) {
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const int o = (bt * 16 + lr) * kStPitch + 4 * j + lq;
+                    const bf16x8_t bhi = as_bf16x8(shi[o]), blo = as_bf16x8(slo[o]);
+#pragma unroll
+                    for (int t = 0; t < TR; ++t) {
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][j], bhi, acc[t][bt], 0, 0, 0);
+                        acc[t][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][j], blo, acc[t][bt], 0, 0, 0);
+                    }
+                }
+            }
+        };
+        f32x4_t hr[XPT][2];
+        u32x4_t v0[TR][L::kInsts], v1[TR][L::kInsts];
+        auto step = [&](auto &cv, auto &nv, int kb) {
+            load_h(hr, kb + 1);
+            load_w(nv, kb + 1);
+            DFK_ISSUE_FENCE();
+            compute(cv, kb);
+            __syncthreads();
+            store_h(hr, kb + 1);
+            __syncthreads();
+        };
+        auto last = [&](auto &cv, int kb) {
+            compute(cv, kb);
+            __syncthreads();
+        };
+        load_h(hr, 0);
+        load_w(v0, 0);
+        store_h(hr, 0);
+        __syncthreads();
+        int kb = 0;
+        for (; kb + 2 < nb; kb += 2) {
+            step(v0, v1, kb);
+            step(v1, v0, kb + 1);
+        }
+        if (kb + 1 < nb) {
+            step(v0, v1, kb);
+            last(v1, kb + 1);
+        } else {
+            last(v0, kb);
+        }
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+            const int tile = tile0 + t;
+            const int m = tile * 16 + 4 * lq;
+            float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (F8) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[e] = a.sd[min(m + e, a.M - 1)];
+            }
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const int b = bt * 16 + lr;
+                if (tile < a.groups && b < a.B && m < a.M) {
+                    f32x4_t v = acc[t][bt];
+                    if constexpr (F8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] *= sc[e];
+                    }
+                    if (S == 1) {
+                        const unsigned lo = to_bf16_rne(v[0]) | ((unsigned)to_bf16_rne(v[1]) << 16);
+                        const unsigned hi = to_bf16_rne(v[2]) | ((unsigned)to_bf16_rne(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(a.y + (size_t)b * a.M + m) = make_uint2(lo, hi);
+                    } else {
+                        *reinterpret_cast<f32x4_t *>(partial + ((size_t)sp * a.B + b) * a.M + m) = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ----------------------- MFMA, workgroup-cooperative weight tile (down) -----
 //
 // The down projection's row traversal on the matrix cores, for batches up to
@@ -3175,6 +3336,38 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_DN_LTS_MIN_CHUNKS
 #define DFK_DN_LTS_MIN_CHUNKS 128
 #endif
+// down column traversal from DFK_DN_LTSW_MIN_BT to DFK_DN_LTSW_MAX_BT batch
+// tiles (0: never): LDS-transposed weights, h staged per workgroup; workgroups
+// of DFK_DN_LTSW_WAVES waves, of four when at most two batch tiles meet fewer
+// row tiles than DFK_DN_LTSW_NARROW_PCT % of the CUs; DFK_DN_LTSW_TR row tiles
+// per wave at one or two batch tiles when the row tiles number at least
+// DFK_DN_LTSW_TR2_X per CU, one otherwise; K splits of at least
+// DFK_DN_LTSW_MIN_CHUNKS chunks.  DFK_DN_LTSW_F8 = 1: FP8 codes take the same
+// kernel.
+#ifndef DFK_DN_LTSW_MIN_BT
+#define DFK_DN_LTSW_MIN_BT 2
+#endif
+#ifndef DFK_DN_LTSW_MAX_BT
+#define DFK_DN_LTSW_MAX_BT 4
+#endif
+#ifndef DFK_DN_LTSW_WAVES
+#define DFK_DN_LTSW_WAVES 8
+#endif
+#ifndef DFK_DN_LTSW_TR
+#define DFK_DN_LTSW_TR 2
+#endif
+#ifndef DFK_DN_LTSW_TR2_X
+#define DFK_DN_LTSW_TR2_X 2
+#endif
+#ifndef DFK_DN_LTSW_F8
+#define DFK_DN_LTSW_F8 0
+#endif
+#ifndef DFK_DN_LTSW_MIN_CHUNKS
+#define DFK_DN_LTSW_MIN_CHUNKS 64
+#endif
+#ifndef DFK_DN_LTSW_NARROW_PCT
+#define DFK_DN_LTSW_NARROW_PCT 50
+#endif
 // B-operand-staged MFMA kernels: used from this many batch tiles up to
 // kStMaxBT (gate-up ROW traversal, down COL traversal); waves per workgroup
 // and LDS buffers per staged block
@@ -3461,6 +3654,80 @@ static bool staged_wide(bool gu, int BT, long tiles, int cus) {
               : ((BT >= 3 && 2 * tiles > (long)DFK_ST_DN_WIDE_X2 * cus) || tiles >= 2L * cus);
 }
 
+// The LDS-transposed staged-h down kernel: instances for (BT, waves, tiles
+// per wave); two tiles per wave up to two batch tiles only (beyond, the two
+// tiles' weights and fragments do not fit in registers without spilling)
+template <int BT, int W, int TR, bool F8> const void *ltsw_fn() {
+    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8>;
+}
+template <bool F8> const void *ltsw_pick(int BT, int W, int TR) {
+    static_assert(DFK_DN_LTSW_MAX_BT <= 4, "instantiated for BT <= 4");
+    static const void *const w8[2][4] = {
+        {ltsw_fn<1, 8, 1, F8>(), ltsw_fn<2, 8, 1, F8>(), ltsw_fn<3, 8, 1, F8>(), ltsw_fn<4, 8, 1, F8>()},
+        {ltsw_fn<1, 8, 2, F8>(), ltsw_fn<2, 8, 2, F8>(), nullptr, nullptr}};
+    static const void *const w4[4] = {ltsw_fn<1, 4, 1, F8>(), ltsw_fn<2, 4, 1, F8>(), ltsw_fn<3, 4, 1, F8>(),
+                                      ltsw_fn<4, 4, 1, F8>()};
+    return W >= 8 ? w8[TR > 1 ? 1 : 0][BT - 1] : w4[BT - 1];
+}
+
+// K split count for row_groups work-item rows over `slots` resident
+// workgroups: the S that minimizes the modelled HBM time, bytes streamed by
+// the busiest slots (rounds x slots x (split + a two-block ramp) of weights
+// per item) plus the split sums written and read back by the reduce.
+static long pick_splits(long row_groups, long rows_per_item, long C, long slots, long min_chunks, long B,
+                        long M) {
+    const long max_s = std::max(1L, C / min_chunks);
+    long best = 1;
+    double best_cost = 0.0;
+    for (long s = 1; s <= max_s; ++s) {
+        long cs = ceil_div(C, s);
+        if (C >= 32) cs = ceil_div(cs, 32L) * 32;
+        const long S = ceil_div(C, cs);
+        const long rounds = ceil_div(row_groups * S, slots);
+        const double cost = (double)rounds * slots * rows_per_item * (cs + 64) * 16.0 +
+                            (S > 1 ? 8.0 * S * B * M : 0.0);
+        if (s == 1 || cost < best_cost) {
+            best_cost = cost;
+            best = S;
+        }
+    }
+    return best;
+}
+
+// Fill the launch shape of down_mfma_ltsw_kernel (q holds the op, B, rows and
+// K): the waves and row tiles per wave of the DFK_DN_LTSW_* rules, one
+// workgroup per resident slot, and the K split of pick_splits (a multiple of
+// the 32-chunk block).
+static bool plan_ltsw(bool f8, int BT, int C, int cus, Plan *q) {
+    const long tiles = ceil_div((long)q->rows, 16L);
+    const int W = (BT <= 2 && 100 * tiles < (long)DFK_DN_LTSW_NARROW_PCT * cus) ? 4 : DFK_DN_LTSW_WAVES;
+    const int tr = (W >= 8 && BT <= 2 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR : 1;
+#if DFK_DN_LTSW_F8
+    const void *fn = f8 ? ltsw_pick<true>(BT, W, tr) : ltsw_pick<false>(BT, W, tr);
+#else
+    const void *fn = f8 ? nullptr : ltsw_pick<false>(BT, W, tr);
+#endif
+    if (!fn) return false;
+    q->kind = KIND_DN_MFMA_STAGED;
+    q->block = W * kWave;
+    q->lds_bytes = (size_t)2 * 16 * BT * kStPitch * 16 + (size_t)W * (f8 ? Lt8<32>::kTile : Lt<32>::kTile) * 16;
+    if (q->lds_bytes > kLdsLimit) return false;
+    q->rows_per_group = 16;
+    q->groups = (int)tiles;
+    const long occ = blocks_per_cu(fn, q->block, q->lds_bytes);
+    const long row_groups = ceil_div(tiles, (long)W * tr);
+    const long target = (long)cus * occ;
+    const long S = pick_splits(row_groups, 16L * W * tr, C, target, DFK_DN_LTSW_MIN_CHUNKS, q->B, q->rows);
+    long cs = ceil_div((long)C, S);
+    if (C >= 32) cs = ceil_div(cs, 32L) * 32;
+    q->splits = (int)ceil_div((long)C, cs);
+    q->chunks_per_split = (int)cs;
+    q->partial_floats = q->splits > 1 ? (size_t)q->splits * q->B * q->rows : 0;
+    q->grid = (int)std::max(1L, std::min(target, row_groups * q->splits));
+    q->fn = fn;
+    return true;
+}
+
 // Fill the launch shape of a B-operand-staged kernel (q holds the op, B,
 // rows and K): LDS per workgroup, a grid that fills every CU's resident
 // workgroups, and for down the K splits (none shorter than
@@ -3632,6 +3899,12 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
+        if (!gu && !row && BT >= DFK_DN_LTSW_MIN_BT && BT <= DFK_DN_LTSW_MAX_BT) {
+            // LDS-transposed weights, h staged in LDS, several row tiles per wave
+            if (!plan_ltsw(false, BT, C, cus, &q)) return false;
+            *out = q;
+            return true;
+        }
         if (BT >= (gu ? DFK_ST_GU_MIN_BT : DFK_ST_DN_MIN_BT) && BT <= kStMaxBT && (gu ? row : !row)) {
             // B operand staged in LDS per workgroup: gate-up ROW, down COL
             const long tiles = ceil_div(q.rows, 16);
@@ -3729,6 +4002,19 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
         const int BT = (int)ceil_div(B, 16);
         if (BT > kLtMaxBT) return false;
         const bool row = (trav == TRAV_ROW);
+        if (DFK_DN_LTSW_F8 && !gu && !row && BT >= DFK_DN_LTSW_MIN_BT && BT <= DFK_DN_LTSW_MAX_BT) {
+            Plan q{};
+            q.op = op;
+            q.engine = ENGINE_MFMA;
+            q.trav = trav;
+            q.B = B;
+            q.rows = d_model;
+            q.K = d_ff;
+            q.chunks_per_split = q.K / 8;
+            if (!plan_ltsw(true, BT, d_ff / 8, cus, &q)) return false;
+            *out = q;
+            return true;
+        }
         if (!gu && !row && BT >= DFK_ST_DN_F8_MIN_BT && BT <= kStMaxBT) {
             // h staged in LDS per workgroup, codes loaded as A fragments (as
             // for bf16 weights)
