@@ -3342,10 +3342,20 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 // row tiles than DFK_DN_LTSW_NARROW_PCT % of the CUs; DFK_DN_LTSW_TR row tiles
 // per wave at one or two batch tiles when the row tiles number at least
 // DFK_DN_LTSW_TR2_X per CU, one otherwise; K splits of at least
-// DFK_DN_LTSW_MIN_CHUNKS chunks.  DFK_DN_LTSW_F8 = 1: FP8 codes take the same
-// kernel.
+// DFK_DN_LTSW_MIN_CHUNKS chunks.  FP8 codes take the same kernel from
+// DFK_DN_LTSW_F8_MIN_BT to DFK_DN_LTSW_F8_MAX_BT batch tiles (event-timed
+// FP8 down, us at B = 4 / 8 / 16: 17.3 / 17.8 / 17.9 against 18.9 / 19.8 /
+// 22.2 on the staged kernel at the Llama-3-8B shape, 45.7 / 46.2 / 47.8
+// against 52.2 / 53.2 / 55.2 at Llama-3-70B; at three and four batch tiles it
+// lost, 94 / 115 against 76 / 87 us at 70B, B = 48 / 64).  With
+// DFK_DN_LTSW_MIN_BT above 1, bf16 weights at one batch tile take
+// down_mfma_lts_kernel instead (event-timed down, us at B = 1 / 8 / 16, that
+// kernel against this one: 8B shape 23.1 / 23.9 / 25.7 against 22.4 / 22.7 /
+// 23.2; 70B 76.2 / 79.5 / 80.3 against 73.2 / 73.7 / 74.5; 5120 x 13824
+// 31.3 / 32.1 / 34.4 against 25.7 / 26.3 / 27.0; 2048 x 5632 12.3 / 12.5 /
+// 12.7 against 9.3 / 9.7 / 10.1; 3072 x 8192 0.1-0.2 us faster).
 #ifndef DFK_DN_LTSW_MIN_BT
-#define DFK_DN_LTSW_MIN_BT 2
+#define DFK_DN_LTSW_MIN_BT 1
 #endif
 #ifndef DFK_DN_LTSW_MAX_BT
 #define DFK_DN_LTSW_MAX_BT 4
@@ -3359,8 +3369,11 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_DN_LTSW_TR2_X
 #define DFK_DN_LTSW_TR2_X 2
 #endif
-#ifndef DFK_DN_LTSW_F8
-#define DFK_DN_LTSW_F8 0
+#ifndef DFK_DN_LTSW_F8_MIN_BT
+#define DFK_DN_LTSW_F8_MIN_BT 1
+#endif
+#ifndef DFK_DN_LTSW_F8_MAX_BT
+#define DFK_DN_LTSW_F8_MAX_BT 1
 #endif
 #ifndef DFK_DN_LTSW_MIN_CHUNKS
 #define DFK_DN_LTSW_MIN_CHUNKS 64
@@ -3702,11 +3715,7 @@ static bool plan_ltsw(bool f8, int BT, int C, int cus, Plan *q) {
     const long tiles = ceil_div((long)q->rows, 16L);
     const int W = (BT <= 2 && 100 * tiles < (long)DFK_DN_LTSW_NARROW_PCT * cus) ? 4 : DFK_DN_LTSW_WAVES;
     const int tr = (W >= 8 && BT <= 2 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR : 1;
-#if DFK_DN_LTSW_F8
     const void *fn = f8 ? ltsw_pick<true>(BT, W, tr) : ltsw_pick<false>(BT, W, tr);
-#else
-    const void *fn = f8 ? nullptr : ltsw_pick<false>(BT, W, tr);
-#endif
     if (!fn) return false;
     q->kind = KIND_DN_MFMA_STAGED;
     q->block = W * kWave;
@@ -3845,7 +3854,7 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
-        if (!gu && !row && BT == 1) {
+        if (!gu && !row && BT == 1 && DFK_DN_LTSW_MIN_BT > 1) {
             // LDS-transposed weights with h staged in LDS per workgroup
             constexpr int W = DFK_DN_LTS_WAVES, WW = DFK_DN_LTS_WIDE_WAVES;
             q.groups = (int)ceil_div(q.rows, 16);
@@ -4002,7 +4011,7 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
         const int BT = (int)ceil_div(B, 16);
         if (BT > kLtMaxBT) return false;
         const bool row = (trav == TRAV_ROW);
-        if (DFK_DN_LTSW_F8 && !gu && !row && BT >= DFK_DN_LTSW_MIN_BT && BT <= DFK_DN_LTSW_MAX_BT) {
+        if (!gu && !row && BT >= DFK_DN_LTSW_F8_MIN_BT && BT <= DFK_DN_LTSW_F8_MAX_BT) {
             Plan q{};
             q.op = op;
             q.engine = ENGINE_MFMA;
