@@ -3268,6 +3268,23 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_GU_LTS_MAX_BT
 #define DFK_GU_LTS_MAX_BT 4
 #endif
+// the same kernel from this many batch tiles, bf16 and FP8 weights; bf16 at
+// one batch tile only while the row tiles number fewer than
+// DFK_GU_LTS_BT1_TILES_X10 / 10 per CU.  Event-timed gate-up row traversal,
+// us at B = 4 / 8 / 16, the LT kernel against this one: 3072 x 8192 20.0 /
+// 19.9 / 20.4 against 17.6 / 17.5 / 17.5; 5120 x 13824 48.3 / 49.4 / 53.6
+// against 47.0 / 47.0 / 47.2; but Llama-3-8B (3.5 tiles per CU) 39.7 / 40.2 /
+// 42.0 against 40.7 / 40.8 / 40.9 and Llama-3-70B 153 against 171.  FP8 codes
+// at one batch tile measured slower than their LT column kernel.
+#ifndef DFK_GU_LTS_MIN_BT
+#define DFK_GU_LTS_MIN_BT 1
+#endif
+#ifndef DFK_GU_LTS_BT1_TILES_X10
+#define DFK_GU_LTS_BT1_TILES_X10 35
+#endif
+#ifndef DFK_GU_LTS_F8_MIN_BT
+#define DFK_GU_LTS_F8_MIN_BT 2
+#endif
 #ifndef DFK_GU_LTS_WAVES
 #define DFK_GU_LTS_WAVES 4
 #endif
@@ -3882,15 +3899,18 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             *out = q;
             return true;
         }
-        if (gu && row && BT >= 2 && BT <= DFK_GU_LTS_MAX_BT) {
+        if (gu && row && BT >= DFK_GU_LTS_MIN_BT && BT <= DFK_GU_LTS_MAX_BT &&
+            (BT > 1 || 10 * ceil_div(q.rows, 16) < (long)DFK_GU_LTS_BT1_TILES_X10 * cus)) {
             // LDS-transposed weights, x staged in LDS per workgroup
             constexpr int W = DFK_GU_LTS_WAVES, WN = DFK_GU_LTS_NARROW_WAVES;
             constexpr int NB3 = DFK_GU_LTS_NBUF_BT3;
             static const void *const lts[2][4] = {
-                {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W>,
+                {DFK_GU_LTS_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, W> : nullptr,
+                 (const void *)gate_up_mfma_lts_kernel<2, W>,
                  (const void *)gate_up_mfma_lts_kernel<3, W, false, NB3>,
                  (const void *)gate_up_mfma_lts_kernel<4, W>},
-                {nullptr, (const void *)gate_up_mfma_lts_kernel<2, WN>, (const void *)gate_up_mfma_lts_kernel<3, WN>,
+                {DFK_GU_LTS_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, WN> : nullptr,
+                 (const void *)gate_up_mfma_lts_kernel<2, WN>, (const void *)gate_up_mfma_lts_kernel<3, WN>,
                  (const void *)gate_up_mfma_lts_kernel<4, WN>}};
             static_assert(DFK_GU_LTS_MAX_BT <= 4, "instantiated for BT <= 4");
             q.groups = (int)ceil_div(q.rows, 16);
@@ -4041,10 +4061,11 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
             *out = q;
             return true;
         }
-        if (gu && row && BT >= 2 && BT <= DFK_GU_LTS_MAX_BT) {
+        if (gu && row && BT >= DFK_GU_LTS_F8_MIN_BT && BT <= DFK_GU_LTS_MAX_BT) {
             // x staged in LDS per workgroup (as for bf16 weights)
             constexpr int W = DFK_GU_LTS_WAVES;
-            static const void *const lts[4] = {nullptr, (const void *)gate_up_mfma_lts_kernel<2, W, true>,
+            static const void *const lts[4] = {DFK_GU_LTS_F8_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, W, true> : nullptr,
+                                               (const void *)gate_up_mfma_lts_kernel<2, W, true>,
                                                (const void *)gate_up_mfma_lts_kernel<3, W, true>,
                                                (const void *)gate_up_mfma_lts_kernel<4, W, true>};
             Plan q{};
