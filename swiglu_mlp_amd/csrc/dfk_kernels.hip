@@ -2860,9 +2860,10 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lts_kernel(DownArgs a
 // past the end stream clamped rows and write nothing, so every wave reaches
 // every barrier.  The next block's loads are issued before the current
 // block's work (h first, then the weights); h(kb + 1) is parked once every
-// wave is done with h(kb).  F8: W_down is FP8 codes (a.qd), widened into the
-// tile, with row scales (a.sd) applied to each split's sums.
-template <int BT, int WAVES, int TR, int WPE, bool F8 = false>
+// wave is done with h(kb) (NBUF = 2: double-buffered h planes, one barrier
+// per block).  F8: W_down is FP8 codes (a.qd), widened into the tile, with
+// row scales (a.sd) applied to each split's sums.
+template <int BT, int WAVES, int TR, int WPE, bool F8 = false, int NBUF = 1>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_ltsw_kernel(
     DownArgs a, float *partial, int S, int CS) {
     using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
@@ -2872,13 +2873,12 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
     constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
     static_assert(XR * KBC % NT == 0, "staging split");
     constexpr int PLANE = XR * kStPitch;
-    extern __shared__ u32x4_t smem[];     // h hi [XR][kStPitch], lo [XR][kStPitch], then [WAVES][L::kTile]
+    extern __shared__ u32x4_t smem[];     // [NBUF][h hi [XR][kStPitch], lo [XR][kStPitch]], then [WAVES][L::kTile]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lr = lane & 15, lq = lane >> 4;
-    u32x4_t *shi = smem, *slo = smem + PLANE;
-    u32x4_t *ltw = smem + 2 * PLANE + (size_t)wave * L::kTile;
+    u32x4_t *ltw = smem + NBUF * 2 * PLANE + (size_t)wave * L::kTile;
     const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
     const int row_groups = (a.groups + WAVES * TR - 1) / (WAVES * TR);
@@ -2905,6 +2905,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
             }
         };
         auto store_h = [&](const f32x4_t (&hr)[XPT][2], int kb) {
+            u32x4_t *shi = smem + (NBUF == 2 ? (kb & 1) : 0) * 2 * PLANE, *slo = shi + PLANE;
 #pragma unroll
             for (int t = 0; t < XPT; ++t) {
                 const int i = t * NT + tid;
@@ -2925,6 +2926,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
         };
         // each B fragment read from LDS serves the wave's TR row tiles
         auto compute = [&](u32x4_t (&v)[TR][L::kInsts], int kb) {
+            const u32x4_t *shi = smem + (NBUF == 2 ? (kb & 1) : 0) * 2 * PLANE, *slo = shi + PLANE;
             bf16x8_t af[TR][L::kSteps];
 #pragma unroll
             for (int t = 0; t < TR; ++t) {
@@ -2953,7 +2955,9 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
             load_w(nv, kb + 1);
             DFK_ISSUE_FENCE();
             compute(cv, kb);
-            __syncthreads();
+            // with two buffers, h(kb + 1) goes to the one that block kb - 1
+            // used, released by the barrier that ended it
+            if constexpr (NBUF == 1) __syncthreads();
             store_h(hr, kb + 1);
             __syncthreads();
         };
@@ -3276,6 +3280,14 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 // against 47.0 / 47.0 / 47.2; but Llama-3-8B (3.5 tiles per CU) 39.7 / 40.2 /
 // 42.0 against 40.7 / 40.8 / 40.9 and Llama-3-70B 153 against 171.  FP8 codes
 // at one batch tile measured slower than their LT column kernel.
+#ifndef DFK_GU_LTS_NBUF_BT2
+#define DFK_GU_LTS_NBUF_BT2 1
+#endif
+// x buffers at four batch tiles (regular width): two measured 51.5 / 188.3 /
+// 64.2 us against 52.1 / 190.5 / 65.2 us at B = 64 (8B / 70B / 5120 x 13824)
+#ifndef DFK_GU_LTS_NBUF_BT4
+#define DFK_GU_LTS_NBUF_BT4 2
+#endif
 #ifndef DFK_GU_LTS_MIN_BT
 #define DFK_GU_LTS_MIN_BT 1
 #endif
@@ -3385,6 +3397,14 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #endif
 #ifndef DFK_DN_LTSW_TR2_X
 #define DFK_DN_LTSW_TR2_X 2
+#endif
+// h buffers of the bf16 instances at one or two batch tiles (two fit next to
+// the tiles there: one barrier per block instead of two).  Event-timed down,
+// us, one buffer against two: 8B B = 8 / 16 / 24 / 32 22.8 / 23.3 / 27.3 /
+// 28.7 against 22.6 / 23.1 / 26.8 / 27.6; 70B B = 32 84.0 against 81.9; FP8
+// codes within +-0.3 us either way, so they keep one.
+#ifndef DFK_DN_LTSW_NBUF_BT12
+#define DFK_DN_LTSW_NBUF_BT12 2
 #endif
 #ifndef DFK_DN_LTSW_F8_MIN_BT
 #define DFK_DN_LTSW_F8_MIN_BT 1
@@ -3687,8 +3707,10 @@ static bool staged_wide(bool gu, int BT, long tiles, int cus) {
 // The LDS-transposed staged-h down kernel: instances for (BT, waves, tiles
 // per wave); two tiles per wave up to two batch tiles only (beyond, the two
 // tiles' weights and fragments do not fit in registers without spilling)
+// two h buffers where they fit next to the tiles (bf16, one or two batch tiles)
+constexpr int ltsw_nbuf(int BT, bool f8) { return !f8 && BT <= 2 ? DFK_DN_LTSW_NBUF_BT12 : 1; }
 template <int BT, int W, int TR, bool F8> const void *ltsw_fn() {
-    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8>;
+    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8, ltsw_nbuf(BT, F8)>;
 }
 template <bool F8> const void *ltsw_pick(int BT, int W, int TR) {
     static_assert(DFK_DN_LTSW_MAX_BT <= 4, "instantiated for BT <= 4");
@@ -3736,7 +3758,8 @@ static bool plan_ltsw(bool f8, int BT, int C, int cus, Plan *q) {
     if (!fn) return false;
     q->kind = KIND_DN_MFMA_STAGED;
     q->block = W * kWave;
-    q->lds_bytes = (size_t)2 * 16 * BT * kStPitch * 16 + (size_t)W * (f8 ? Lt8<32>::kTile : Lt<32>::kTile) * 16;
+    q->lds_bytes = (size_t)ltsw_nbuf(BT, f8) * 2 * 16 * BT * kStPitch * 16 +
+                   (size_t)W * (f8 ? Lt8<32>::kTile : Lt<32>::kTile) * 16;
     if (q->lds_bytes > kLdsLimit) return false;
     q->rows_per_group = 16;
     q->groups = (int)tiles;
@@ -3906,9 +3929,9 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             constexpr int NB3 = DFK_GU_LTS_NBUF_BT3;
             static const void *const lts[2][4] = {
                 {DFK_GU_LTS_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, W> : nullptr,
-                 (const void *)gate_up_mfma_lts_kernel<2, W>,
+                 (const void *)gate_up_mfma_lts_kernel<2, W, false, DFK_GU_LTS_NBUF_BT2>,
                  (const void *)gate_up_mfma_lts_kernel<3, W, false, NB3>,
-                 (const void *)gate_up_mfma_lts_kernel<4, W>},
+                 (const void *)gate_up_mfma_lts_kernel<4, W, false, DFK_GU_LTS_NBUF_BT4>},
                 {DFK_GU_LTS_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, WN> : nullptr,
                  (const void *)gate_up_mfma_lts_kernel<2, WN>, (const void *)gate_up_mfma_lts_kernel<3, WN>,
                  (const void *)gate_up_mfma_lts_kernel<4, WN>}};
@@ -3918,7 +3941,7 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             const int w = narrow ? WN : W;
             q.kind = KIND_GU_MFMA_LT;
             q.block = w * kWave;
-            const int nbuf = (!narrow && BT == 3) ? NB3 : 1;
+            const int nbuf = narrow ? 1 : BT == 2 ? DFK_GU_LTS_NBUF_BT2 : BT == 3 ? NB3 : BT == 4 ? DFK_GU_LTS_NBUF_BT4 : 1;
             q.lds_bytes = (size_t)nbuf * 16 * BT * kStPitch * 16 + (size_t)w * 2 * Lt<32>::kTile * 16;
             if (q.lds_bytes > kLdsLimit) return false;
             q.rows_per_group = 16;
