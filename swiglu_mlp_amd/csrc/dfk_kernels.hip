@@ -2863,17 +2863,17 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lts_kernel(DownArgs a
 // wave is done with h(kb) (NBUF = 2: double-buffered h planes, one barrier
 // per block).  F8: W_down is FP8 codes (a.qd), widened into the tile, with
 // row scales (a.sd) applied to each split's sums.
-template <int BT, int WAVES, int TR, int WPE, bool F8 = false, int NBUF = 1>
+template <int BT, int WAVES, int TR, int WPE, bool F8 = false, int NBUF = 1, int KBC = 32>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_ltsw_kernel(
     DownArgs a, float *partial, int S, int CS) {
-    using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
-    constexpr int KBC = 32;
+    using L = typename Pick<F8, Lt8<KBC>, Lt<KBC>>::T;
+    constexpr int KP = KBC + 1;           // LDS pitch of a staged h row, chunks
     constexpr int NT = WAVES * kWave;
     constexpr int XR = 16 * BT;           // staged h rows: the padded batch
     constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
     static_assert(XR * KBC % NT == 0, "staging split");
-    constexpr int PLANE = XR * kStPitch;
-    extern __shared__ u32x4_t smem[];     // [NBUF][h hi [XR][kStPitch], lo [XR][kStPitch]], then [WAVES][L::kTile]
+    constexpr int PLANE = XR * KP;
+    extern __shared__ u32x4_t smem[];     // [NBUF][h hi [XR][KP], lo [XR][KP]], then [WAVES][L::kTile]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -2913,8 +2913,8 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
                 const bool ok = b < a.B && kb * KBC + cc < nch;
                 bf16x8_t hi, lo;
                 split_hi_lo(ok ? hr[t][0] : fzero, ok ? hr[t][1] : fzero, hi, lo);
-                shi[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, hi);
-                slo[b * kStPitch + cc] = __builtin_bit_cast(u32x4_t, lo);
+                shi[b * KP + cc] = __builtin_bit_cast(u32x4_t, hi);
+                slo[b * KP + cc] = __builtin_bit_cast(u32x4_t, lo);
             }
         };
         auto load_w = [&](u32x4_t (&v)[TR][L::kInsts], int kb) {
@@ -2938,7 +2938,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
             for (int j = 0; j < L::kSteps; ++j) {
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
-                    const int o = (bt * 16 + lr) * kStPitch + 4 * j + lq;
+                    const int o = (bt * 16 + lr) * KP + 4 * j + lq;
                     const bf16x8_t bhi = as_bf16x8(shi[o]), blo = as_bf16x8(slo[o]);
 #pragma unroll
                     for (int t = 0; t < TR; ++t) {
@@ -3403,6 +3403,28 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 // us, one buffer against two: 8B B = 8 / 16 / 24 / 32 22.8 / 23.3 / 27.3 /
 // 28.7 against 22.6 / 23.1 / 26.8 / 27.6; 70B B = 32 84.0 against 81.9; FP8
 // codes within +-0.3 us either way, so they keep one.
+// bf16 K block at four batch tiles: 32 chunks (256 elements) or 16.  With 16,
+// two row tiles per wave fit in registers (239 VGPRs, no spill), taken when
+// the row tiles number at least DFK_DN_LTSW_BT4_TR2_Q quarters per CU, and
+// three batch tiles run the four-tile instance (one zero tile; 48 rows x 16
+// chunks do not split evenly over 512 threads) when DFK_DN_LTSW_BT3_AS_BT4
+// and the row tiles number at least one per CU (B = 33 / 40 / 48, us: 70B
+// 100.6 / 102.3 / 105.3 -> 87.2 / 89.2 / 91.0; 5120 x 13824 39.2 / 40.2 ->
+// 36.0 / 36.1 at B = 40 / 48; 8B 31.4 / 32.4 / 33.1 -> 30.4 / 31.5 / 32.9; on
+// the two smaller shapes 0.4-1 us slower).
+// Event-timed down at B = 64, us, 32 chunks and one tile per wave against 16
+// chunks and two: 8B 39.4 against 35.8; 70B 123.8 against 95.8; 5120 x 13824
+// 45.6 against 39.3; 3072 x 8192 24.7 against 23.1; 2048 x 5632 (half a row
+// tile per CU) 16.9 against 19.4, and 16.4 with 16 chunks and one tile.
+#ifndef DFK_DN_LTSW_KBC_BT4
+#define DFK_DN_LTSW_KBC_BT4 16
+#endif
+#ifndef DFK_DN_LTSW_BT4_TR2_Q
+#define DFK_DN_LTSW_BT4_TR2_Q 3
+#endif
+#ifndef DFK_DN_LTSW_BT3_AS_BT4
+#define DFK_DN_LTSW_BT3_AS_BT4 1
+#endif
 #ifndef DFK_DN_LTSW_NBUF_BT12
 #define DFK_DN_LTSW_NBUF_BT12 2
 #endif
@@ -3707,16 +3729,23 @@ static bool staged_wide(bool gu, int BT, long tiles, int cus) {
 // The LDS-transposed staged-h down kernel: instances for (BT, waves, tiles
 // per wave); two tiles per wave up to two batch tiles only (beyond, the two
 // tiles' weights and fragments do not fit in registers without spilling)
-// two h buffers where they fit next to the tiles (bf16, one or two batch tiles)
-constexpr int ltsw_nbuf(int BT, bool f8) { return !f8 && BT <= 2 ? DFK_DN_LTSW_NBUF_BT12 : 1; }
+// K block (bf16 chunks) and h buffers: 128-element blocks at four batch tiles
+// (bf16) when DFK_DN_LTSW_KBC_BT4 says so, two buffers where they fit next to
+// the tiles
+constexpr int ltsw_kbc(int BT, bool f8) { return !f8 && BT == 4 ? DFK_DN_LTSW_KBC_BT4 : 32; }
+constexpr int ltsw_nbuf(int BT, bool f8) {
+    return !f8 && (BT <= 2 || ltsw_kbc(BT, f8) == 16) ? DFK_DN_LTSW_NBUF_BT12 : 1;
+}
 template <int BT, int W, int TR, bool F8> const void *ltsw_fn() {
-    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8, ltsw_nbuf(BT, F8)>;
+    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8, ltsw_nbuf(BT, F8),
+                                               ltsw_kbc(BT, F8)>;
 }
 template <bool F8> const void *ltsw_pick(int BT, int W, int TR) {
     static_assert(DFK_DN_LTSW_MAX_BT <= 4, "instantiated for BT <= 4");
     static const void *const w8[2][4] = {
         {ltsw_fn<1, 8, 1, F8>(), ltsw_fn<2, 8, 1, F8>(), ltsw_fn<3, 8, 1, F8>(), ltsw_fn<4, 8, 1, F8>()},
-        {ltsw_fn<1, 8, 2, F8>(), ltsw_fn<2, 8, 2, F8>(), nullptr, nullptr}};
+        {ltsw_fn<1, 8, 2, F8>(), ltsw_fn<2, 8, 2, F8>(), nullptr,
+         ltsw_kbc(4, F8) == 16 ? ltsw_fn<4, 8, 2, F8>() : nullptr}};
     static const void *const w4[4] = {ltsw_fn<1, 4, 1, F8>(), ltsw_fn<2, 4, 1, F8>(), ltsw_fn<3, 4, 1, F8>(),
                                       ltsw_fn<4, 4, 1, F8>()};
     return W >= 8 ? w8[TR > 1 ? 1 : 0][BT - 1] : w4[BT - 1];
@@ -3752,14 +3781,18 @@ static long pick_splits(long row_groups, long rows_per_item, long C, long slots,
 // the 32-chunk block).
 static bool plan_ltsw(bool f8, int BT, int C, int cus, Plan *q) {
     const long tiles = ceil_div((long)q->rows, 16L);
+    if (BT == 3 && DFK_DN_LTSW_BT3_AS_BT4 && ltsw_kbc(4, f8) == 16 && tiles >= cus) BT = 4;  // padded batch tile
     const int W = (BT <= 2 && 100 * tiles < (long)DFK_DN_LTSW_NARROW_PCT * cus) ? 4 : DFK_DN_LTSW_WAVES;
-    const int tr = (W >= 8 && BT <= 2 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR : 1;
+    const int tr = (W >= 8 && BT <= 2 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR
+                   : (W >= 8 && BT == 4 && ltsw_kbc(BT, f8) == 16 && 4 * tiles >= (long)DFK_DN_LTSW_BT4_TR2_Q * cus) ? 2
+                   : 1;
     const void *fn = f8 ? ltsw_pick<true>(BT, W, tr) : ltsw_pick<false>(BT, W, tr);
     if (!fn) return false;
     q->kind = KIND_DN_MFMA_STAGED;
     q->block = W * kWave;
-    q->lds_bytes = (size_t)ltsw_nbuf(BT, f8) * 2 * 16 * BT * kStPitch * 16 +
-                   (size_t)W * (f8 ? Lt8<32>::kTile : Lt<32>::kTile) * 16;
+    const int kbc = ltsw_kbc(BT, f8);
+    q->lds_bytes = (size_t)ltsw_nbuf(BT, f8) * 2 * 16 * BT * (kbc + 1) * 16 +
+                   (size_t)W * 16 * (kbc + 1) * 16;
     if (q->lds_bytes > kLdsLimit) return false;
     q->rows_per_group = 16;
     q->groups = (int)tiles;
