@@ -3419,6 +3419,14 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_DN_LTSW_KBC_BT4
 #define DFK_DN_LTSW_KBC_BT4 16
 #endif
+// the same at two batch tiles (B = 17 / 24 / 32, us, 32 chunks against 16:
+// 70B 78.2 / 79.1 / 81.3 against 74.6 / 75.4 / 77.4; 8B 26.1 / 26.5 / 27.4
+// against 25.0 / 26.1 / 27.3; 5120 x 13824 31.3 / 32.3 against 29.9 / 31.2 at
+// B = 24 / 32; 3072 x 8192 within 0.3 us).  One batch tile keeps 32 chunks:
+// 16 rows x 16 chunks do not split over eight waves.
+#ifndef DFK_DN_LTSW_KBC_BT2
+#define DFK_DN_LTSW_KBC_BT2 16
+#endif
 #ifndef DFK_DN_LTSW_BT4_TR2_Q
 #define DFK_DN_LTSW_BT4_TR2_Q 3
 #endif
@@ -3732,7 +3740,9 @@ static bool staged_wide(bool gu, int BT, long tiles, int cus) {
 // K block (bf16 chunks) and h buffers: 128-element blocks at four batch tiles
 // (bf16) when DFK_DN_LTSW_KBC_BT4 says so, two buffers where they fit next to
 // the tiles
-constexpr int ltsw_kbc(int BT, bool f8) { return !f8 && BT == 4 ? DFK_DN_LTSW_KBC_BT4 : 32; }
+constexpr int ltsw_kbc(int BT, bool f8) {
+    return f8 ? 32 : BT == 4 ? DFK_DN_LTSW_KBC_BT4 : BT == 2 ? DFK_DN_LTSW_KBC_BT2 : 32;
+}
 constexpr int ltsw_nbuf(int BT, bool f8) {
     return !f8 && (BT <= 2 || ltsw_kbc(BT, f8) == 16) ? DFK_DN_LTSW_NBUF_BT12 : 1;
 }
@@ -3783,8 +3793,9 @@ static bool plan_ltsw(bool f8, int BT, int C, int cus, Plan *q) {
     const long tiles = ceil_div((long)q->rows, 16L);
     if (BT == 3 && DFK_DN_LTSW_BT3_AS_BT4 && ltsw_kbc(4, f8) == 16 && tiles >= cus) BT = 4;  // padded batch tile
     const int W = (BT <= 2 && 100 * tiles < (long)DFK_DN_LTSW_NARROW_PCT * cus) ? 4 : DFK_DN_LTSW_WAVES;
-    const int tr = (W >= 8 && BT <= 2 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR
-                   : (W >= 8 && BT == 4 && ltsw_kbc(BT, f8) == 16 && 4 * tiles >= (long)DFK_DN_LTSW_BT4_TR2_Q * cus) ? 2
+    const bool k16 = ltsw_kbc(BT, f8) == 16;
+    const int tr = (W >= 8 && BT <= 2 && !k16 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR
+                   : (W >= 8 && k16 && 4 * tiles >= (long)DFK_DN_LTSW_BT4_TR2_Q * cus) ? 2
                    : 1;
     const void *fn = f8 ? ltsw_pick<true>(BT, W, tr) : ltsw_pick<false>(BT, W, tr);
     if (!fn) return false;
