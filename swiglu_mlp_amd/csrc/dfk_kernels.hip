@@ -3427,6 +3427,13 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_DN_LTSW_KBC_BT2
 #define DFK_DN_LTSW_KBC_BT2 16
 #endif
+// one batch tile with 16 chunks needs four-wave workgroups; measured mixed
+// against eight waves and 32 chunks (us at B = 1 / 4 / 16: 8B 23.3 / 23.4 /
+// 25.3 against 22.8 / 22.8 / 23.1; 3072 x 8192 12.4 / 12.8 / 14.1 against 13.2
+// / 13.4 / 14.0; 70B 72.3 / 72.4 / 76.6 against 73.4 / 73.6 / 74.6), so 32
+#ifndef DFK_DN_LTSW_KBC_BT1
+#define DFK_DN_LTSW_KBC_BT1 32
+#endif
 #ifndef DFK_DN_LTSW_BT4_TR2_Q
 #define DFK_DN_LTSW_BT4_TR2_Q 3
 #endif
@@ -3644,6 +3651,19 @@ template <int BT> KernelInfo gu_lt_col_f8() {
     constexpr int W = DFK_LT_GU_WAVES(BT), KS = DFK_LT_GU_KSPLIT(BT);
     return {(const void *)gate_up_mfma_lt_kernel<BT, KS, W, true>, 16, W * kWave, KS, 2 * BT * 4};
 }
+// FP8 gate-up column traversal on shapes with fewer than
+// DFK_LT_GU_F8_KS2_TILES row tiles per CU: K split two ways, two tiles per
+// workgroup.  Event-timed FP8 gate-up, us at B = 4 / 8 / 16, four-way against
+// two-way: 8B 25.3 / 26.1 / 29.6 against 24.2 / 24.4 / 27.9; 5120 x 13824 31.4 /
+// 38.3 against 29.4 / 36.3 at B = 4 / 16; but 70B (7 tiles per CU) 76.5 / 90.8
+// against 94.4 / 104.9 at B = 4 / 16.
+#ifndef DFK_LT_GU_F8_KS2_TILES
+#define DFK_LT_GU_F8_KS2_TILES 4
+#endif
+template <int BT> KernelInfo gu_lt_col_f8_k2() {
+    constexpr int W = DFK_LT_GU_WAVES(BT);
+    return {(const void *)gate_up_mfma_lt_kernel<BT, 2, W, true>, 16, W * kWave, 2, 2 * BT * 4};
+}
 template <int BT> KernelInfo dn_lt_row_f8() {
     constexpr int W = DFK_LT_DN_WAVES(BT);
     return {(const void *)down_mfma_lt_kernel<BT, 1, W, DFK_LT_DN_KBC, true>, 16, W * kWave, 1, BT * 4};
@@ -3654,6 +3674,7 @@ template <int BT> KernelInfo dn_lt_col_f8() {
 }
 static const KernelInfo kGuLtRowF8[kLtMaxBT] = DFK_B_TABLE(gu_lt_row_f8);
 static const KernelInfo kGuLtColF8[kLtMaxBT] = DFK_B_TABLE(gu_lt_col_f8);
+static const KernelInfo kGuLtColF8K2[kLtMaxBT] = DFK_B_TABLE(gu_lt_col_f8_k2);
 static const KernelInfo kDnLtRowF8[kLtMaxBT] = DFK_B_TABLE(dn_lt_row_f8);
 static const KernelInfo kDnLtColF8[kLtMaxBT] = DFK_B_TABLE(dn_lt_col_f8);
 constexpr int kStMaxBT = 8;
@@ -3740,25 +3761,27 @@ static bool staged_wide(bool gu, int BT, long tiles, int cus) {
 // K block (bf16 chunks) and h buffers: 128-element blocks at four batch tiles
 // (bf16) when DFK_DN_LTSW_KBC_BT4 says so, two buffers where they fit next to
 // the tiles
-constexpr int ltsw_kbc(int BT, bool f8) {
-    return f8 ? 32 : BT == 4 ? DFK_DN_LTSW_KBC_BT4 : BT == 2 ? DFK_DN_LTSW_KBC_BT2 : 32;
+constexpr int ltsw_kbc(int BT, bool f8, int W) {
+    return f8 ? 32 : BT == 4 ? DFK_DN_LTSW_KBC_BT4 : BT == 2 ? DFK_DN_LTSW_KBC_BT2
+                   : (BT == 1 && W < 8) ? DFK_DN_LTSW_KBC_BT1 : 32;
 }
-constexpr int ltsw_nbuf(int BT, bool f8) {
-    return !f8 && (BT <= 2 || ltsw_kbc(BT, f8) == 16) ? DFK_DN_LTSW_NBUF_BT12 : 1;
+constexpr int ltsw_nbuf(int BT, bool f8, int W) {
+    return !f8 && (BT <= 2 || ltsw_kbc(BT, f8, W) == 16) ? DFK_DN_LTSW_NBUF_BT12 : 1;
 }
 template <int BT, int W, int TR, bool F8> const void *ltsw_fn() {
-    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8, ltsw_nbuf(BT, F8),
-                                               ltsw_kbc(BT, F8)>;
+    return (const void *)down_mfma_ltsw_kernel<BT, W, TR, (W >= 8 ? 2 : 1), F8, ltsw_nbuf(BT, F8, W),
+                                               ltsw_kbc(BT, F8, W)>;
 }
 template <bool F8> const void *ltsw_pick(int BT, int W, int TR) {
     static_assert(DFK_DN_LTSW_MAX_BT <= 4, "instantiated for BT <= 4");
     static const void *const w8[2][4] = {
         {ltsw_fn<1, 8, 1, F8>(), ltsw_fn<2, 8, 1, F8>(), ltsw_fn<3, 8, 1, F8>(), ltsw_fn<4, 8, 1, F8>()},
         {ltsw_fn<1, 8, 2, F8>(), ltsw_fn<2, 8, 2, F8>(), nullptr,
-         ltsw_kbc(4, F8) == 16 ? ltsw_fn<4, 8, 2, F8>() : nullptr}};
+         ltsw_kbc(4, F8, 8) == 16 ? ltsw_fn<4, 8, 2, F8>() : nullptr}};
     static const void *const w4[4] = {ltsw_fn<1, 4, 1, F8>(), ltsw_fn<2, 4, 1, F8>(), ltsw_fn<3, 4, 1, F8>(),
                                       ltsw_fn<4, 4, 1, F8>()};
-    return W >= 8 ? w8[TR > 1 ? 1 : 0][BT - 1] : w4[BT - 1];
+    static const void *const w4tr2 = ltsw_kbc(1, F8, 4) == 16 ? ltsw_fn<1, 4, 2, F8>() : nullptr;
+    return W >= 8 ? w8[TR > 1 ? 1 : 0][BT - 1] : (TR > 1 && BT == 1) ? w4tr2 : w4[BT - 1];
 }
 
 // K split count for row_groups work-item rows over `slots` resident
@@ -3791,18 +3814,19 @@ static long pick_splits(long row_groups, long rows_per_item, long C, long slots,
 // the 32-chunk block).
 static bool plan_ltsw(bool f8, int BT, int C, int cus, Plan *q) {
     const long tiles = ceil_div((long)q->rows, 16L);
-    if (BT == 3 && DFK_DN_LTSW_BT3_AS_BT4 && ltsw_kbc(4, f8) == 16 && tiles >= cus) BT = 4;  // padded batch tile
-    const int W = (BT <= 2 && 100 * tiles < (long)DFK_DN_LTSW_NARROW_PCT * cus) ? 4 : DFK_DN_LTSW_WAVES;
-    const bool k16 = ltsw_kbc(BT, f8) == 16;
+    if (BT == 3 && DFK_DN_LTSW_BT3_AS_BT4 && ltsw_kbc(4, f8, 8) == 16 && tiles >= cus) BT = 4;  // padded batch tile
+    const int W = ((BT <= 2 && 100 * tiles < (long)DFK_DN_LTSW_NARROW_PCT * cus) || (BT == 1 && ltsw_kbc(1, f8, 4) == 16))
+                      ? 4 : DFK_DN_LTSW_WAVES;
+    const bool k16 = ltsw_kbc(BT, f8, W) == 16;
     const int tr = (W >= 8 && BT <= 2 && !k16 && tiles >= (long)DFK_DN_LTSW_TR2_X * cus) ? DFK_DN_LTSW_TR
-                   : (W >= 8 && k16 && 4 * tiles >= (long)DFK_DN_LTSW_BT4_TR2_Q * cus) ? 2
+                   : ((W >= 8 || BT == 1) && k16 && 4 * tiles >= (long)DFK_DN_LTSW_BT4_TR2_Q * cus) ? 2
                    : 1;
     const void *fn = f8 ? ltsw_pick<true>(BT, W, tr) : ltsw_pick<false>(BT, W, tr);
     if (!fn) return false;
     q->kind = KIND_DN_MFMA_STAGED;
     q->block = W * kWave;
-    const int kbc = ltsw_kbc(BT, f8);
-    q->lds_bytes = (size_t)ltsw_nbuf(BT, f8) * 2 * 16 * BT * (kbc + 1) * 16 +
+    const int kbc = ltsw_kbc(BT, f8, W);
+    q->lds_bytes = (size_t)ltsw_nbuf(BT, f8, W) * 2 * 16 * BT * (kbc + 1) * 16 +
                    (size_t)W * 16 * (kbc + 1) * 16;
     if (q->lds_bytes > kLdsLimit) return false;
     q->rows_per_group = 16;
@@ -4156,7 +4180,9 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
             *out = q;
             return true;
         }
-        const KernelInfo ki = row ? (gu ? kGuLtRowF8 : kDnLtRowF8)[BT - 1] : (gu ? kGuLtColF8 : kDnLtColF8)[BT - 1];
+        const bool ks2 = gu && !row && ceil_div((long)d_ff, 16L) < (long)DFK_LT_GU_F8_KS2_TILES * cus;
+        const KernelInfo ki = row ? (gu ? kGuLtRowF8 : kDnLtRowF8)[BT - 1]
+                                  : (gu ? (ks2 ? kGuLtColF8K2 : kGuLtColF8) : kDnLtColF8)[BT - 1];
         Plan q{};
         q.op = op;
         q.engine = ENGINE_MFMA;
