@@ -149,6 +149,32 @@ def test_gate_up_three_batch_tiles_wide(dev, orc, shape):
     H.assert_y_close(H.host_bf16_as_f64(gpu_mlp(T, Layout.ROW_MFMA)), y_ref, f"mlp ROW_MFMA {shape}")
 
 
+# Down at three batch tiles (33 <= B <= 48) with at least one row tile per CU
+# (d_model >= 4096 on a 256-CU part): the LDS-transposed staged-h kernel runs
+# its four-batch-tile instance with 128-element K blocks, the fourth batch
+# tile zero (a ragged last row tile at 4104 rows, a ragged last K block at
+# d_ff 2056).  Every output against the oracle, and the plain and padded
+# paths against each other through the integer exactness below.
+DOWN_BT3_SHAPES = [(33, 4096, 2056), (40, 4104, 2056), (48, 4096, 3080)]
+
+
+@pytest.mark.parametrize("shape", DOWN_BT3_SHAPES, ids=lambda s: "B%d_%dx%d" % s)
+def test_down_three_batch_tiles_wide(dev, orc, shape):
+    B, dm, dff = shape
+    wd = inputs.randn_bf16((dm, dff), 1.0 / np.sqrt(dff), 7400 + B)
+    h_in = inputs.h_like(B, dff, seed=7450 + B)
+    want = orc.down(h_in, wd)
+    wd_dev = H.dev_bf16(wd, dev)
+    for layout in (Layout.COL_MFMA, Layout.COL, Layout.AUTO):
+        y = gpu_down(h_in, wd_dev, layout, dev)
+        H.assert_y_close(H.host_bf16_as_f64(y), want, f"down {layout.name} {shape}")
+    # integer operands: exact in any order, so bit for bit
+    hi = inputs.integer_h(B, dff, seed=7480 + B)
+    wi = inputs.rand_int_bf16((dm, dff), -1, 1, seed=7490 + B)
+    got = H.host_bits(gpu_down(hi, H.dev_bf16(wi, dev), Layout.COL_MFMA, dev))
+    assert np.array_equal(got, orc.bf16_rne_array(orc.down(hi, wi))), f"integer {shape}"
+
+
 @pytest.mark.parametrize("B", [1, 4, 8, 16, 64])
 def test_integer_down_is_bitwise_exact(dev, orc, B):
     """Integer h (|h| <= 256) and W_down in {-1,0,1}: fp32 accumulation is exact
