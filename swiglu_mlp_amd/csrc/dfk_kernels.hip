@@ -2580,17 +2580,17 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
 // barrier.
 // F8: the weights are FP8 codes (a.qg, a.qu) with row scales (a.sg, a.su).
 // NBUF = 2 double-buffers the staged x block (one barrier per block).
-template <int BT, int WAVES, bool F8 = false, int NBUF = 1>
+template <int BT, int WAVES, bool F8 = false, int NBUF = 1, int KBC = 32>
 __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpArgs a) {
-    using L = typename Pick<F8, Lt8<32>, Lt<32>>::T;
-    constexpr int KBC = 32;
+    using L = typename Pick<F8, Lt8<KBC>, Lt<KBC>>::T;
+    constexpr int KP = KBC + 1;           // LDS pitch of a staged x row, chunks
     constexpr int NT = WAVES * kWave;
     constexpr int XR = 16 * BT;           // staged x rows: the padded batch
     constexpr int XPT = XR * KBC / NT;    // staged chunks per thread
     static_assert(XR * KBC % NT == 0, "staging split");
     static_assert(!(F8 && NBUF == 2), "FP8 instances keep one x buffer");
-    constexpr int XBUF = XR * kStPitch;
-    extern __shared__ u32x4_t smem[];     // x blocks [NBUF][XR][kStPitch], then [WAVES][2][L::kTile]
+    constexpr int XBUF = XR * KP;
+    extern __shared__ u32x4_t smem[];     // x blocks [NBUF][XR][KP], then [WAVES][2][L::kTile]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -2624,7 +2624,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
             const int i = t * NT + tid;
             const int b = i / KBC, cc = i % KBC;
             const bool ok = b < a.B && kb * KBC + cc < a.C;
-            xd[b * kStPitch + cc] = ok ? xr[t] : zero;
+            xd[b * KP + cc] = ok ? xr[t] : zero;
         }
     };
 
@@ -2662,7 +2662,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
                 const bf16x8_t au = L::frag(ltu, j, lr, lq);
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
-                    const bf16x8_t xb = as_bf16x8(xd[(bt * 16 + lr) * kStPitch + 4 * j + lq]);
+                    const bf16x8_t xb = as_bf16x8(xd[(bt * 16 + lr) * KP + 4 * j + lq]);
                     accg[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb, accg[bt], 0, 0, 0);
                     accu[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb, accu[bt], 0, 0, 0);
                 }
@@ -3290,6 +3290,28 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #endif
 #ifndef DFK_GU_LTS_MIN_BT
 #define DFK_GU_LTS_MIN_BT 1
+#endif
+// K block of the bf16 staged-x gate-up kernel: 16 chunks (128 elements, a
+// double-buffered x block, a third of the LDS) from DFK_GU_LTS_K16_MIN_BT
+// batch tiles, with four-wave workgroups from DFK_GU_LTS_K16_W4_X row tiles
+// per CU and two-wave ones below (more workgroups per CU).  Event-timed
+// gate-up at B = 64, us, 32 chunks against 16: 8B 51.8 against 48.8 (four
+// waves); 70B 188.5 against 185.0 (four); 5120 x 13824 64.4 against 56.2
+// (four); 3072 x 8192 31.1 against 27.7 (two); 2048 x 5632 21.9 against 19.7
+// (two).  At three batch tiles (B = 40 / 48) 8B 46.1 / 46.2 against 44.7 /
+// 44.9, 5120 x 13824 56.8 / 57.0 against 49.8 / 50.4, 3072 x 8192 and 2048 x
+// 5632 1.1-1.8 us faster, but 70B 168.9 / 170.1 against 178.5 / 176.7: there
+// (at least DFK_GU_LTS_K16_BT3_MAX_X row tiles per CU) 32 chunks stay.  At two
+// batch tiles it was shape-dependent (70B B = 32: 159 against 166-175 us), so
+// 32 chunks stay there.
+#ifndef DFK_GU_LTS_K16_MIN_BT
+#define DFK_GU_LTS_K16_MIN_BT 3
+#endif
+#ifndef DFK_GU_LTS_K16_BT3_MAX_X
+#define DFK_GU_LTS_K16_BT3_MAX_X 4
+#endif
+#ifndef DFK_GU_LTS_K16_W4_X
+#define DFK_GU_LTS_K16_W4_X 3
 #endif
 #ifndef DFK_GU_LTS_BT1_TILES_X10
 #define DFK_GU_LTS_BT1_TILES_X10 35
@@ -4005,6 +4027,25 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
                  (const void *)gate_up_mfma_lts_kernel<4, WN>}};
             static_assert(DFK_GU_LTS_MAX_BT <= 4, "instantiated for BT <= 4");
             q.groups = (int)ceil_div(q.rows, 16);
+            if (BT >= DFK_GU_LTS_K16_MIN_BT && (BT > 3 || q.groups < (long)DFK_GU_LTS_K16_BT3_MAX_X * cus)) {
+                // 128-element blocks, x double-buffered
+                static const void *const lts16[2][2] = {
+                    {(const void *)gate_up_mfma_lts_kernel<3, 2, false, 2, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<4, 2, false, 2, 16>},
+                    {(const void *)gate_up_mfma_lts_kernel<3, 4, false, 2, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<4, 4, false, 2, 16>}};
+                static_assert(DFK_GU_LTS_K16_MIN_BT >= 3, "instantiated for BT 3 and 4");
+                const int w = q.groups >= (long)DFK_GU_LTS_K16_W4_X * cus ? 4 : 2;
+                q.kind = KIND_GU_MFMA_LT;
+                q.block = w * kWave;
+                q.lds_bytes = (size_t)2 * 16 * BT * 17 * 16 + (size_t)w * 2 * Lt<16>::kTile * 16;
+                q.rows_per_group = 16;
+                q.fn = lts16[w == 4 ? 1 : 0][BT - 3];
+                const long occ = blocks_per_cu(q.fn, q.block, q.lds_bytes);
+                q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)w)));
+                *out = q;
+                return true;
+            }
             const bool narrow = 2L * q.groups < (long)(BT == 2 ? DFK_GU_LTS_NARROW_X2_BT2 : DFK_GU_LTS_NARROW_X2) * cus;
             const int w = narrow ? WN : W;
             q.kind = KIND_GU_MFMA_LT;
