@@ -3310,6 +3310,18 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_GU_LTS_K16_BT3_MAX_X
 #define DFK_GU_LTS_K16_BT3_MAX_X 4
 #endif
+// FP8 codes in the staged-x gate-up kernel from this many batch tiles:
+// 128-element blocks (one x buffer), workgroup width as for bf16.  Event-timed
+// FP8 gate-up, us at B = 40 / 64, 256-element blocks against 128: 70B 141.8 /
+// 168.4 against 107.7 / 124.7; 3072 x 8192 28.9 / 34.0 against 22.0 / 25.5;
+// 2048 x 5632 20.4 / 23.7 against 15.9 / 18.2; 5120 x 13824 46.5 / 54.8
+// against 46.5 / 51.3; 8B 38.2 / 44.9 against 38.3 / 42.6; at B = 24 / 32 70B
+// 121.3 / 121.1 against 95.6 / 98.6, 3072 x 8192 24.6 / 24.8 against 21.7 /
+// 21.7, 2048 x 5632 17.3 / 17.4 against 15.3 / 15.3, 8B and 5120 x 13824
+// within 0.3 us.
+#ifndef DFK_GU_LTS_F8_K16_MIN_BT
+#define DFK_GU_LTS_F8_K16_MIN_BT 2
+#endif
 #ifndef DFK_GU_LTS_K16_W4_X
 #define DFK_GU_LTS_K16_W4_X 3
 #endif
@@ -4210,6 +4222,27 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
             q.splits = 1;
             q.chunks_per_split = q.K / 8;
             q.kind = KIND_GU_MFMA_LT;
+            q.groups = (int)ceil_div(q.rows, 16);
+            if (BT >= DFK_GU_LTS_F8_K16_MIN_BT) {
+                // 128-element blocks (as for bf16 weights; one x buffer)
+                static_assert(DFK_GU_LTS_F8_K16_MIN_BT >= 2, "instantiated for BT 2 to 4");
+                static const void *const lts16[2][3] = {
+                    {(const void *)gate_up_mfma_lts_kernel<2, 2, true, 1, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<3, 2, true, 1, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<4, 2, true, 1, 16>},
+                    {(const void *)gate_up_mfma_lts_kernel<2, 4, true, 1, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<3, 4, true, 1, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<4, 4, true, 1, 16>}};
+                const int w = q.groups >= (long)DFK_GU_LTS_K16_W4_X * cus ? 4 : 2;
+                q.block = w * kWave;
+                q.lds_bytes = (size_t)16 * BT * 17 * 16 + (size_t)w * 2 * Lt8<16>::kTile * 16;
+                q.rows_per_group = 16;
+                q.fn = lts16[w == 4 ? 1 : 0][BT - 2];
+                const long occ = blocks_per_cu(q.fn, q.block, q.lds_bytes);
+                q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)w)));
+                *out = q;
+                return true;
+            }
             q.block = W * kWave;
             q.lds_bytes = (size_t)16 * BT * kStPitch * 16 + (size_t)W * 2 * Lt8<32>::kTile * 16;
             if (q.lds_bytes > kLdsLimit) return false;
