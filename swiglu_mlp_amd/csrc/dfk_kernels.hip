@@ -3575,8 +3575,19 @@ template <int B, bool HLDS> KernelInfo dn_valu_row_t() {
     constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
     return {(const void *)down_valu_row_kernel<B, R, U, HLDS>, R, kValuBlock, 1, 0};
 }
+// rows per workgroup and load groups in flight of the down column walk: one
+// row at B = 1, else those of the row walk.  Event-timed down column walk,
+// us at B = 1, two rows against one: 8B 21.2 against 19.6 (the row walk:
+// 19.7-20.1), 5120 x 13824 24.7 against 22.7, 3072 x 8192 and 2048 x 5632
+// within 0.1 us; at B = 2 one row was 1-4 us slower.
+#ifndef DFK_DN_VALU_COL_R
+#define DFK_DN_VALU_COL_R(B) ((B) == 1 ? 1 : DFK_DN_VALU_R(B))
+#endif
+#ifndef DFK_DN_VALU_COL_U
+#define DFK_DN_VALU_COL_U(B) DFK_DN_VALU_U(B)
+#endif
 template <int B, bool HLDS> KernelInfo dn_valu_col_t() {
-    constexpr int R = DFK_DN_VALU_R(B), U = DFK_DN_VALU_U(B);
+    constexpr int R = DFK_DN_VALU_COL_R(B), U = DFK_DN_VALU_COL_U(B);
     return {(const void *)down_valu_col_kernel<B, R, U, HLDS>, R, kValuBlock, kValuBlock / kWave, R * B};
 }
 // load groups in flight per lane in the K-panel down walk (B = 4: one, which
