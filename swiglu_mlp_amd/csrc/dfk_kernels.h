@@ -39,7 +39,8 @@ enum Kind {
     KIND_DN_MFMA_COOP = 15,    // down ROW (B <= 16), workgroup-cooperative LDS weight tile
     KIND_GU_FP8_ROW = 16,      // gate-up over FP8 E4M3 weights + row scales, VALU row walk
     KIND_DN_FP8_ROW = 17,      // down, the same
-    KIND_DN_VALU_PANEL = 18    // down VALU row walk over K panels whose h fits in LDS + a reduce kernel
+    KIND_DN_VALU_PANEL = 18,   // down VALU row walk over K panels whose h fits in LDS + a reduce kernel
+    KIND_DN_VALU_HREG = 19     // down VALU column walk, h held in registers, row groups pipelined
 };
 
 // A fully resolved launch: which kernel and how the weight matrix is cut.

@@ -1535,6 +1535,164 @@ __global__ __launch_bounds__(kValuBlock) void down_valu_col_kernel(DownArgs a) {
     }
 }
 
+// ================================== VALU down, h held in registers =====
+//
+// The down projection at small batch with h kept in registers for the whole
+// launch.  A workgroup's waves cut K (d_ff) into contiguous slices, one per
+// wave; lane l of wave w holds h[b][8c .. 8c+7] for the chunks
+// c = c_w + l + 64 j (j < J) of its slice, for every batch row b.  The
+// workgroup then walks groups of R rows of W_down (groups blockIdx.x,
+// blockIdx.x + gridDim.x, ...): each wave streams its slice of every row of
+// the group (one load instruction = 1 KB contiguous of one row), the loads of
+// the next group are in flight while the current group is multiplied, and the
+// waves' sums are added in wave order through LDS (two buffers, one barrier
+// per group; the barrier waits for LDS traffic only, so the prefetched
+// weights stay in flight across it).  No K split crosses workgroups, so no
+// second kernel adds partial sums, and h is read from memory once per
+// workgroup.
+constexpr int kHregMaxWaves = 16;
+
+// LDS-only workgroup barrier: this wave's LDS writes are done and every wave
+// has arrived; outstanding global loads are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Largest workgroup an instance is compiled for: 16 waves hold at most 128
+// VGPRs each, so the instances with more than four chunks per lane (used with
+// at most eight waves) get 256.
+constexpr int hreg_max_waves(int J) { return J <= 4 ? kHregMaxWaves : 8; }
+
+template <int B, int J, int R>
+__global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kernel(DownArgs a) {
+    __shared__ float red[2][kHregMaxWaves][R * B];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = blockDim.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int cw = (a.C + waves - 1) / waves;
+    const int c_beg = min(wave * cw, a.C);
+    const int c_end = min(c_beg + cw, a.C);
+    // this lane's chunks; one past the slice loads a chunk in bounds (the
+    // slice's last, or chunk 0 for an empty slice) and multiplies it by zero
+    int cj[J];
+    bool okj[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = c_beg + lane + kWave * j;
+        okj[j] = c < c_end;
+        cj[j] = okj[j] ? c : (c_end > c_beg ? c_end - 1 : 0);
+    }
+    const u32x4_t *wd = reinterpret_cast<const u32x4_t *>(a.wd);
+    const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
+    // row groups of this workgroup: blockIdx.x + t * gridDim.x, t < n
+    if ((int)blockIdx.x >= a.groups) return;  // the whole workgroup, before any barrier
+    const int n = (a.groups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    auto load = [&](u32x4_t (&w)[J][R], int t) {
+        const int gi = (int)blockIdx.x + t * (int)gridDim.x;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = min(gi * R + r, a.M - 1);
+            const u32x4_t *p = wd + (size_t)m * a.C;
+#pragma unroll
+            for (int j = 0; j < J; ++j) w[j][r] = load_stream(p + cj[j]);
+        }
+    };
+    u32x4_t w0[J][R], w1[J][R];
+    load(w0, 0);
+    DFK_ISSUE_FENCE();
+    f32x4_t hv[J][B][2];
+    const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const f32x4_t h0 = hg[(size_t)b * 2 * a.C + 2 * cj[j]];
+            const f32x4_t h1 = hg[(size_t)b * 2 * a.C + 2 * cj[j] + 1];
+            hv[j][b][0] = okj[j] ? h0 : fzero;
+            hv[j][b][1] = okj[j] ? h1 : fzero;
+        }
+    float acc[R][B];
+    auto compute = [&](const u32x4_t (&w)[J][R]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const u32x4_t v = w[j][r];
+                const float e0 = bf16_lo(v.x), e1 = bf16_hi(v.x), e2 = bf16_lo(v.y), e3 = bf16_hi(v.y),
+                            e4 = bf16_lo(v.z), e5 = bf16_hi(v.z), e6 = bf16_lo(v.w), e7 = bf16_hi(v.w);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const f32x4_t h0 = hv[j][b][0], h1 = hv[j][b][1];
+                    float t = acc[r][b];
+                    t = fmaf(e0, h0.x, t);
+                    t = fmaf(e1, h0.y, t);
+                    t = fmaf(e2, h0.z, t);
+                    t = fmaf(e3, h0.w, t);
+                    t = fmaf(e4, h1.x, t);
+                    t = fmaf(e5, h1.y, t);
+                    t = fmaf(e6, h1.z, t);
+                    t = fmaf(e7, h1.w, t);
+                    acc[r][b] = t;
+                }
+            }
+    };
+    // group t's sums go through LDS buffer t & 1: a buffer is written again
+    // two groups later, after a barrier that wave 0 reaches only when it has
+    // read the buffer
+    auto finish = [&](int t) {
+        const int buf = t & 1;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = wave_sum_to_lane63(acc[r][b]);
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int b = 0; b < B; ++b) red[buf][wave][r * B + b] = acc[r][b];
+        }
+        lds_barrier();
+        if (wave == 0 && lane < R * B) {
+            float v = 0.0f;
+            for (int w = 0; w < waves; ++w) v += red[buf][w][lane];
+            const int r = lane / B, b = lane - (lane / B) * B;
+            const int m = ((int)blockIdx.x + t * (int)gridDim.x) * R + r;
+            if (m < a.M) a.y[(size_t)b * a.M + m] = to_bf16_rne(v);
+        }
+    };
+    // group t is in w0 at the top of each turn; the loads in the loop are
+    // unconditional, so the compiler's load counting waits only for the
+    // buffer about to be multiplied
+    int t = 0;
+    for (; t + 2 < n; t += 2) {
+        load(w1, t + 1);
+        DFK_ISSUE_FENCE();
+        compute(w0);
+        finish(t);
+        load(w0, t + 2);
+        DFK_ISSUE_FENCE();
+        compute(w1);
+        finish(t + 1);
+    }
+    if (t + 1 < n) {
+        load(w1, t + 1);
+        DFK_ISSUE_FENCE();
+        compute(w0);
+        finish(t);
+        compute(w1);
+        finish(t + 1);
+    } else {
+        compute(w0);
+        finish(t);
+    }
+}
+
 // ================================================================ MFMA =====
 //
 // v_mfma_f32_16x16x32_bf16, lane l: r = l & 15, q = l >> 4.
@@ -3924,6 +4082,69 @@ static bool plan_staged(bool gu, int B, int BT, int C, int cus, const KernelInfo
 
 
 
+// Down with h held in registers (COL traversal, vector ALU): instances for
+// J chunks per lane and batch B where the J * 8 * B h registers stay within
+// DFK_DN_HREG_VGPRS; R rows per group.  The plan takes the first waves-per-
+// workgroup count (DFK_DN_HREG_WAVES, then 16, 8, 4) whose slice gives an
+// instantiated J.
+#ifndef DFK_DN_HREG
+#define DFK_DN_HREG 1
+#endif
+#ifndef DFK_DN_HREG_VGPRS
+#define DFK_DN_HREG_VGPRS 64
+#endif
+// rows per group: two where a lane holds at most two chunks of h per batch
+// row (Llama-3-8B down at B = 3 / 4, 16-wave workgroups: 22.9 / 24.1 ->
+// 21.2 / 22.3 us), else one (two at four chunks: B = 1 20.2 -> 22.5 us)
+#ifndef DFK_DN_HREG_R
+#define DFK_DN_HREG_R(J) ((J) <= 2 ? 2 : 1)
+#endif
+#ifndef DFK_DN_HREG_WAVES
+#define DFK_DN_HREG_WAVES 8
+#endif
+// from this batch up (at B = 1 the column walk with h in LDS is as fast or
+// faster on the larger shapes: kernel durations at 4096 x 14336 19.7 against
+// 20.4 us, at 5120 x 13824 22.8 against 23.8 us)
+#ifndef DFK_DN_HREG_MIN_B
+#define DFK_DN_HREG_MIN_B 2
+#endif
+constexpr int kHregMaxJ = 8;
+template <int B, int J> const void *hreg_inst() {
+    if constexpr (J * 8 * B <= DFK_DN_HREG_VGPRS) return (const void *)down_valu_hreg_kernel<B, J, DFK_DN_HREG_R(J)>;
+    else return nullptr;
+}
+#define DFK_HREG_ROW(B) \
+    {hreg_inst<B, 1>(), hreg_inst<B, 2>(), hreg_inst<B, 3>(), hreg_inst<B, 4>(), \
+     hreg_inst<B, 5>(), hreg_inst<B, 6>(), hreg_inst<B, 7>(), hreg_inst<B, 8>()}
+static const void *const kDnHreg[kValuMaxBatch][kHregMaxJ] = {
+    DFK_HREG_ROW(1), DFK_HREG_ROW(2), DFK_HREG_ROW(3), DFK_HREG_ROW(4),
+    DFK_HREG_ROW(5), DFK_HREG_ROW(6), DFK_HREG_ROW(7), DFK_HREG_ROW(8)};
+#undef DFK_HREG_ROW
+
+static bool plan_hreg(int B, int C, int M, int cus, Plan *q) {
+    if (!DFK_DN_HREG || B < DFK_DN_HREG_MIN_B || B > kValuMaxBatch || C < 1) return false;
+    const int order[4] = {DFK_DN_HREG_WAVES, 16, 8, 4};
+    for (int w : order) {
+        if (w < 1 || w > kHregMaxWaves) continue;
+        const long J = ceil_div(ceil_div((long)C, (long)w), (long)kWave);
+        if (J > kHregMaxJ) continue;
+        const void *fn = kDnHreg[B - 1][J - 1];
+        if (!fn || w > hreg_max_waves((int)J)) continue;
+        q->kind = KIND_DN_VALU_HREG;
+        q->block = w * kWave;
+        q->lds_bytes = 0;
+        q->rows_per_group = DFK_DN_HREG_R((int)J);
+        q->groups = (int)ceil_div((long)M, (long)q->rows_per_group);
+        const long slots = (long)cus * blocks_per_cu(fn, q->block, 0);
+        // balanced: every workgroup walks the same number of row groups
+        const long per_wg = ceil_div((long)q->groups, slots);
+        q->grid = (int)std::max(1L, ceil_div((long)q->groups, per_wg));
+        q->fn = fn;
+        return true;
+    }
+    return false;
+}
+
 bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out,
                bool norm) {
     if (B < 1 || d_model < 8 || d_ff < 8 || (d_model % 8) || (d_ff % 8) || cus < 1) return false;
@@ -3951,6 +4172,10 @@ bool make_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_f
             if (q.lds_bytes > kLdsLimit) return false;
             q.fused_norm = norm;
             q.kind = row ? KIND_GU_VALU_ROW : KIND_GU_VALU_COL;
+        } else if (!row && plan_hreg(B, q.K / 8, q.rows, cus, &q)) {
+            // h in registers, row groups walked with the next group's loads in flight
+            *out = q;
+            return true;
         } else if (row && (size_t)B * q.K * 4 > DFK_HLDS_LIMIT) {
             // h does not fit in LDS whole: cut K into the fewest panels whose h
             // slice does (32 bytes per weight chunk and batch row), partial

@@ -175,6 +175,29 @@ def test_down_three_batch_tiles_wide(dev, orc, shape):
     assert np.array_equal(got, orc.bf16_rne_array(orc.down(hi, wi))), f"integer {shape}"
 
 
+# Down column walk with h held in registers (vector ALU, 2 <= B <= 8 where
+# h fits the lane's registers): shapes where every workgroup walks several row
+# groups, an odd number of them (5 and 3: the two-group turn plus a single
+# tail group) and an even number (4), with one or two rows per group, slices
+# of one to three chunks per lane and 8- and 16-wave workgroups.  Every output
+# against the oracle; integer operands bit for bit.
+DOWN_HREG_SHAPES = [(2, 8200, 1000), (2, 6144, 3000), (3, 2048, 9000), (4, 4096, 2056), (8, 4096, 1024)]
+
+
+@pytest.mark.parametrize("shape", DOWN_HREG_SHAPES, ids=lambda s: "B%d_%dx%d" % s)
+def test_down_h_in_registers_walks(dev, orc, shape):
+    B, dm, dff = shape
+    wd = inputs.randn_bf16((dm, dff), 1.0 / np.sqrt(dff), 7500 + B)
+    h_in = inputs.h_like(B, dff, seed=7550 + B)
+    want = orc.down(h_in, wd)
+    y = gpu_down(h_in, H.dev_bf16(wd, dev), Layout.COL_VALU, dev)
+    H.assert_y_close(H.host_bf16_as_f64(y), want, f"down COL_VALU {shape}")
+    hi = inputs.integer_h(B, dff, seed=7580 + B)
+    wi = inputs.rand_int_bf16((dm, dff), -1, 1, seed=7590 + B)
+    got = H.host_bits(gpu_down(hi, H.dev_bf16(wi, dev), Layout.COL_VALU, dev))
+    assert np.array_equal(got, orc.bf16_rne_array(orc.down(hi, wi))), f"integer {shape}"
+
+
 @pytest.mark.parametrize("B", [1, 4, 8, 16, 64])
 def test_integer_down_is_bitwise_exact(dev, orc, B):
     """Integer h (|h| <= 256) and W_down in {-1,0,1}: fp32 accumulation is exact
