@@ -221,7 +221,10 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * multiplied by its scale once.  The computed h and out are those of the bf16
  * entry points over the dequantized weights (to fp32 summation order).
  * Engines: the vector-ALU row walk (B <= 8; x kept in LDS, so
- * B * d_model * 2 <= 160 KiB) and the matrix-core kernels (B <= 128),
+ * B * d_model * 2 <= 160 KiB), for the down projection also a vector-ALU
+ * column walk with h held in registers (B <= 4, d_ff small enough that a
+ * lane's share of h fits: 16 * B fp32 per 16-byte chunk, at most 64), and
+ * the matrix-core kernels (B <= 128),
  * which widen the codes to bf16 exactly: on their way into LDS, or in
  * registers (the down projection's column traversal).  Layouts:
  * AUTO = the tuning table's FP8 entry for the shape (see
@@ -229,8 +232,9 @@ dfk_status_t dfk_swiglu_mlp_packed(const uint16_t *x, const uint16_t *W_gu, cons
  * (gate-up: vector ALU to B = 3, matrix-core column traversal to B = 16, row
  * traversal above; down: vector ALU to B = 2, matrix-core column traversal
  * above); ROW = vector ALU up to B = 8, else matrix cores; COL = matrix
- * cores; ROW_VALU, ROW_MFMA, COL_MFMA force the engine; COL_VALU and
- * ROW_PERSISTENT are DFK_ERR_UNSUPPORTED.  d_model and d_ff must be
+ * cores; ROW_VALU, ROW_MFMA, COL_MFMA force the engine; COL_VALU forces
+ * the down column walk (DFK_ERR_UNSUPPORTED for gate-up, and where h does
+ * not fit); ROW_PERSISTENT is DFK_ERR_UNSUPPORTED.  d_model and d_ff must be
  * multiples of 16.  Code and tensor pointers must be 16-byte aligned, scale
  * pointers 4-byte aligned.
  */

@@ -1565,8 +1565,13 @@ __device__ __forceinline__ void lds_barrier() {
 // at most eight waves) get 256.
 constexpr int hreg_max_waves(int J) { return J <= 4 ? kHregMaxWaves : 8; }
 
-template <int B, int J, int R>
+// F8: W_down as FP8 E4M3 codes with a scale per row (16 codes per 16-byte
+// chunk, widened exactly to fp32; y = bf16(scale * sum)); a.C counts the
+// 16-byte chunks of a row either way.  Each lane's scale for a group rides
+// with the group's weight loads, issued before them.
+template <int B, int J, int R, bool F8 = false>
 __global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kernel(DownArgs a) {
+    constexpr int H4 = F8 ? 4 : 2;  // f32x4 of h per chunk and batch row
     __shared__ float red[2][kHregMaxWaves][R * B];
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = blockDim.x / kWave;
@@ -1584,13 +1589,18 @@ __global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kern
         okj[j] = c < c_end;
         cj[j] = okj[j] ? c : (c_end > c_beg ? c_end - 1 : 0);
     }
-    const u32x4_t *wd = reinterpret_cast<const u32x4_t *>(a.wd);
+    const u32x4_t *wd = reinterpret_cast<const u32x4_t *>(F8 ? static_cast<const void *>(a.qd)
+                                                              : static_cast<const void *>(a.wd));
     const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
     // row groups of this workgroup: blockIdx.x + t * gridDim.x, t < n
     if ((int)blockIdx.x >= a.groups) return;  // the whole workgroup, before any barrier
     const int n = (a.groups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    auto load = [&](u32x4_t (&w)[J][R], int t) {
+    // F8: the lanes that write y (lane < R * B, row lane / B) load their row's
+    // scale; the others load row 0's
+    const int srow = lane < R * B ? lane / B : 0;
+    auto load = [&](u32x4_t (&w)[J][R], float &sc, int t) {
         const int gi = (int)blockIdx.x + t * (int)gridDim.x;
+        if constexpr (F8) sc = a.sd[min(gi * R + srow, a.M - 1)];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int m = min(gi * R + r, a.M - 1);
@@ -1600,19 +1610,20 @@ __global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kern
         }
     };
     u32x4_t w0[J][R], w1[J][R];
-    load(w0, 0);
+    float s0 = 1.0f, s1 = 1.0f;
+    load(w0, s0, 0);
     DFK_ISSUE_FENCE();
-    f32x4_t hv[J][B][2];
+    f32x4_t hv[J][B][H4];
     const f32x4_t fzero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const f32x4_t h0 = hg[(size_t)b * 2 * a.C + 2 * cj[j]];
-            const f32x4_t h1 = hg[(size_t)b * 2 * a.C + 2 * cj[j] + 1];
-            hv[j][b][0] = okj[j] ? h0 : fzero;
-            hv[j][b][1] = okj[j] ? h1 : fzero;
-        }
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int q = 0; q < H4; ++q) {
+                const f32x4_t v = hg[((size_t)b * a.C + cj[j]) * H4 + q];
+                hv[j][b][q] = okj[j] ? v : fzero;
+            }
     float acc[R][B];
     auto compute = [&](const u32x4_t (&w)[J][R]) {
 #pragma unroll
@@ -1624,28 +1635,49 @@ __global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kern
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const u32x4_t v = w[j][r];
-                const float e0 = bf16_lo(v.x), e1 = bf16_hi(v.x), e2 = bf16_lo(v.y), e3 = bf16_hi(v.y),
-                            e4 = bf16_lo(v.z), e5 = bf16_hi(v.z), e6 = bf16_lo(v.w), e7 = bf16_hi(v.w);
+                if constexpr (F8) {
+                    // chunk element 4q + i is code i of word q
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const f32x4_t h0 = hv[j][b][0], h1 = hv[j][b][1];
-                    float t = acc[r][b];
-                    t = fmaf(e0, h0.x, t);
-                    t = fmaf(e1, h0.y, t);
-                    t = fmaf(e2, h0.z, t);
-                    t = fmaf(e3, h0.w, t);
-                    t = fmaf(e4, h1.x, t);
-                    t = fmaf(e5, h1.y, t);
-                    t = fmaf(e6, h1.z, t);
-                    t = fmaf(e7, h1.w, t);
-                    acc[r][b] = t;
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t word = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+                        float e0, e1, e2, e3;
+                        e4m3x2_to_f32<false>(word, e0, e1);
+                        e4m3x2_to_f32<true>(word, e2, e3);
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            const f32x4_t hq = hv[j][b][q];
+                            float t = acc[r][b];
+                            t = fmaf(e0, hq.x, t);
+                            t = fmaf(e1, hq.y, t);
+                            t = fmaf(e2, hq.z, t);
+                            t = fmaf(e3, hq.w, t);
+                            acc[r][b] = t;
+                        }
+                    }
+                } else {
+                    const float e0 = bf16_lo(v.x), e1 = bf16_hi(v.x), e2 = bf16_lo(v.y), e3 = bf16_hi(v.y),
+                                e4 = bf16_lo(v.z), e5 = bf16_hi(v.z), e6 = bf16_lo(v.w), e7 = bf16_hi(v.w);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const f32x4_t h0 = hv[j][b][0], h1 = hv[j][b][1];
+                        float t = acc[r][b];
+                        t = fmaf(e0, h0.x, t);
+                        t = fmaf(e1, h0.y, t);
+                        t = fmaf(e2, h0.z, t);
+                        t = fmaf(e3, h0.w, t);
+                        t = fmaf(e4, h1.x, t);
+                        t = fmaf(e5, h1.y, t);
+                        t = fmaf(e6, h1.z, t);
+                        t = fmaf(e7, h1.w, t);
+                        acc[r][b] = t;
+                    }
                 }
             }
     };
     // group t's sums go through LDS buffer t & 1: a buffer is written again
     // two groups later, after a barrier that wave 0 reaches only when it has
     // read the buffer
-    auto finish = [&](int t) {
+    auto finish = [&](int t, float sc) {
         const int buf = t & 1;
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -1661,6 +1693,7 @@ __global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kern
         if (wave == 0 && lane < R * B) {
             float v = 0.0f;
             for (int w = 0; w < waves; ++w) v += red[buf][w][lane];
+            if constexpr (F8) v = sc * v;
             const int r = lane / B, b = lane - (lane / B) * B;
             const int m = ((int)blockIdx.x + t * (int)gridDim.x) * R + r;
             if (m < a.M) a.y[(size_t)b * a.M + m] = to_bf16_rne(v);
@@ -1671,25 +1704,25 @@ __global__ __launch_bounds__(hreg_max_waves(J) * kWave) void down_valu_hreg_kern
     // buffer about to be multiplied
     int t = 0;
     for (; t + 2 < n; t += 2) {
-        load(w1, t + 1);
+        load(w1, s1, t + 1);
         DFK_ISSUE_FENCE();
         compute(w0);
-        finish(t);
-        load(w0, t + 2);
+        finish(t, s0);
+        load(w0, s0, t + 2);
         DFK_ISSUE_FENCE();
         compute(w1);
-        finish(t + 1);
+        finish(t + 1, s1);
     }
     if (t + 1 < n) {
-        load(w1, t + 1);
+        load(w1, s1, t + 1);
         DFK_ISSUE_FENCE();
         compute(w0);
-        finish(t);
+        finish(t, s0);
         compute(w1);
-        finish(t + 1);
+        finish(t + 1, s1);
     } else {
         compute(w0);
-        finish(t);
+        finish(t, s0);
     }
 }
 
@@ -4109,31 +4142,44 @@ static bool plan_staged(bool gu, int B, int BT, int C, int cus, const KernelInfo
 #define DFK_DN_HREG_MIN_B 2
 #endif
 constexpr int kHregMaxJ = 8;
+// FP8 codes: 16 h values per chunk and batch row, so J * 16 * B registers,
+// and two rows per group at one chunk per lane
+#ifndef DFK_DN_HREG_F8_R
+#define DFK_DN_HREG_F8_R(J) ((J) <= 1 ? 2 : 1)
+#endif
 template <int B, int J> const void *hreg_inst() {
     if constexpr (J * 8 * B <= DFK_DN_HREG_VGPRS) return (const void *)down_valu_hreg_kernel<B, J, DFK_DN_HREG_R(J)>;
     else return nullptr;
 }
-#define DFK_HREG_ROW(B) \
-    {hreg_inst<B, 1>(), hreg_inst<B, 2>(), hreg_inst<B, 3>(), hreg_inst<B, 4>(), \
-     hreg_inst<B, 5>(), hreg_inst<B, 6>(), hreg_inst<B, 7>(), hreg_inst<B, 8>()}
+template <int B, int J> const void *hreg_inst_f8() {
+    if constexpr (J * 16 * B <= DFK_DN_HREG_VGPRS)
+        return (const void *)down_valu_hreg_kernel<B, J, DFK_DN_HREG_F8_R(J), true>;
+    else return nullptr;
+}
+#define DFK_HREG_ROW(F, B) \
+    {F<B, 1>(), F<B, 2>(), F<B, 3>(), F<B, 4>(), F<B, 5>(), F<B, 6>(), F<B, 7>(), F<B, 8>()}
 static const void *const kDnHreg[kValuMaxBatch][kHregMaxJ] = {
-    DFK_HREG_ROW(1), DFK_HREG_ROW(2), DFK_HREG_ROW(3), DFK_HREG_ROW(4),
-    DFK_HREG_ROW(5), DFK_HREG_ROW(6), DFK_HREG_ROW(7), DFK_HREG_ROW(8)};
+    DFK_HREG_ROW(hreg_inst, 1), DFK_HREG_ROW(hreg_inst, 2), DFK_HREG_ROW(hreg_inst, 3), DFK_HREG_ROW(hreg_inst, 4),
+    DFK_HREG_ROW(hreg_inst, 5), DFK_HREG_ROW(hreg_inst, 6), DFK_HREG_ROW(hreg_inst, 7), DFK_HREG_ROW(hreg_inst, 8)};
+static const void *const kDnHregF8[4][kHregMaxJ] = {
+    DFK_HREG_ROW(hreg_inst_f8, 1), DFK_HREG_ROW(hreg_inst_f8, 2), DFK_HREG_ROW(hreg_inst_f8, 3),
+    DFK_HREG_ROW(hreg_inst_f8, 4)};
 #undef DFK_HREG_ROW
 
-static bool plan_hreg(int B, int C, int M, int cus, Plan *q) {
-    if (!DFK_DN_HREG || B < DFK_DN_HREG_MIN_B || B > kValuMaxBatch || C < 1) return false;
+// C: 16-byte chunks per W_down row (K / 8 bf16, K / 16 FP8 codes)
+static bool plan_hreg(int B, int C, int M, int cus, Plan *q, bool f8 = false) {
+    if (!DFK_DN_HREG || B < (f8 ? 1 : DFK_DN_HREG_MIN_B) || B > (f8 ? 4 : kValuMaxBatch) || C < 1) return false;
     const int order[4] = {DFK_DN_HREG_WAVES, 16, 8, 4};
     for (int w : order) {
         if (w < 1 || w > kHregMaxWaves) continue;
         const long J = ceil_div(ceil_div((long)C, (long)w), (long)kWave);
         if (J > kHregMaxJ) continue;
-        const void *fn = kDnHreg[B - 1][J - 1];
+        const void *fn = (f8 ? kDnHregF8 : kDnHreg)[B - 1][J - 1];
         if (!fn || w > hreg_max_waves((int)J)) continue;
         q->kind = KIND_DN_VALU_HREG;
         q->block = w * kWave;
         q->lds_bytes = 0;
-        q->rows_per_group = DFK_DN_HREG_R((int)J);
+        q->rows_per_group = f8 ? DFK_DN_HREG_F8_R((int)J) : DFK_DN_HREG_R((int)J);
         q->groups = (int)ceil_div((long)M, (long)q->rows_per_group);
         const long slots = (long)cus * blocks_per_cu(fn, q->block, 0);
         // balanced: every workgroup walks the same number of row groups
@@ -4406,6 +4452,22 @@ hipError_t launch_mlp(const MlpPlan &p, const uint16_t *x, const uint16_t *w_gat
 bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int d_ff, int cus, Plan *out) {
     if (B < 1 || d_model < 16 || d_ff < 16 || (d_model % 16) || (d_ff % 16) || cus < 1) return false;
     const bool gu = (op == OP_GATE_UP);
+    if (engine == ENGINE_VALU && trav == TRAV_COL) {
+        // down only: the column walk with h held in registers
+        if (gu) return false;
+        Plan q{};
+        q.op = op;
+        q.engine = engine;
+        q.trav = trav;
+        q.B = B;
+        q.rows = d_model;
+        q.K = d_ff;
+        q.splits = 1;
+        q.chunks_per_split = q.K / 16;
+        if (!plan_hreg(B, d_ff / 16, d_model, cus, &q, true)) return false;
+        *out = q;
+        return true;
+    }
     if (engine == ENGINE_MFMA) {
         // the LDS-transposed matrix-core kernels, FP8 codes widened into LDS
         const int BT = (int)ceil_div(B, 16);
@@ -4580,6 +4642,13 @@ hipError_t launch_gate_up_fp8(const Plan &p, const uint16_t *x, const uint8_t *q
 
 hipError_t launch_down_fp8(const Plan &p, const float *h, const uint8_t *q_down, const float *s_down, uint16_t *y,
                            float *partial, hipStream_t stream) {
+    if (p.kind == KIND_DN_VALU_HREG) {
+        DownArgs a{};
+        a.h = h; a.qd = q_down; a.sd = s_down; a.y = y;
+        a.B = p.B; a.K = p.K; a.M = p.rows; a.C = p.K / 16; a.groups = p.groups;
+        void *argv[] = {&a};
+        return hipLaunchKernel(p.fn, dim3(p.grid), dim3(p.block), argv, p.lds_bytes, stream);
+    }
     if (p.kind == KIND_DN_MFMA_LT) {
         DownArgs a{};
         a.h = h; a.qd = q_down; a.sd = s_down; a.y = y;

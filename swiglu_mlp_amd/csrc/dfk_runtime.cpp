@@ -405,9 +405,8 @@ int load_table_file(const std::string &path, std::vector<Entry> *out, std::strin
         en.d_model = (int)dm->num;
         en.d_ff = (int)df->num;
         if (!variant_from_name(w->str, &en.v)) return 1;
-        if ((en.op == T_GATE_UP_FP8 || en.op == T_DOWN_FP8) && en.v.engine == dfk::ENGINE_VALU &&
-            en.v.trav == dfk::TRAV_COL)
-            return 1;  // no vector-ALU column walk over FP8 codes
+        if (en.op == T_GATE_UP_FP8 && en.v.engine == dfk::ENGINE_VALU && en.v.trav == dfk::TRAV_COL)
+            return 1;  // no vector-ALU column walk for gate-up over FP8 codes
         if (en.B < 1 || en.d_model < 1 || en.d_ff < 1) return 1;
         v.push_back(en);
     }
@@ -938,9 +937,10 @@ dfk_status_t dfk_rmsnorm_swiglu_mlp(const uint16_t *x, const uint16_t *gain, dou
 // B = 3, the matrix cores' column traversal up to B = 16, their row traversal
 // above; down on the VALU row walk up to B = 2, the matrix cores' column
 // traversal above.  ROW: VALU up to B = 8, else the matrix cores; COL: the
-// matrix cores; *_VALU / *_MFMA force the engine (there is no VALU column walk
-// for FP8).  A table choice the VALU kernel cannot run falls back to the
-// matrix cores with the same traversal.
+// matrix cores; *_VALU / *_MFMA force the engine (COL_VALU: the down column
+// walk with h in registers; gate-up has no VALU column walk over FP8 codes).
+// A table choice the VALU kernel cannot run falls back to the matrix cores
+// with the same traversal.
 static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model, int d_ff, int dev, Plan *p) {
     using dfk::ENGINE_MFMA;
     using dfk::ENGINE_VALU;
@@ -968,7 +968,8 @@ static dfk_status_t fp8_plan(dfk::Op op, dfk_layout_t layout, int B, int d_model
         case DFK_LAYOUT_ROW_VALU: e = ENGINE_VALU, tr = TRAV_ROW; break;
         case DFK_LAYOUT_ROW_MFMA: e = ENGINE_MFMA, tr = TRAV_ROW; break;
         case DFK_LAYOUT_COL_MFMA: e = ENGINE_MFMA, tr = TRAV_COL; break;
-        default: return DFK_ERR_UNSUPPORTED;  // COL_VALU, ROW_PERSISTENT
+        case DFK_LAYOUT_COL_VALU: e = ENGINE_VALU, tr = TRAV_COL; break;  // down only, B <= 4
+        default: return DFK_ERR_UNSUPPORTED;  // ROW_PERSISTENT
     }
     if (!dfk::make_fp8_plan(op, e, tr, B, d_model, d_ff, device_cus(dev), p) &&
         !(from_table && e == ENGINE_VALU && dfk::make_fp8_plan(op, ENGINE_MFMA, tr, B, d_model, d_ff,

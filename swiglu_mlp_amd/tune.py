@@ -6,7 +6,8 @@
 
 For every (d_model, d_ff) shape, batch B and op (gate_up, down and their FP8
 weight-only forms gate_up_fp8, down_fp8), each variant that can run the shape
-(row_valu, col_valu, row_mfma, col_mfma; FP8 has no col_valu) is launched back
+(row_valu, col_valu, row_mfma, col_mfma; FP8 gate-up has no col_valu, FP8 down
+has it up to B = 4) is launched back
 to back with rotating weight copies (at least 1.5 GB of distinct weights, so
 every launch streams from HBM rather than the 256 MB Infinity Cache).  The
 winner is the variant with the lowest median per-call cost; variants within
@@ -76,7 +77,11 @@ def layer_bytes(d_model, d_ff, fp8=False):
 
 def runnable(variant, op, B, d_model):
     fp8 = op.endswith("_fp8")
-    if fp8 and (variant == "col_valu" or B > FP8_MAX_BATCH):
+    if fp8 and B > FP8_MAX_BATCH:
+        return False
+    # FP8 codes: the vector-ALU column walk exists for down only (h in
+    # registers, B <= 4)
+    if fp8 and variant == "col_valu" and (op != "down_fp8" or B > 4):
         return False
     if variant.endswith("valu"):
         if B > 8:

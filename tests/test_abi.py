@@ -258,7 +258,7 @@ _V = '"lib_version": "%s", "rocm_version": "%s"'
     '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "gate_up"}]}',
     '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "x", "B": 1, "d_model": 8, "d_ff": 8, "winner": "row_valu"}]}',
     '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "down", "B": 1, "d_model": 8, "d_ff": 8, "winner": "diag"}]}',
-    '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "down_fp8", "B": 1, "d_model": 16, "d_ff": 16, "winner": "col_valu"}]}',
+    '{"format": "dfk-tuning-v2", "arch": "gfx950", %V, "entries": [{"op": "gate_up_fp8", "B": 1, "d_model": 16, "d_ff": 16, "winner": "col_valu"}]}',
 ])
 def test_bad_table_falls_back_to_heuristic(tmp_path, content, restore_table):
     p = tmp_path / "bad.json"

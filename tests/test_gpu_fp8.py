@@ -51,10 +51,12 @@ def code_matrix(rows, cols, shift=0):
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 6, 8, 20])
-@pytest.mark.parametrize("layout", [Layout.ROW_VALU, Layout.ROW_MFMA, Layout.COL_MFMA])
+@pytest.mark.parametrize("layout", [Layout.ROW_VALU, Layout.COL_VALU, Layout.ROW_MFMA, Layout.COL_MFMA])
 def test_every_code_through_down(dev, orc, B, layout):
     if layout == Layout.ROW_VALU and B > 8:
-        pytest.skip("the vector-ALU FP8 kernels take B <= 8")
+        pytest.skip("the vector-ALU FP8 row walk takes B <= 8")
+    if layout == Layout.COL_VALU and B > 4:
+        pytest.skip("the FP8 down column walk (h in registers) takes B <= 4")
     M = K = 256
     q = code_matrix(M, K)
     s = np.array([2.0 ** -(m % 4) for m in range(M)], dtype=np.float32)
@@ -113,6 +115,41 @@ def test_fp8_small_shapes(dev, orc, shape):
         H.assert_h_close(h.double().cpu().numpy(), h_ref, f"gate_up_fp8 {what}")
         H.assert_y_close(H.host_bf16_as_f64(y), y_ref, f"mlp_fp8 {what}")
         H.assert_y_close(H.host_bf16_as_f64(yd), yd_ref, f"down_fp8 {what}")
+    if B <= 4:
+        # the down column walk with h held in registers (fits every shape here)
+        yd = dfk.dfk_down_proj_fp8(H.dev_f32(h_in, dev), d["q_down"], d["s_down"], layout=Layout.COL_VALU)
+        torch.cuda.synchronize()
+        H.assert_y_close(H.host_bf16_as_f64(yd), yd_ref, f"down_fp8 COL_VALU {shape}")
+
+
+# FP8 down column walk with h in registers where every workgroup walks several
+# row groups (odd and even counts, one or two rows per group, 8- and 16-wave
+# workgroups), and the Llama-3-8B down shape: against the oracle, and integer
+# codes with power-of-two scales bit for bit.
+DOWN_HREG_F8_SHAPES = [(1, 4096, 14336), (2, 4096, 14336), (3, 4096, 14336), (4, 4096, 14336),
+                       (2, 8192, 4096), (3, 6144, 3008), (4, 2048, 9008)]
+
+
+@pytest.mark.parametrize("shape", DOWN_HREG_F8_SHAPES, ids=lambda s: "B%d_%dx%d" % s)
+def test_fp8_down_h_in_registers(dev, orc, shape):
+    B, dm, dff = shape
+    rng = np.random.default_rng(9600 + B + dm)
+    q = rng.integers(0, 256, size=(dm, dff), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0  # no NaN codes
+    s = (2.0 ** rng.integers(-3, 1, size=dm)).astype(np.float32)
+    qd, sd = to_dev(q, dev), to_dev(s, dev)
+    h_in = inputs.h_like(B, dff, seed=9650 + B)
+    want = orc.down_fp8(h_in.astype(np.float64), q, s)
+    y = dfk.dfk_down_proj_fp8(H.dev_f32(h_in, dev), qd, sd, layout=Layout.COL_VALU)
+    torch.cuda.synchronize()
+    H.assert_y_close(H.host_bf16_as_f64(y), want, f"down_fp8 COL_VALU {shape}")
+    # small integer h and codes of small integers (|e4m3| <= 4): every sum exact
+    qi = rng.choice(np.array([0x00, 0x38, 0xB8, 0x40, 0xC0, 0x48, 0xC8], dtype=np.uint8), size=(dm, dff))
+    hi = inputs.integer_h(B, dff, seed=9680 + B, bound=64)
+    got = dfk.dfk_down_proj_fp8(H.dev_f32(hi, dev), to_dev(qi, dev), sd, layout=Layout.COL_VALU)
+    torch.cuda.synchronize()
+    exact = orc.bf16_rne_array(orc.down_fp8(hi.astype(np.float64), qi, s))
+    np.testing.assert_array_equal(H.host_bits(got), exact, err_msg=f"integer {shape}")
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 16, 64])
@@ -135,6 +172,12 @@ def test_fp8_unsupported(dev):
     cases = [(mk(129, 64, 48), Layout.AUTO), (mk(9, 64, 48), Layout.ROW_VALU), (mk(1, 72, 48), Layout.AUTO),
              (mk(1, 64, 40), Layout.AUTO)]
     cases += [(mk(1, 64, 48), l) for l in (Layout.COL_VALU, Layout.ROW_PERSISTENT)]
+    # the down column walk takes B <= 4
+    d5 = mk(5, 64, 48)
+    with pytest.raises(dfk.DfkError) as e:
+        dfk.dfk_down_proj_fp8(torch.zeros((5, 48), dtype=torch.float32, device=dev), d5["q_down"], d5["s_down"],
+                              layout=Layout.COL_VALU)
+    assert e.value.status == Status.UNSUPPORTED
     for d, layout in cases:
         with pytest.raises(dfk.DfkError) as e:
             dfk.dfk_swiglu_mlp_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], d["q_down"],

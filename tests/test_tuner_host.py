@@ -93,9 +93,14 @@ def test_fp8_ops_plan_and_limits():
     blocks = tune.plan_blocks([(4096, 14336), (4104, 14336)], [1, 16], reps=5,
                               ops=("gate_up", "gate_up_fp8", "down_fp8"))
     fp8 = [b for b in blocks if b["op"].endswith("_fp8")]
-    # no vector-ALU column walk over FP8 codes; d_model 4104 is not a multiple of 16
-    assert fp8 and all(b["variant"] != "col_valu" and b["d_model"] == 4096 for b in fp8)
-    assert {b["variant"] for b in fp8 if b["B"] == 1} == {"row_valu", "row_mfma", "col_mfma"}
+    # no vector-ALU column walk for gate-up over FP8 codes (down: B <= 4);
+    # d_model 4104 is not a multiple of 16
+    assert fp8 and all(b["d_model"] == 4096 for b in fp8)
+    assert all(b["variant"] != "col_valu" for b in fp8 if b["op"] == "gate_up_fp8")
+    assert {b["variant"] for b in fp8 if b["B"] == 1 and b["op"] == "gate_up_fp8"} == {"row_valu", "row_mfma",
+                                                                                       "col_mfma"}
+    assert {b["variant"] for b in fp8 if b["B"] == 1 and b["op"] == "down_fp8"} == {"row_valu", "col_valu",
+                                                                                    "row_mfma", "col_mfma"}
     assert {b["variant"] for b in fp8 if b["B"] == 16} == {"row_mfma", "col_mfma"}
     # per shape, the bf16 blocks come before the FP8 ones (one weight set at a time)
     for dm in (4096, 4104):
