@@ -4135,11 +4135,16 @@ static bool plan_staged(bool gu, int B, int BT, int C, int cus, const KernelInfo
 #ifndef DFK_DN_HREG_WAVES
 #define DFK_DN_HREG_WAVES 8
 #endif
-// from this batch up (at B = 1 the column walk with h in LDS is as fast or
-// faster on the larger shapes: kernel durations at 4096 x 14336 19.7 against
-// 20.4 us, at 5120 x 13824 22.8 against 23.8 us)
+// from this batch up, and at B = 1 on W_down of at most DFK_DN_HREG_B1_MAX
+// elements (at B = 1 the column walk with h in LDS is faster on the larger
+// shapes, kernel durations at 4096 x 14336 19.7 against 20.4 us and at
+// 5120 x 13824 22.8 against 23.8 us; slower on the smaller ones, 3072 x 8192
+// 10.9 against 10.6 us and 2048 x 5632 6.9 against 6.6 us)
 #ifndef DFK_DN_HREG_MIN_B
 #define DFK_DN_HREG_MIN_B 2
+#endif
+#ifndef DFK_DN_HREG_B1_MAX
+#define DFK_DN_HREG_B1_MAX (3072L * 8192L)
 #endif
 constexpr int kHregMaxJ = 8;
 // FP8 codes: 16 h values per chunk and batch row, so J * 16 * B registers,
@@ -4168,7 +4173,8 @@ static const void *const kDnHregF8[4][kHregMaxJ] = {
 
 // C: 16-byte chunks per W_down row (K / 8 bf16, K / 16 FP8 codes)
 static bool plan_hreg(int B, int C, int M, int cus, Plan *q, bool f8 = false) {
-    if (!DFK_DN_HREG || B < (f8 ? 1 : DFK_DN_HREG_MIN_B) || B > (f8 ? 4 : kValuMaxBatch) || C < 1) return false;
+    if (!DFK_DN_HREG || B < 1 || B > (f8 ? 4 : kValuMaxBatch) || C < 1) return false;
+    if (!f8 && B < DFK_DN_HREG_MIN_B && (long)M * C * 8 > DFK_DN_HREG_B1_MAX) return false;
     const int order[4] = {DFK_DN_HREG_WAVES, 16, 8, 4};
     for (int w : order) {
         if (w < 1 || w > kHregMaxWaves) continue;
