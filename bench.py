@@ -252,15 +252,16 @@ def time_stack(device, B=1, layers=32, steps=20, warmup=3):
             "fused_rescale_graph_us_per_layer": round(gt["fused"] / layers, 2)}
 
 
-def time_stream_ceiling(device, steps=100, warmup=10, rotate=5):
+def time_stream_ceiling(device, steps=100, warmup=10, rotate=5, d_model=D_MODEL, d_ff=D_FF, only_two=False):
     """The practical HBM read ceiling on this machine: dfk_stream_read (plain
-    16-byte streaming loads, no arithmetic) over `rotate` buffers of the 8B
-    layer's weight bytes, read as the MLP call reads them (gate-up's bytes in
-    one launch, then down's) and in one launch; us and GB/s."""
+    16-byte streaming loads, no arithmetic) over `rotate` buffers of a layer's
+    weight bytes (the 8B layer's by default), read as the MLP call reads them
+    (gate-up's bytes in one launch, then down's) and in one launch; us and
+    GB/s.  only_two: the two-launch figure alone."""
     import torch
     import swiglu_mlp_amd as dfk
 
-    gu, dn = 2 * 2 * D_FF * D_MODEL, 2 * D_MODEL * D_FF
+    gu, dn = 2 * 2 * d_ff * d_model, 2 * d_model * d_ff
     bufs = [torch.ones(gu + dn, dtype=torch.uint8, device=device) for _ in range(rotate)]
     sink = torch.zeros(64, dtype=torch.int32, device=device)
 
@@ -270,10 +271,11 @@ def time_stream_ceiling(device, steps=100, warmup=10, rotate=5):
         dfk.dfk_stream_read(b[gu:], sink)
 
     res = {}
-    for name, fn, nbytes in (("gate_up_bytes", lambda i: dfk.dfk_stream_read(bufs[i % rotate][:gu], sink), gu),
-                             ("down_bytes", lambda i: dfk.dfk_stream_read(bufs[i % rotate][gu:], sink), dn),
-                             ("both_two_launches", two, gu + dn),
-                             ("both_one_launch", lambda i: dfk.dfk_stream_read(bufs[i % rotate], sink), gu + dn)):
+    legs = (("gate_up_bytes", lambda i: dfk.dfk_stream_read(bufs[i % rotate][:gu], sink), gu),
+            ("down_bytes", lambda i: dfk.dfk_stream_read(bufs[i % rotate][gu:], sink), dn),
+            ("both_two_launches", two, gu + dn),
+            ("both_one_launch", lambda i: dfk.dfk_stream_read(bufs[i % rotate], sink), gu + dn))
+    for name, fn, nbytes in (legs[2:3] if only_two else legs):
         us = _timed(fn, steps, warmup) * 1e3
         res[name] = {"bytes": nbytes, "us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
     del bufs
@@ -316,7 +318,9 @@ def time_shape_sweep(device, steps=100, warmup=10, min_rotated_bytes=600e6):
     (d_model, d_ff) x batch of the sweep, under AUTO and with both kernels
     forced to ROW or to COL (the scheduler picks per kernel among four
     variants, so AUTO should be at least as fast as either).  Enough weight
-    sets are rotated that they do not fit in the 256 MB last-level cache."""
+    sets are rotated that they do not fit in the 256 MB last-level cache.
+    Per shape also the practical ceiling (two streaming-read launches over
+    the same bytes, as many buffers rotated) and each call's fraction of it."""
     import math
     import torch
     import swiglu_mlp_amd as dfk
@@ -329,7 +333,9 @@ def time_shape_sweep(device, steps=100, warmup=10, min_rotated_bytes=600e6):
         sets = [(inputs.randn_bf16_device((dff, dm), 0.02, 8000 + 100 * s + 10 * r + 1, device),
                  inputs.randn_bf16_device((dff, dm), 0.02, 8000 + 100 * s + 10 * r + 2, device),
                  inputs.randn_bf16_device((dm, dff), 0.02, 8000 + 100 * s + 10 * r + 3, device)) for r in range(R)]
-        shape = {}
+        ceiling = time_stream_ceiling(device, steps, warmup, rotate=R, d_model=dm, d_ff=dff,
+                                      only_two=True)["both_two_launches"]
+        shape = {"practical_two_launch_us": ceiling["us"]}
         for B in inputs.SWEEP_BATCHES:
             x = inputs.randn_bf16_device((B, dm), 1.0, 8900 + B, device)
             out = torch.empty((B, dm), dtype=torch.bfloat16, device=device)
@@ -341,6 +347,7 @@ def time_shape_sweep(device, steps=100, warmup=10, min_rotated_bytes=600e6):
                 t[name] = _timed(lambda i: dfk.dfk_swiglu_mlp(x, *sets[i % R], out, layout=layout), steps, warmup) * 1e3
             gbps = mlp_bytes(B, dm, dff) / (t["auto"] * 1e-6) / 1e9
             shape[str(B)] = {"us_per_call": round(t["auto"], 2), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                             "frac_of_practical": round(gbps / ceiling["GBps"], 4),
                              "row_us": round(t["row"], 2), "col_us": round(t["col"], 2)}
         res[f"{dm}x{dff}"] = shape
         del sets
