@@ -152,6 +152,57 @@ def test_fp8_down_h_in_registers(dev, orc, shape):
     np.testing.assert_array_equal(H.host_bits(got), exact, err_msg=f"integer {shape}")
 
 
+def _hreg_f8_fits(B, d_ff):
+    """Whether the FP8 down column walk takes the shape: some workgroup width
+    (8, 16 or 4 waves) leaves a lane J <= 8 chunks of h with J * 16 * B <= 64
+    registers (16 waves only up to J = 4)."""
+    if B > 4:
+        return False
+    c16 = d_ff // 16
+    for w in (8, 16, 4):
+        J = -(-(-(-c16 // w)) // 64)
+        if J <= 8 and J * 16 * B <= 64 and (w <= 8 or J <= 4):
+            return True
+    return False
+
+
+# Seeded random shapes (multiples of 16 up to 3072, B up to 128): every FP8
+# variant, and the down column walk wherever it takes the shape (else it must
+# refuse it), against the oracle.
+def _random_fp8_shapes(n=16, seed=20261205):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 17, 40, 64, 128])), 16 * int(rng.integers(1, 193)),
+             16 * int(rng.integers(1, 193))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("shape", _random_fp8_shapes(), ids=lambda s: "B%d_%dx%d" % s)
+def test_fp8_random_shapes(dev, orc, shape):
+    B, dm, dff = shape
+    L = inputs.fp8_layer(B, dm, dff, seed=9700 + B + dm, std=0.05)
+    d = {k: (H.dev_bf16(v, dev) if k == "x" else to_dev(v, dev)) for k, v in L.items()}
+    y_ref, h_ref = orc.mlp_fp8(L["x"], L["q_gate"], L["s_gate"], L["q_up"], L["s_up"], L["q_down"], L["s_down"])
+    h_in = inputs.h_like(B, dff, seed=9750 + B)
+    yd_ref = orc.down_fp8(h_in.astype(np.float64), L["q_down"], L["s_down"])
+    for layout in layouts_for(B):
+        what = f"{layout.name} {shape}"
+        h = dfk.dfk_gate_up_silu_mul_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], layout=layout)
+        y = dfk.dfk_swiglu_mlp_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], d["q_down"],
+                                   d["s_down"], layout=layout)
+        yd = dfk.dfk_down_proj_fp8(H.dev_f32(h_in, dev), d["q_down"], d["s_down"], layout=layout)
+        torch.cuda.synchronize()
+        H.assert_h_close(h.double().cpu().numpy(), h_ref, f"gate_up_fp8 {what}")
+        H.assert_y_close(H.host_bf16_as_f64(y), y_ref, f"mlp_fp8 {what}")
+        H.assert_y_close(H.host_bf16_as_f64(yd), yd_ref, f"down_fp8 {what}")
+    if _hreg_f8_fits(B, dff):
+        yd = dfk.dfk_down_proj_fp8(H.dev_f32(h_in, dev), d["q_down"], d["s_down"], layout=Layout.COL_VALU)
+        torch.cuda.synchronize()
+        H.assert_y_close(H.host_bf16_as_f64(yd), yd_ref, f"down_fp8 COL_VALU {shape}")
+    else:
+        with pytest.raises(dfk.DfkError) as e:
+            dfk.dfk_down_proj_fp8(H.dev_f32(h_in, dev), d["q_down"], d["s_down"], layout=Layout.COL_VALU)
+        assert e.value.status == Status.UNSUPPORTED, shape
+
+
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 16, 64])
 def test_fp8_llama8b_shape(dev, orc, B):
     L = inputs.fp8_layer(B, 4096, 14336, seed=9300, std=0.02)

@@ -105,6 +105,40 @@ def test_small_shapes_all_variants(dev, orc, shape):
         H.assert_y_close(H.host_bf16_as_f64(y), yd_ref, f"down {layout.name} {shape}")
 
 
+# Seeded random shapes (d_model and d_ff multiples of 8 from 8 to 3072, B from
+# 1 to 64, a few up to 256): every plan rule's boundary is crossed somewhere
+# (chunks per lane and waves per workgroup of the h-in-registers walk, K
+# panels, batch tiles, K splits), and every variant of every entry point is
+# compared with the oracle.
+def _random_shapes(n=24, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 20, 33, 64, 100, 256] if i % 4 == 0 else
+                           [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 17, 31, 48, 64]))
+        dm = 8 * int(rng.integers(1, 385))
+        dff = 8 * int(rng.integers(1, 385))
+        out.append((B, dm, dff))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(), ids=lambda s: "B%d_%dx%d" % s)
+def test_random_shapes_all_variants(dev, orc, shape):
+    B, dm, dff = shape
+    L = inputs.random_layer(B, dm, dff, seed=7700 + B + dm + dff)
+    T = to_dev(L, dev)
+    _, _, h_ref = orc.gate_up(L.x, L.w_gate, L.w_up)
+    y_ref, _ = orc.mlp(L.x, L.w_gate, L.w_up, L.w_down)
+    h_in = inputs.h_like(B, dff, seed=7800 + B)
+    yd_ref = orc.down(h_in, L.w_down)
+    for layout in layouts_for("gate_up", B, dm):
+        H.assert_h_close(gpu_gate_up(T, layout), h_ref, f"gate_up {layout.name} {shape}")
+        H.assert_y_close(H.host_bf16_as_f64(gpu_mlp(T, layout)), y_ref, f"mlp {layout.name} {shape}")
+    for layout in layouts_for("down", B, dm):
+        y = gpu_down(h_in, T["w_down"], layout, dev)
+        H.assert_y_close(H.host_bf16_as_f64(y), yd_ref, f"down {layout.name} {shape}")
+
+
 @pytest.mark.parametrize("op", ["gate_up", "down"])
 def test_forced_valu_beyond_its_range_is_unsupported(dev, op):
     B, dm, dff = 16, 64, 48
