@@ -994,11 +994,15 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t w, float &a, float &b) {
 }
 
 // K is cut into gridDim.y panels of CS weight chunks, each small enough that
-// its slice of h ([B][16 CS] fp32) sits in LDS; one panel writes y directly,
-// several write scaled fp32 partial sums that panel_reduce_kernel adds.
+// its slice of h (16 CS fp32 per batch row) sits in LDS; one panel writes y
+// directly, several write scaled fp32 partial sums that panel_reduce_kernel
+// adds.  In LDS each batch row's slice is four planes: plane q holds the
+// q-th 16-byte quarter of every chunk (pitch CS + 1), so the 64 lanes of a
+// wave, which take consecutive chunks, read consecutive 16-byte words of a
+// plane (without the planes, lanes 4 chunks apart would share LDS banks).
 template <int B, int R, int U>
 __global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, float *partial, int CS) {
-    extern __shared__ f32x4_t hs[];  // [B][4 CS]: this panel's h
+    extern __shared__ f32x4_t hs[];  // [B][4][CS + 1]: this panel's h
     constexpr int waves = kValuBlock / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * waves + threadIdx.x / kWave);
@@ -1007,7 +1011,8 @@ __global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, 
     const int c_lo = panel * CS;
     const int cn = min(CS, a.C16 - c_lo);  // weight chunks in this panel
     const int HC = a.K / 4;                // f32x4 chunks of a whole h row
-    const int HP = 4 * CS;                 // LDS pitch of a panel's h row
+    const int P = CS + 1;                  // LDS pitch of a quarter plane
+    const int HP = 4 * P;                  // LDS pitch of a panel's h row
     constexpr int G = kWave * U;
     const int gpr = (cn + G - 1) / G;
     const int rows = max(0, (a.groups - wave_id + total_waves - 1) / total_waves);
@@ -1045,7 +1050,7 @@ __global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, 
                 f32x4_t hv[B];
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    hv[b] = hs[(size_t)b * HP + 4 * cc + q];  // unconditional read, masked after
+                    hv[b] = hs[(size_t)b * HP + q * P + cc];  // unconditional read, masked after
                     if (!ok) hv[b] = fzero;
                 }
 #pragma unroll
@@ -1107,10 +1112,9 @@ __global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, 
     load(f0, k0, j0);
     __builtin_amdgcn_sched_barrier(0);
     const f32x4_t *hg = reinterpret_cast<const f32x4_t *>(a.h);
-    if (panels == 1) {
-        stage_lds(hs, hg, B * HC);  // all of h, contiguous
-    } else {
-        // this panel's slice of each of the B rows of h (4 cn chunks)
+    {
+        // this panel's slice of each of the B rows of h (4 cn quarters, the
+        // whole row with one panel), quarter g of the slice to plane g % 4
         const int rc = 4 * cn;
         constexpr int kBatch = 8;
 #pragma unroll
@@ -1123,8 +1127,10 @@ __global__ __launch_bounds__(kValuBlock) void down_fp8_row_kernel(DownF8Args a, 
                 for (int s = 0; s < kBatch; ++s)
                     if (base + s * kValuBlock < rc) v[s] = src[base + s * kValuBlock];
 #pragma unroll
-                for (int s = 0; s < kBatch; ++s)
-                    if (base + s * kValuBlock < rc) dst[base + s * kValuBlock] = v[s];
+                for (int s = 0; s < kBatch; ++s) {
+                    const int g = base + s * kValuBlock;
+                    if (g < rc) dst[(g & 3) * P + (g >> 2)] = v[s];
+                }
             }
         }
         __syncthreads();
@@ -4604,7 +4610,9 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
     } else {
         // h in LDS, K cut into the fewest panels whose h slice fits
         const long c16 = q.K / 16;
-        const long max_cs = std::max(1L, (long)(kHLdsLimit / ((size_t)B * 64)));
+        // (cs + 1) x 64 bytes per batch row: four quarter planes, each
+        // padded by one 16-byte word
+        const long max_cs = std::max(1L, (long)(kHLdsLimit / ((size_t)B * 64)) - 1);
         const long S = ceil_div(c16, max_cs);
         const long cs = ceil_div(c16, S);
         q.splits = (int)ceil_div(c16, cs);
@@ -4612,7 +4620,7 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
         q.partial_floats = q.splits > 1 ? (size_t)q.splits * B * q.rows : 0;
         q.h_in_lds = true;
         ki = kDnF8Row[B - 1];
-        q.lds_bytes = (size_t)B * cs * 64;
+        q.lds_bytes = (size_t)B * (cs + 1) * 64;
         q.kind = KIND_DN_FP8_ROW;
     }
     q.block = ki.block;
