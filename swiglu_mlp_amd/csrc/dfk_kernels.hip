@@ -1933,13 +1933,26 @@ template <int KBC> struct Lt {
     static __device__ __forceinline__ bf16x8_t frag(const u32x4_t *lt, int j, int lr, int lq) {
         return as_bf16x8(lt[lr * kPitch + 4 * j + lq]);
     }
+    // The block's chunk at tile position p (the B operand's K index for it).
+    static __device__ __forceinline__ int kpos(int p) { return p; }
 };
 
 // The same LDS tile filled from FP8 E4M3 codes: one 16-byte load carries 16
 // codes (two bf16 chunks), so a row of a block takes KBC / 2 lanes and an
 // instruction covers 64 / (KBC / 2) rows; the codes are widened to bf16
 // (exactly) on the way into LDS.  C counts bf16 chunks (K / 8) as for Lt.
-template <int KBC> struct Lt8 {
+// A lane parks its two bf16 chunks (2p, 2p + 1) side by side, so the lanes'
+// 16-byte words in one store are 32 bytes apart and pairs of lanes share an
+// LDS bank.  SPLIT parks the low chunk at tile position p and the high one at
+// KBC / 2 + p instead (consecutive positions per store, no shared bank) and
+// permutes the block's K order in the tile accordingly: kpos maps a tile
+// position to its chunk, and the B operand is read at that chunk (any order
+// of K within a block gives the same sum terms, paired alike on both
+// operands).  Taken where the B operand comes from LDS planes that are read
+// once per block anyway (the staged-h down kernel); where it is loaded from
+// memory per fragment, the permuted order splits each fragment's 64
+// contiguous bytes and costs more than the conflicts.
+template <int KBC, bool SPLIT = false> struct Lt8 {
     static constexpr int kC8 = KBC / 2;
     static constexpr int kRowsPerInst = 64 / kC8;
     static constexpr int kInsts = 16 / kRowsPerInst;
@@ -1963,13 +1976,16 @@ template <int KBC> struct Lt8 {
         for (int i = 0; i < kInsts; ++i) {
             u32x4_t lo, hi;
             e4m3x16_to_bf16(v[i], lo, hi);
-            u32x4_t *dst = lt + (i * kRowsPerInst + lane / kC8) * kPitch + 2 * (lane % kC8);
+            u32x4_t *dst = lt + (i * kRowsPerInst + lane / kC8) * kPitch + (SPLIT ? 1 : 2) * (lane % kC8);
             dst[0] = ok ? lo : zero;
-            dst[1] = ok ? hi : zero;
+            dst[SPLIT ? kC8 : 1] = ok ? hi : zero;
         }
     }
     static __device__ __forceinline__ bf16x8_t frag(const u32x4_t *lt, int j, int lr, int lq) {
         return as_bf16x8(lt[lr * kPitch + 4 * j + lq]);
+    }
+    static __device__ __forceinline__ int kpos(int p) {
+        return !SPLIT ? p : p < kC8 ? 2 * p : 2 * (p - kC8) + 1;
     }
 };
 
@@ -2030,7 +2046,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
 
         u32x4_t xf[XS][BT];
         auto load_x = [&](int kb, int j, u32x4_t (&xb)[BT]) {
-            const int c = min(kb * KBC + 4 * j + lq, a.C - 1);
+            const int c = min(kb * KBC + L::kpos(4 * j + lq), a.C - 1);
 #pragma unroll
             for (int bt = 0; bt < BT; ++bt) xb[bt] = px[bt][c];
         };
@@ -2050,7 +2066,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lt_kernel(GateUpAr
                 if constexpr (!kPre) {
                     if (j + 1 < L::kSteps) load_x(kb, j + 1, xf[(j + 1) & 1]);
                 }
-                const bool cok = !tail || kb * KBC + 4 * j + lq < a.C;
+                const bool cok = !tail || kb * KBC + L::kpos(4 * j + lq) < a.C;
                 const bf16x8_t ag = L::frag(ltg, j, lr, lq);
                 const bf16x8_t au = L::frag(ltu, j, lr, lq);
 #pragma unroll
@@ -2189,7 +2205,7 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a)
 
         f32x4_t hf[HS][BT][2];
         auto load_h = [&](int kb, int j, f32x4_t (&hb)[BT][2]) {
-            const int c = min(kb * KBC + 4 * j + lq, a.C - 1);
+            const int c = min(kb * KBC + L::kpos(4 * j + lq), a.C - 1);
 #pragma unroll
             for (int bt = 0; bt < BT; ++bt) {
                 hb[bt][0] = ph[bt][2 * c];
@@ -2212,7 +2228,7 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lt_kernel(DownArgs a)
                 if constexpr (!kPre) {
                     if (j + 1 < L::kSteps) load_h(kb, j + 1, hf[(j + 1) & 1]);
                 }
-                const bool cok = !tail || kb * KBC + 4 * j + lq < a.C;
+                const bool cok = !tail || kb * KBC + L::kpos(4 * j + lq) < a.C;
                 const bf16x8_t aw = L::frag(ltw, j, lr, lq);
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
@@ -2859,7 +2875,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gate_up_mfma_lts_kernel(GateUpA
                 const bf16x8_t au = L::frag(ltu, j, lr, lq);
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
-                    const bf16x8_t xb = as_bf16x8(xd[(bt * 16 + lr) * KP + 4 * j + lq]);
+                    const bf16x8_t xb = as_bf16x8(xd[(bt * 16 + lr) * KP + L::kpos(4 * j + lq)]);
                     accg[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb, accg[bt], 0, 0, 0);
                     accu[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb, accu[bt], 0, 0, 0);
                 }
@@ -3063,7 +3079,7 @@ __global__ __launch_bounds__(WAVES * kWave) void down_mfma_lts_kernel(DownArgs a
 template <int BT, int WAVES, int TR, int WPE, bool F8 = false, int NBUF = 1, int KBC = 32>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void down_mfma_ltsw_kernel(
     DownArgs a, float *partial, int S, int CS) {
-    using L = typename Pick<F8, Lt8<KBC>, Lt<KBC>>::T;
+    using L = typename Pick<F8, Lt8<KBC, true>, Lt<KBC>>::T;
     constexpr int KP = KBC + 1;           // LDS pitch of a staged h row, chunks
     constexpr int NT = WAVES * kWave;
     constexpr int XR = 16 * BT;           // staged h rows: the padded batch
@@ -3135,7 +3151,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(W
             for (int j = 0; j < L::kSteps; ++j) {
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
-                    const int o = (bt * 16 + lr) * KP + 4 * j + lq;
+                    const int o = (bt * 16 + lr) * KP + L::kpos(4 * j + lq);
                     const bf16x8_t bhi = as_bf16x8(shi[o]), blo = as_bf16x8(slo[o]);
 #pragma unroll
                     for (int t = 0; t < TR; ++t) {
