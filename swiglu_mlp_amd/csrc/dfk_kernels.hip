@@ -3503,7 +3503,12 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 // 19.9 / 20.4 against 17.6 / 17.5 / 17.5; 5120 x 13824 48.3 / 49.4 / 53.6
 // against 47.0 / 47.0 / 47.2; but Llama-3-8B (3.5 tiles per CU) 39.7 / 40.2 /
 // 42.0 against 40.7 / 40.8 / 40.9 and Llama-3-70B 153 against 171.  FP8 codes
-// at one batch tile measured slower than their LT column kernel.
+// at one batch tile while the row tiles number fewer than
+// DFK_GU_LTS_F8_BT1_TILES_X10 / 10 per CU: event-timed FP8 row traversal, us at
+// B = 4 / 8 / 16, the LT kernel against this one: Llama-3-8B 31.9 / 29.9 /
+// 29.9 against 29.8 / 26.4 / 26.1, 5120 x 13824 34.2 / 34.5 / 36.4 against
+// 30.5 / 30.5 / 30.7, but Llama-3-70B (7 tiles per CU) 82.3 / 83.4 / 90.2
+// against 94.9 / 96.5 / 96.0
 #ifndef DFK_GU_LTS_NBUF_BT2
 #define DFK_GU_LTS_NBUF_BT2 1
 #endif
@@ -3553,7 +3558,10 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #define DFK_GU_LTS_BT1_TILES_X10 35
 #endif
 #ifndef DFK_GU_LTS_F8_MIN_BT
-#define DFK_GU_LTS_F8_MIN_BT 2
+#define DFK_GU_LTS_F8_MIN_BT 1
+#endif
+#ifndef DFK_GU_LTS_F8_BT1_TILES_X10
+#define DFK_GU_LTS_F8_BT1_TILES_X10 50
 #endif
 #ifndef DFK_GU_LTS_WAVES
 #define DFK_GU_LTS_WAVES 4
@@ -4542,7 +4550,8 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
             *out = q;
             return true;
         }
-        if (gu && row && BT >= DFK_GU_LTS_F8_MIN_BT && BT <= DFK_GU_LTS_MAX_BT) {
+        if (gu && row && BT >= DFK_GU_LTS_F8_MIN_BT && BT <= DFK_GU_LTS_MAX_BT &&
+            (BT > 1 || 10 * ceil_div((long)d_ff, 16L) < (long)DFK_GU_LTS_F8_BT1_TILES_X10 * cus)) {
             // x staged in LDS per workgroup (as for bf16 weights)
             constexpr int W = DFK_GU_LTS_WAVES;
             static const void *const lts[4] = {DFK_GU_LTS_F8_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, W, true> : nullptr,
