@@ -3503,12 +3503,13 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 // 19.9 / 20.4 against 17.6 / 17.5 / 17.5; 5120 x 13824 48.3 / 49.4 / 53.6
 // against 47.0 / 47.0 / 47.2; but Llama-3-8B (3.5 tiles per CU) 39.7 / 40.2 /
 // 42.0 against 40.7 / 40.8 / 40.9 and Llama-3-70B 153 against 171.  FP8 codes
-// at one batch tile while the row tiles number fewer than
-// DFK_GU_LTS_F8_BT1_TILES_X10 / 10 per CU: event-timed FP8 row traversal, us at
-// B = 4 / 8 / 16, the LT kernel against this one: Llama-3-8B 31.9 / 29.9 /
-// 29.9 against 29.8 / 26.4 / 26.1, 5120 x 13824 34.2 / 34.5 / 36.4 against
-// 30.5 / 30.5 / 30.7, but Llama-3-70B (7 tiles per CU) 82.3 / 83.4 / 90.2
-// against 94.9 / 96.5 / 96.0
+// at one batch tile too: event-timed FP8 row traversal, us at B = 4 / 8 / 16,
+// the LT kernel against this one: Llama-3-8B 31.9 / 29.9 / 29.9 against 29.8 /
+// 26.4 / 26.1, 5120 x 13824 34.2 / 34.5 / 36.4 against 30.5 / 30.5 / 30.7, but
+// Llama-3-70B (7 row tiles per CU) 82.3 / 83.4 / 90.2 against 94.9 / 96.5 /
+// 96.0; there (at least DFK_GU_LTS_F8_BT1_TILES_X10 / 10 row tiles per CU)
+// one batch tile takes 128-element blocks, 79.3 / 79.6 / 79.3 (below it they
+// lost: 8B 28.2 / 27.8 / 27.9, 5120 x 13824 32.8 / 32.9 / 33.0)
 #ifndef DFK_GU_LTS_NBUF_BT2
 #define DFK_GU_LTS_NBUF_BT2 1
 #endif
@@ -3539,7 +3540,8 @@ static hipError_t launch_reduce(const float *partial, uint16_t *y, int S, int n,
 #ifndef DFK_GU_LTS_K16_BT3_MAX_X
 #define DFK_GU_LTS_K16_BT3_MAX_X 4
 #endif
-// FP8 codes in the staged-x gate-up kernel from this many batch tiles:
+// FP8 codes in the staged-x gate-up kernel from this many batch tiles (and at
+// one batch tile from DFK_GU_LTS_F8_BT1_TILES_X10 / 10 row tiles per CU):
 // 128-element blocks (one x buffer), workgroup width as for bf16.  Event-timed
 // FP8 gate-up, us at B = 40 / 64, 256-element blocks against 128: 70B 141.8 /
 // 168.4 against 107.7 / 124.7; 3072 x 8192 28.9 / 34.0 against 22.0 / 25.5;
@@ -4550,8 +4552,7 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
             *out = q;
             return true;
         }
-        if (gu && row && BT >= DFK_GU_LTS_F8_MIN_BT && BT <= DFK_GU_LTS_MAX_BT &&
-            (BT > 1 || 10 * ceil_div((long)d_ff, 16L) < (long)DFK_GU_LTS_F8_BT1_TILES_X10 * cus)) {
+        if (gu && row && BT >= DFK_GU_LTS_F8_MIN_BT && BT <= DFK_GU_LTS_MAX_BT) {
             // x staged in LDS per workgroup (as for bf16 weights)
             constexpr int W = DFK_GU_LTS_WAVES;
             static const void *const lts[4] = {DFK_GU_LTS_F8_MIN_BT <= 1 ? (const void *)gate_up_mfma_lts_kernel<1, W, true> : nullptr,
@@ -4569,21 +4570,23 @@ bool make_fp8_plan(Op op, Engine engine, Traversal trav, int B, int d_model, int
             q.chunks_per_split = q.K / 8;
             q.kind = KIND_GU_MFMA_LT;
             q.groups = (int)ceil_div(q.rows, 16);
-            if (BT >= DFK_GU_LTS_F8_K16_MIN_BT) {
+            if (BT >= DFK_GU_LTS_F8_K16_MIN_BT ||
+                10 * (long)q.groups >= (long)DFK_GU_LTS_F8_BT1_TILES_X10 * cus) {
                 // 128-element blocks (as for bf16 weights; one x buffer)
-                static_assert(DFK_GU_LTS_F8_K16_MIN_BT >= 2, "instantiated for BT 2 to 4");
-                static const void *const lts16[2][3] = {
-                    {(const void *)gate_up_mfma_lts_kernel<2, 2, true, 1, 16>,
+                static const void *const lts16[2][4] = {
+                    {(const void *)gate_up_mfma_lts_kernel<1, 2, true, 1, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<2, 2, true, 1, 16>,
                      (const void *)gate_up_mfma_lts_kernel<3, 2, true, 1, 16>,
                      (const void *)gate_up_mfma_lts_kernel<4, 2, true, 1, 16>},
-                    {(const void *)gate_up_mfma_lts_kernel<2, 4, true, 1, 16>,
+                    {(const void *)gate_up_mfma_lts_kernel<1, 4, true, 1, 16>,
+                     (const void *)gate_up_mfma_lts_kernel<2, 4, true, 1, 16>,
                      (const void *)gate_up_mfma_lts_kernel<3, 4, true, 1, 16>,
                      (const void *)gate_up_mfma_lts_kernel<4, 4, true, 1, 16>}};
                 const int w = q.groups >= (long)DFK_GU_LTS_K16_W4_X * cus ? 4 : 2;
                 q.block = w * kWave;
                 q.lds_bytes = (size_t)16 * BT * 17 * 16 + (size_t)w * 2 * Lt8<16>::kTile * 16;
                 q.rows_per_group = 16;
-                q.fn = lts16[w == 4 ? 1 : 0][BT - 2];
+                q.fn = lts16[w == 4 ? 1 : 0][BT - 1];
                 const long occ = blocks_per_cu(q.fn, q.block, q.lds_bytes);
                 q.grid = (int)std::max(1L, std::min((long)cus * occ, ceil_div((long)q.groups, (long)w)));
                 *out = q;

@@ -203,6 +203,24 @@ def test_fp8_random_shapes(dev, orc, shape):
         assert e.value.status == Status.UNSUPPORTED, shape
 
 
+# FP8 gate-up row traversal at one batch tile with many row tiles (at least
+# five per CU on a 256-CU device: the staged-x kernel with 128-element K
+# blocks), ragged K blocks and a partial batch tile, against the oracle.
+MANY_ROWS_F8_SHAPES = [(1, 272, 28688), (5, 1040, 28688), (16, 528, 20496)]
+
+
+@pytest.mark.parametrize("shape", MANY_ROWS_F8_SHAPES, ids=lambda s: "B%d_%dx%d" % s)
+def test_fp8_gate_up_one_tile_many_rows(dev, orc, shape):
+    B, dm, dff = shape
+    L = inputs.fp8_layer(B, dm, dff, seed=9800 + B + dm, std=0.05)
+    d = {k: (H.dev_bf16(v, dev) if k == "x" else to_dev(v, dev)) for k, v in L.items()}
+    _, h_ref = orc.mlp_fp8(L["x"], L["q_gate"], L["s_gate"], L["q_up"], L["s_up"], L["q_down"], L["s_down"])
+    for layout in (Layout.ROW_MFMA, Layout.COL_MFMA, Layout.AUTO):
+        h = dfk.dfk_gate_up_silu_mul_fp8(d["x"], d["q_gate"], d["s_gate"], d["q_up"], d["s_up"], layout=layout)
+        torch.cuda.synchronize()
+        H.assert_h_close(h.double().cpu().numpy(), h_ref, f"gate_up_fp8 {layout.name} {shape}")
+
+
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 16, 64])
 def test_fp8_llama8b_shape(dev, orc, B):
     L = inputs.fp8_layer(B, 4096, 14336, seed=9300, std=0.02)
